@@ -1,0 +1,109 @@
+"""The seeded input generator: structure of the pools, tables, slots and pairs (CPU)."""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_59_amd import workloads as wl
+
+BS = 16
+
+
+def test_tiny_workload_positions():
+    w = wl.make_named("tiny_d64")
+    assert list(w.context_lens) == [1, 16, 17, 50]
+    assert w.num_blocks == 64 and w.max_blocks_per_seq == 4
+    assert w.scale == np.float32(0.125)
+    # the append goes to position ctx-1 of each sequence
+    for s, n in enumerate(w.context_lens):
+        j, off = divmod(int(n) - 1, BS)
+        assert w.slot_mapping[s] == w.block_tables[s, j] * BS + off
+    # 1 -> block 0 slot 0; 16 -> block 0 slot 15; 17 -> block 1 slot 0; 50 -> block 3 slot 1
+    assert [int(x) % BS for x in w.slot_mapping] == [0, 15, 0, 1]
+    assert (w.block_tables[0, 1:] == -1).all() and (w.block_tables[3] >= 0).all()
+
+
+def test_same_seed_same_bytes():
+    a = wl.make_workload("x", 7, 8, 2, 32, len_range=(1, 60), num_seqs=4)
+    b = wl.make_workload("x", 7, 8, 2, 32, len_range=(1, 60), num_seqs=4)
+    for f in ("q", "k_cache", "v_cache", "k_new", "v_new"):
+        assert np.array_equal(getattr(a, f).view(np.uint16), getattr(b, f).view(np.uint16))
+    assert np.array_equal(a.block_tables, b.block_tables)
+
+
+def test_pool_size_and_placement():
+    w = wl.make_workload("x", 8, 8, 2, 32, len_range=(1, 100), num_seqs=9)
+    needed = int(sum(-(-int(n) // BS) for n in w.context_lens))
+    assert w.num_blocks == int(np.ceil(1.25 * needed))
+    used = w.block_tables[w.block_tables >= 0]
+    assert used.size == needed and np.unique(used).size == needed       # no sharing here
+    assert used.max() < w.num_blocks
+
+
+def test_canaries_sit_where_they_should():
+    w = wl.make_workload("x", 9, 4, 2, 16, context_lens=[5, 16, 33], num_blocks=12)
+    ku = w.k_cache.view(np.uint16)
+    vu = w.v_cache.view(np.uint16)
+    used = set(int(b) for b in w.block_tables[w.block_tables >= 0])
+    for b in range(w.num_blocks):
+        if b not in used:
+            assert (ku[b] == 0x7E00).all() and (vu[b] == 0x7E00).all()
+    # sequence 0: positions 4..15 of its only block are canaries, 4 is NaN
+    b0 = int(w.block_tables[0, 0])
+    assert (ku[b0, :, :, 4, :] == 0x7E00).all()
+    assert (vu[b0, :, 0, :, 4] == 0x7E00).all()
+    assert (ku[b0, :, :, 5, :] == 0xFBFF).all()       # 5 % 3 == 2 -> -65504
+    assert np.isfinite(w.k_cache[b0, :, :, :4, :].astype(np.float32)).all()
+
+
+def test_prefix_workload_shares_and_copies():
+    w = wl.make_workload("p", 10, 8, 2, 32, num_seqs=8, prefix_groups=2, prefix_len=64,
+                         suffix_range=(16, 80))
+    tab = w.block_tables
+    for g in range(2):
+        rows = tab[g * 4:(g + 1) * 4, :4]
+        assert (rows == rows[0]).all()                     # shared prompt blocks
+    assert not np.intersect1d(tab[0:4, :4], tab[4:8, :4]).size
+    # one copy per sequence whose append lands inside a partly filled block
+    expect = int(sum(((int(n) - 1) % BS) != 0 for n in w.context_lens))
+    assert w.block_mapping.shape == (expect, 2)
+    for src, dst in w.block_mapping:
+        assert dst in tab and src not in tab              # the table points at the copy
+    # the step is well defined: copy then append then decode, no NaN reaches the output
+    out, _, _ = oracle.decode_step(w.q, w.k_new, w.v_new, w.k_cache, w.v_cache, tab,
+                                   w.context_lens, w.slot_mapping, w.block_mapping,
+                                   w.scale, w.num_kv_heads)
+    assert np.isfinite(out).all()
+
+
+def test_skipping_the_copy_is_visible():
+    """Decoding without the copy-on-write reads a NaN-filled destination block."""
+    w = wl.make_workload("p", 12, 4, 1, 16, num_seqs=4, prefix_groups=1, prefix_len=32,
+                         suffix_range=(18, 30))
+    assert w.block_mapping.shape[0] > 0
+    kc, vc = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_mapping)
+    out = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.num_kv_heads)
+    assert not np.isfinite(out).all()
+
+
+def test_skipping_the_append_is_visible():
+    w = wl.make_named("tiny_d64")
+    out = oracle.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                        w.scale, w.num_kv_heads)
+    assert not np.isfinite(out).any(axis=(1, 2)).any()    # every row saw the NaN slot
+
+
+def test_pool_exhaustion():
+    bm = wl.BlockManager(2)
+    bm.allocate("a", 32)
+    with pytest.raises(wl.PoolExhausted):
+        bm.append_token("a")
+
+
+def test_byte_accounting():
+    w = wl.make_workload("x", 13, 32, 8, 128, context_lens=[100, 2000])
+    per_tok = 2 * 8 * 128 * 2
+    kv = 2100 * per_tok
+    qo = 2 * 2 * 32 * 128 * 2
+    table = (7 + 125) * 4
+    assert w.decode_bytes() == kv + qo + table + 8
+    assert w.append_bytes() == 2 * 2 * per_tok
