@@ -1,0 +1,175 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+A step is the whole hot path over one batch: copy-on-write of shared blocks
+(when the batch has any), append of each sequence's new token, then decode
+attention through the block tables.  Inputs are synthetic and seeded (the
+generator in paged_kv_cache_59_amd.workloads) and resident in HBM before the
+timed region.  The pools are cloned into several replicas totalling at least
+2 GB and the steps rotate over them, so the 256 MB Infinity Cache cannot
+serve a step from the previous one's reads.
+
+Prints one JSON line:
+  value        bytes the step must move / step time, GB/s
+  roofline     the decode kernels (split-context partition kernel plus, when
+               used, the merge) timed with HIP events on their stream:
+               algorithmic decode bytes / mean launch duration vs 8 TB/s
+  cpu_baseline the CPU oracle on this host on one whole step of the same batch
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (fraction of peak) + sequences/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_b64")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replica-gb", type=float, default=2.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (as it is) on whole steps of the same batch, on this host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    step_bytes = w.decode_bytes() + w.append_bytes() + w.copy_bytes()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(w.q, w.k_new, w.v_new, w.k_cache, w.v_cache, w.block_tables,
+                           w.context_lens, w.slot_mapping, w.block_mapping, w.scale,
+                           w.num_kv_heads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s * 0.5 or reps >= 20:
+            break
+    sec = el / reps
+    return {"value": step_bytes / sec / 1e9, "unit": "GB/s", "cores": int(blas),
+            "kind": "oracle", "seconds_per_step": sec, "seqs_per_s": w.num_seqs / sec,
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{reps} whole step(s) of {w.name} (copy, append, fp64 decode of all "
+                      f"{w.num_seqs} sequences), NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_59_amd import binding as pk
+    from paged_kv_cache_59_amd import workloads as wl
+
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    w = wl.make_named(args.workload)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, tab, lens = t(w.q), t(w.block_tables), t(w.context_lens)
+    k_new, v_new, slots = t(w.k_new), t(w.v_new), t(w.slot_mapping)
+    pairs = t(w.block_mapping)
+    kc0, vc0 = t(w.k_cache), t(w.v_cache)
+    pool_bytes = kc0.numel() * 2 + vc0.numel() * 2
+    R = max(1, int(np.ceil(args.replica_gb * 1e9 / pool_bytes)))
+    replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    out = torch.empty_like(q)
+    P = args.partition_size or pk.pa_decode_partition_size(w.num_seqs, w.num_kv_heads,
+                                                           w.max_context_len)
+    ws_bytes = pk.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                           w.head_dim, w.max_context_len, P)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    has_copy = w.block_mapping.shape[0] > 0
+
+    def step(i, ev=None):
+        kc, vc = replicas[i % R]
+        if has_copy:
+            pk.pa_copy_blocks(kc, vc, pairs)
+        pk.pa_reshape_and_cache(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pk.pa_decode(out, q, kc, vc, tab, lens, float(w.scale), w.num_kv_heads,
+                     max_context_len=w.max_context_len, partition_size=P, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    ms_per_step = wall * 1e3 / args.steps
+    step_bytes = w.decode_bytes() + w.append_bytes() + w.copy_bytes()
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_mean_s = float(dec_ms.mean()) * 1e-3
+    achieved = w.decode_bytes() / dec_mean_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+            "max_context_len": w.max_context_len, "mean_context_len": float(w.context_lens.mean()),
+            "seed": w.seed, "partition_size": P, "replicas": R, "accumulate": "f32",
+            "copies_per_step": int(w.block_mapping.shape[0]),
+            "step_bytes": step_bytes, "decode_bytes": w.decode_bytes(),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode_partition_kernel (+ decode_reduce_kernel when split)",
+            "mean_us": round(dec_mean_s * 1e6, 3),
+            "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+            "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if w.name == "prefix_b256":
+        res["config"]["unique_kv_bytes"] = w.unique_kv_bytes()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache decode library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library implements the decode-step hot path of paged attention: the KV
+ * cache of every sequence lives in fixed blocks of 16 token slots that may sit
+ * anywhere in one shared pool, and a per-sequence block table maps logical
+ * block j to its physical block.  Sources (web pages, by title and section):
+ *
+ *   [AQ] "PagedAttention and Continuous Batching Explained (2026)", aquanode.io
+ *        - "PagedAttention: a block table for the KV cache": 16-token blocks,
+ *          per-request block table, the kernel reads through the table, blocks
+ *          need not be contiguous, blocks are shared with copy-on-write.
+ *        - "Why the KV cache is the problem": one K and one V vector per layer
+ *          per token; the cache grows by one entry per token ("TL;DR").
+ *        - "FAQ": the attention computed is the ordinary one.
+ *   [TT] "KV Cache in Serving Engines: PagedAttention, Continuous Batching, and
+ *        Prefix Caching", ttlab - section 2 "Blocks and Block Tables" (a block
+ *        is taken only when the last is full; only the last block is partly
+ *        empty; the computation is that of a contiguous array) and "Sharing
+ *        Blocks" (reference counts; copy when a holder appends).
+ *   [AG] "Continuous batching and paged attention", abhi-g.dev - "Paged
+ *        attention": K and V are gathered through the block table.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Element types: K, V, q and out are IEEE fp16; block tables and context
+ *    lengths int32; slot indices and block pairs int64; scale fp32.
+ *  - Block size: 16 token slots (the only value accepted; [AQ], [TT]).
+ *  - Pool layout (part of this ABI).  With NB physical blocks, Hkv KV heads
+ *    and head dimension D (64 or 128):
+ *        K pool: fp16 [NB][Hkv][D/8][16][8]
+ *                element (block b, head h, slot offset o, dim d) at
+ *                ((((b*Hkv + h)*(D/8) + d/8)*16 + o)*8 + d%8)
+ *        V pool: fp16 [NB][Hkv][2][D][8]
+ *                element (b, h, o, d) at ((((b*Hkv + h)*2 + o/8)*D + d)*8 + o%8)
+ *    so one (block, head) tile is 16*D contiguous elements in both pools.
+ *  - A slot index is  physical_block * 16 + offset  (offset < 16).
+ *  - Pointers are device pointers unless stated; all buffers are owned and
+ *    allocated by the caller.  The library keeps no state and allocates
+ *    nothing; it never synchronises and never reads device data on the host.
+ *  - Every call only enqueues work on `stream` (0 = the null stream) and
+ *    returns.  Faults inside a kernel surface at the caller's next
+ *    synchronisation.  The library clears the HIP error state on entry.
+ *  - Return value: PA_OK (0) or a negative PA_ERR_* code; argument errors are
+ *    detected on the host before anything is enqueued.
+ *  - Data preconditions that the host cannot check (slot and block ids inside
+ *    the pool, table entries valid for every block a length covers, distinct
+ *    slots, non-overlapping copy pairs) are the caller's.  The kernels never
+ *    access memory outside the pools for ids outside [0, NB): such slots,
+ *    pairs and blocks are skipped, which leaves results undefined but safe.
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size     */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size not 16, G > 4   */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
+  PA_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError)        */
+};
+
+#define PA_BLOCK_SIZE 16
+
+/*
+ * Append: write each new token's K and V rows into its slot ([AQ] "TL;DR",
+ * [TT] "Blocks and Block Tables").
+ *
+ *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], contiguous
+ *   k_cache       K pool (layout above), v_cache V pool
+ *   slot_mapping  int64 [num_tokens]; token t goes to slot slot_mapping[t];
+ *                 negative = padding, skipped; >= num_blocks*16 is skipped
+ *   Two tokens with the same non-negative slot in one call race (precondition).
+ *   The write is a bit copy.  num_tokens == 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, hipStream_t stream);
+
+/*
+ * Copy-on-write: for each pair (src, dst) copy the whole block, K and V, all
+ * KV heads ([TT] "Sharing Blocks"; [AQ] sharing bullet of "PagedAttention:
+ * a block table for the KV cache").
+ *
+ *   block_mapping int64 [num_pairs][2] = (src, dst), device memory
+ *   Pairs with src == dst, or an id outside [0, num_blocks), are skipped.
+ *   Preconditions: dsts distinct and none of them is also a src.
+ *   Reference counting and the decision to copy are the caller's.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                   int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * The partition size pa_decode uses when it is passed partition_size == 0:
+ * a multiple of 64 tokens chosen from the batch shape so the GPU has enough
+ * independent work.  Returns a negative PA_ERR_* code for invalid sizes.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t max_context_len);
+
+/*
+ * Workspace bytes pa_decode needs for these sizes (0 when no sequence is
+ * split).  partition_size as for pa_decode.  Returns 0 for invalid sizes.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size);
+
+/*
+ * Decode attention through the block table ([AQ] "PagedAttention: a block
+ * table for the KV cache" and "FAQ"; [TT] "Blocks and Block Tables"; [AG]
+ * "Paged attention").  For sequence s and query head h, with
+ * G = num_q_heads / num_kv_heads and KV head kh = h / G:
+ *
+ *   out[s][h] = softmax_i( scale * q[s][h] . K_s[kh][i] ) V_s[kh][i],
+ *               i = 0 .. context_lens[s]-1,
+ *
+ * where position i of sequence s is slot offset i%16 of physical block
+ * block_tables[s][i/16].  The unused tail of the last block never enters the
+ * result, whatever it holds (NaN included).  A length of 0 gives a zero row.
+ *
+ *   out               fp16 [num_seqs][num_q_heads][head_dim]
+ *   q                 fp16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq] (row stride
+ *                     max_blocks_per_seq); entries past ceil(len/16) unread
+ *   context_lens      int32 [num_seqs]; values are clamped to [0, max_context_len]
+ *   scale             softmax scale (e.g. 1/sqrt(head_dim))
+ *   max_context_len   host-known upper bound of context_lens, at most
+ *                     max_blocks_per_seq*16; sizes the launch grid
+ *   partition_size    0 = automatic; else a multiple of 64: long contexts are
+ *                     split into partitions of this many tokens whose partial
+ *                     results are merged by a second kernel (log-sum-exp
+ *                     rescaling); a value >= max_context_len disables splitting
+ *   workspace         device buffer of at least pa_decode_workspace_size(...)
+ *                     bytes, 256-byte aligned; may be NULL when that size is 0
+ *
+ * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
+ * the value product rounded to fp16); out is rounded to nearest even fp16.
+ * 1 <= G <= 4.  num_seqs == 0 is a no-op.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+              int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text for a PA_* code (static storage, never NULL). */
+const char* pa_strerror(int code);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

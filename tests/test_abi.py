@@ -1,0 +1,117 @@
+"""The C-ABI library on the CPU: it loads, exports what include/pa.h declares,
+and rejects bad arguments on the host before any HIP call.  Calls here never
+reach a kernel launch (no GPU in this container)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_59_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding._LIB_PATH):
+        pytest.fail("libpagedkv.so is not built (python -m paged_kv_cache_59_amd.build)")
+    return binding.lib()
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_copy_blocks"):
+        assert n in names
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding._LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(L, name)
+
+
+def test_version_and_messages(L):
+    assert L.pa_version() >= 100
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.pa_strerror(code)
+
+
+NULL = None
+
+
+def dec(L, **kw):
+    args = dict(out=1, q=1, k=1, v=1, tab=1, lens=1, scale=0.125, hkv=8, S=4, hq=32, D=128,
+                bs=16, mb=8, nb=100, maxctx=100, part=0, ws=NULL, wsb=0)
+    args.update(kw)
+    a = args
+    return L.pa_decode(a["out"], a["q"], a["k"], a["v"], a["tab"], a["lens"], a["scale"],
+                       a["hkv"], a["S"], a["hq"], a["D"], a["bs"], a["mb"], a["nb"], a["maxctx"],
+                       a["part"], a["ws"], a["wsb"], NULL)
+
+
+def test_decode_argument_errors(L):
+    E = binding
+    assert dec(L, hq=30) == E.PA_ERR_INVALID_ARG            # Hq % Hkv != 0
+    assert dec(L, D=96) == E.PA_ERR_UNSUPPORTED
+    assert dec(L, bs=32) == E.PA_ERR_UNSUPPORTED
+    assert dec(L, hq=64) == E.PA_ERR_UNSUPPORTED             # G = 8
+    assert dec(L, maxctx=129) == E.PA_ERR_INVALID_ARG        # > 8 blocks * 16
+    assert dec(L, S=-1) == E.PA_ERR_INVALID_ARG
+    assert dec(L, part=100) == E.PA_ERR_INVALID_ARG          # not a multiple of 64
+    assert dec(L, scale=float("nan")) == E.PA_ERR_INVALID_ARG
+    assert dec(L, out=NULL) == E.PA_ERR_INVALID_ARG
+    assert dec(L, S=0, out=NULL) == E.PA_OK                  # empty batch: no-op
+    # a split launch needs a workspace
+    assert dec(L, maxctx=128, part=64) == E.PA_ERR_WORKSPACE
+    need = L.pa_decode_workspace_size(4, 32, 8, 128, 128, 64)
+    assert need == 4 * 32 * 2 * 2 * 4 + 4 * 32 * 2 * 128 * 4 or need >= 4 * 32 * 2 * 130 * 4
+    assert dec(L, maxctx=128, part=64, ws=256, wsb=need - 1) == E.PA_ERR_WORKSPACE
+    assert dec(L, maxctx=128, part=64, ws=257, wsb=need) == E.PA_ERR_WORKSPACE  # misaligned
+
+
+def test_workspace_sizes(L):
+    assert L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 4096) == 0     # unsplit
+    assert L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 2048) == 0
+    big = L.pa_decode_workspace_size(16, 32, 8, 128, 32768, 512)
+    assert big >= 16 * 32 * 64 * 130 * 4
+    assert L.pa_decode_workspace_size(-1, 32, 8, 128, 10, 0) == 0
+    assert L.pa_decode_partition_size(64, 8, 2048) % 64 == 0
+    assert L.pa_decode_partition_size(-1, 8, 2048) < 0
+    # the automatic choice never exceeds 1024 partitions
+    p = L.pa_decode_partition_size(1, 1, 2_000_000)
+    assert -(-2_000_000 // p) <= 1024
+
+
+def test_cache_op_argument_errors(L):
+    E = binding
+    r = L.pa_reshape_and_cache
+    assert r(1, 1, 1, 1, 1, 4, 8, 96, 16, 10, NULL) == E.PA_ERR_UNSUPPORTED
+    assert r(1, 1, 1, 1, 1, 4, 8, 128, 8, 10, NULL) == E.PA_ERR_UNSUPPORTED
+    assert r(1, 1, 1, 1, 1, -1, 8, 128, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
+    assert r(NULL, 1, 1, 1, 1, 4, 8, 128, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
+    assert r(NULL, NULL, NULL, NULL, NULL, 0, 8, 128, 16, 10, NULL) == E.PA_OK
+    c = L.pa_copy_blocks
+    assert c(1, 1, 1, 2, 8, 64, 16, 0, NULL) == E.PA_ERR_INVALID_ARG
+    assert c(1, 1, 1, 2, 8, 80, 16, 10, NULL) == E.PA_ERR_UNSUPPORTED
+    assert c(1, NULL, 1, 2, 8, 64, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
+    assert c(NULL, NULL, NULL, 0, 8, 64, 16, 10, NULL) == E.PA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros(4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        binding.pa_copy_blocks(t, t, torch.zeros(1, 2, dtype=torch.int64))
