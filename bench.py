@@ -10,9 +10,9 @@ serve a step from the previous one's reads.
 
 Prints one JSON line:
   value        bytes the step must move / step time, GB/s
-  roofline     the decode kernels (split-context partition kernel plus, when
-               used, the merge) timed with HIP events on their stream:
-               algorithmic decode bytes / mean launch duration vs 8 TB/s
+  roofline     the decode kernel (one launch: balanced persistent workers with
+               the merge of cut sequences fused) timed with HIP events on its
+               stream: algorithmic decode bytes / mean launch duration vs 8 TB/s
   cpu_baseline the CPU oracle on this host on one whole step of the same batch
 """
 import argparse
@@ -36,8 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_b64")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--num-workers", type=int, default=0)
     ap.add_argument("--replica-gb", type=float, default=2.0)
+    ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     return ap.parse_args()
@@ -81,7 +82,7 @@ def main():
 
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
-    w = wl.make_named(args.workload)
+    w = wl.make_named(args.workload, placement=args.placement)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, tab, lens = t(w.q), t(w.block_tables), t(w.context_lens)
     k_new, v_new, slots = t(w.k_new), t(w.v_new), t(w.slot_mapping)
@@ -91,11 +92,8 @@ def main():
     R = max(1, int(np.ceil(args.replica_gb * 1e9 / pool_bytes)))
     replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
-    P = args.partition_size or pk.pa_decode_partition_size(w.num_seqs, w.num_kv_heads,
-                                                           w.max_context_len)
-    ws_bytes = pk.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                           w.head_dim, w.max_context_len, P)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    workers = args.num_workers or pk.pa_decode_num_workers()
+    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, workers)
     stream = torch.cuda.current_stream()
     has_copy = w.block_mapping.shape[0] > 0
 
@@ -107,7 +105,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         pk.pa_decode(out, q, kc, vc, tab, lens, float(w.scale), w.num_kv_heads,
-                     max_context_len=w.max_context_len, partition_size=P, workspace=ws)
+                     max_context_len=w.max_context_len, num_workers=workers, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -150,14 +148,14 @@ def main():
             "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
             "max_context_len": w.max_context_len, "mean_context_len": float(w.context_lens.mean()),
-            "seed": w.seed, "partition_size": P, "replicas": R, "accumulate": "f32",
-            "copies_per_step": int(w.block_mapping.shape[0]),
+            "seed": w.seed, "num_workers": workers, "replicas": R, "accumulate": "f32",
+            "copies_per_step": int(w.block_mapping.shape[0]), "placement": args.placement,
             "step_bytes": step_bytes, "decode_bytes": w.decode_bytes(),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "decode_partition_kernel (+ decode_reduce_kernel when split)",
+            "kernel": "decode_kernel",
             "mean_us": round(dec_mean_s * 1e6, 3),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
             "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),

@@ -37,8 +37,9 @@
  *    so one (block, head) tile is 16*D contiguous elements in both pools.
  *  - A slot index is  physical_block * 16 + offset  (offset < 16).
  *  - Pointers are device pointers unless stated; all buffers are owned and
- *    allocated by the caller.  The library keeps no state and allocates
- *    nothing; it never synchronises and never reads device data on the host.
+ *    allocated by the caller.  The library allocates nothing and keeps no
+ *    state beyond a per-device cache of the compute-unit count; it never
+ *    synchronises and never reads device data on the host.
  *  - Every call only enqueues work on `stream` (0 = the null stream) and
  *    returns.  Faults inside a kernel surface at the caller's next
  *    synchronisation.  The library clears the HIP error state on entry.
@@ -66,7 +67,7 @@ enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size     */
   PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size not 16, G > 4   */
   PA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
-  PA_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError)        */
+  PA_ERR_HIP = -4,         /* a HIP call or kernel launch failed              */
 };
 
 #define PA_BLOCK_SIZE 16
@@ -102,20 +103,20 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                    int32_t block_size, int64_t num_blocks, hipStream_t stream);
 
 /*
- * The partition size pa_decode uses when it is passed partition_size == 0:
- * a multiple of 64 tokens chosen from the batch shape so the GPU has enough
- * independent work.  Returns a negative PA_ERR_* code for invalid sizes.
+ * Number of decode workers (wavefronts of 64 lanes) pa_decode uses when it is
+ * passed num_workers == 0: 8 per compute unit of the current HIP device.
+ * Returns a negative PA_ERR_* code if the device cannot be queried.
  */
-int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                 int32_t max_context_len);
+int32_t pa_decode_num_workers(void);
 
 /*
- * Workspace bytes pa_decode needs for these sizes (0 when no sequence is
- * split).  partition_size as for pa_decode.  Returns 0 for invalid sizes.
+ * Workspace bytes pa_decode needs for these sizes; num_workers as for
+ * pa_decode (0 = automatic, on the current device).  Returns 0 for invalid
+ * sizes.  The workspace holds one arrival counter per (sequence, KV head) and
+ * two partial-result slots per worker.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_context_len,
-                                int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t num_workers);
 
 /*
  * Decode attention through the block table ([AQ] "PagedAttention: a block
@@ -135,15 +136,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   block_tables      int32 [num_seqs][max_blocks_per_seq] (row stride
  *                     max_blocks_per_seq); entries past ceil(len/16) unread
  *   context_lens      int32 [num_seqs]; values are clamped to [0, max_context_len]
- *   scale             softmax scale (e.g. 1/sqrt(head_dim))
+ *   scale             softmax scale (e.g. 1/sqrt(head_dim)), finite
  *   max_context_len   host-known upper bound of context_lens, at most
- *                     max_blocks_per_seq*16; sizes the launch grid
- *   partition_size    0 = automatic; else a multiple of 64: long contexts are
- *                     split into partitions of this many tokens whose partial
- *                     results are merged by a second kernel (log-sum-exp
- *                     rescaling); a value >= max_context_len disables splitting
+ *                     max_blocks_per_seq*16
+ *   num_workers       0 = automatic (pa_decode_num_workers()); else the number
+ *                     of persistent wavefronts that share the work.  Every
+ *                     (sequence, KV head) is cut into 64-token units and the
+ *                     workers take equal contiguous shares of all units; a
+ *                     sequence cut between workers is merged by the last of
+ *                     them to finish (log-sum-exp rescaling).  1 = no cuts.
  *   workspace         device buffer of at least pa_decode_workspace_size(...)
- *                     bytes, 256-byte aligned; may be NULL when that size is 0
+ *                     bytes, 256-byte aligned, ZERO-FILLED before its first
+ *                     use; each call leaves its counters at zero again, so a
+ *                     workspace is reusable without clearing.  Two calls that
+ *                     overlap in time must not share one workspace.
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.
@@ -153,7 +159,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               const int32_t* block_tables, const int32_t* context_lens, float scale,
               int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-              int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+              int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Text for a PA_* code (static storage, never NULL). */

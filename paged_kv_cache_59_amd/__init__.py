@@ -8,14 +8,16 @@ from .binding import (  # noqa: F401
     PagedKVError,
     pa_copy_blocks,
     pa_decode,
-    pa_decode_partition_size,
+    pa_decode_num_workers,
     pa_decode_workspace_size,
     pa_reshape_and_cache,
     pa_strerror,
     pa_version,
+    new_workspace,
 )
 
 __all__ = [
-    "PagedKVError", "pa_copy_blocks", "pa_decode", "pa_decode_partition_size",
+    "PagedKVError", "pa_copy_blocks", "pa_decode", "pa_decode_num_workers",
     "pa_decode_workspace_size", "pa_reshape_and_cache", "pa_strerror", "pa_version",
+    "new_workspace",
 ]

@@ -25,7 +25,7 @@ PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
-            "pa_decode_partition_size", "pa_strerror", "pa_version")
+            "pa_decode_num_workers", "pa_strerror", "pa_version")
 
 
 class PagedKVError(RuntimeError):
@@ -49,9 +49,9 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
-    L.pa_decode_partition_size.argtypes = [i32, i32, i32]
-    L.pa_decode_partition_size.restype = i32
-    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pa_decode_num_workers.argtypes = []
+    L.pa_decode_num_workers.restype = i32
+    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     L.pa_decode_workspace_size.restype = sz
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32,
                             i32, i64, i32, i32, vp, sz, vp]
@@ -131,25 +131,31 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     _check(code, "pa_copy_blocks")
 
 
-def pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len) -> int:
-    p = int(lib().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len))
-    _check(min(p, 0), "pa_decode_partition_size")
-    return p
+def pa_decode_num_workers() -> int:
+    """Workers pa_decode uses by default on the current device (8 per CU)."""
+    n = int(lib().pa_decode_num_workers())
+    _check(min(n, 0), "pa_decode_num_workers")
+    return n
 
 
-def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                             partition_size=0) -> int:
-    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                              max_context_len, partition_size))
+def pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, num_workers=0) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, num_workers))
+
+
+def new_workspace(num_seqs, num_kv_heads, head_dim, num_workers=0, device="cuda"):
+    """A zero-filled decode workspace (the counters must start at zero)."""
+    n = pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, num_workers)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
-              max_context_len=None, partition_size=0, workspace=None, stream=None):
+              max_context_len=None, num_workers=0, workspace=None, stream=None):
     """Paged decode attention; writes out [S, Hq, D] fp16 and returns it.
 
     ``max_context_len`` is the host-known bound of ``context_lens``; when None
-    it is read back from the GPU (one synchronising copy).  ``workspace`` is a
-    uint8 GPU tensor; when None and one is needed, torch allocates it.
+    the table width bound ``max_blocks_per_seq * 16`` is used.  ``workspace``
+    is a zero-filled uint8 GPU tensor of pa_decode_workspace_size(...) bytes
+    (reusable across calls that do not overlap); when None a fresh one is made.
     """
     _dev(out, "out", torch.float16)
     _dev(q, "q", torch.float16)
@@ -167,19 +173,16 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], context_lens [num_seqs]")
     mb = int(block_tables.shape[1])
     if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if S else 0
-    need = pa_decode_workspace_size(S, hq, hkv, d, max_context_len, partition_size)
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        _dev(workspace, "workspace", torch.uint8)
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+        max_context_len = mb * BLOCK_SIZE
+    if workspace is None:
+        workspace = new_workspace(S, hkv, d, num_workers, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
     code = lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv,
                            S, hq, d, BLOCK_SIZE, mb, nb, int(max_context_len),
-                           int(partition_size), ws_ptr, ws_bytes, _stream(q, stream))
+                           int(num_workers), workspace.data_ptr(), workspace.numel(),
+                           _stream(q, stream))
     _check(code, "pa_decode")
     return out

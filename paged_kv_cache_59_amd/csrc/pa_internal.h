@@ -14,17 +14,20 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kBlockSize = 16;   // token slots per block
 constexpr int kChunk = 8;        // fp16 elements per 16-byte chunk
 constexpr int kGroupTokens = 64; // tokens one wave handles per step of its loop
-constexpr int kMaxPartitions = 1024;
+constexpr int kWorkersPerCU = 8;  // decode waves per compute unit (2 per SIMD)
+constexpr int kMaxWorkers = 1 << 20;
 
-// Workspace geometry for split contexts: per (seq, q head, partition) one
-// (max, sum) pair and one D-vector of unnormalised fp32 output.
+// Decode workspace: one arrival counter per (sequence, KV head) run, then two
+// partial slots per worker, each holding for 4 query-head rows a (max, sum)
+// pair and a D-vector of unnormalised fp32 output.
 struct DecodeWorkspace {
-  float* ml;  // [S][Hq][NP][2]
-  float* o;   // [S][Hq][NP][D]
+  int* counters;  // [S][Hkv], zero between calls
+  float* ml;      // [2*workers][4][2]
+  float* o;       // [2*workers][4][D]
 };
 
-size_t decode_workspace_bytes(int64_t S, int64_t Hq, int64_t D, int64_t NP);
-DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hq, int64_t NP);
+size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
+DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t workers);
 
 hipError_t launch_reshape_and_cache(const half_t* k, const half_t* v, half_t* k_cache,
                                     half_t* v_cache, const int64_t* slot_mapping,
@@ -47,9 +50,8 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int64_t num_blocks;
   int max_context_len;
-  int partition_size;
-  int num_partitions;  // ceil(max_context_len / partition_size), >= 1
-  DecodeWorkspace ws;  // unused when num_partitions == 1
+  int num_workers;  // grid size: persistent waves sharing the work
+  DecodeWorkspace ws;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -249,7 +249,7 @@ def _set_slot_bits(k_u16, v_u16, block: int, offset: int, bits) -> None:
 def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=None,
                   len_range=None, num_seqs=None, max_context_bound=None, pool_factor=1.25,
                   num_blocks=None, prefix_groups=0, prefix_len=0, suffix_range=None,
-                  tail="canary", scale=None) -> Workload:
+                  tail="canary", scale=None, placement="shuffled") -> Workload:
     """Build one decode step: pools, tables, lengths, q, new k/v, slots, CoW pairs.
 
     ``context_lens`` (or ``len_range`` + ``num_seqs``) give each sequence's
@@ -258,7 +258,9 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
     (a multiple of 16) followed by private suffixes drawn from
     ``suffix_range``; the block holding each sequence's append position is
     shared with a forked sibling, so the append first copies it
-    (copy-on-write).  ``tail`` is "canary" or "stale".
+    (copy-on-write).  ``tail`` is "canary" or "stale".  ``placement`` is
+    "shuffled" (free list = a seeded permutation of the pool) or "sequential"
+    (free list in pool order: each sequence's blocks end up contiguous).
     """
     assert num_q_heads % num_kv_heads == 0 and head_dim % CHUNK == 0
     rng = np.random.default_rng(seed)
@@ -294,8 +296,9 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
         num_blocks = max(1, math.ceil(pool_factor * needed))
     NB = int(num_blocks)
 
-    # 2. placement
-    bm = BlockManager(NB, free_order=rng.permutation(NB))
+    # 2. placement (the permutation is drawn in both modes, to keep the stream)
+    perm = rng.permutation(NB)
+    bm = BlockManager(NB, free_order=perm if placement == "shuffled" else None)
     slots = np.full(S, -1, dtype=np.int64)
     cows = []
     shadows = []
@@ -378,7 +381,7 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
         context_lens=lens.astype(np.int32), k_new=k_new, v_new=v_new,
         slot_mapping=slots, block_mapping=np.asarray(cows, dtype=np.int64).reshape(-1, 2),
         meta={"tail": tail, "prefix_groups": prefix_groups, "prefix_len": prefix_len,
-              "pool_factor": pool_factor},
+              "pool_factor": pool_factor, "placement": placement},
     )
 
 

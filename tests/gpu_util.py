@@ -34,21 +34,21 @@ def to_device(w):
     return d
 
 
-def gpu_decode(w, d, partition_size=0, max_context_len=None):
+def gpu_decode(w, d, num_workers=0, max_context_len=None, workspace=None):
     mcl = w.max_context_len if max_context_len is None else max_context_len
     pk.pa_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                  d["context_lens"], float(w.scale), w.num_kv_heads, max_context_len=mcl,
-                 partition_size=partition_size)
+                 num_workers=num_workers, workspace=workspace)
     torch.cuda.synchronize()
     return d["out"].cpu().numpy()
 
 
-def gpu_step(w, d, partition_size=0):
+def gpu_step(w, d, num_workers=0):
     """copy-on-write, append, decode on one stream; returns out as numpy fp16."""
     if w.block_mapping.shape[0]:
         pk.pa_copy_blocks(d["k_cache"], d["v_cache"], d["block_mapping"])
     pk.pa_reshape_and_cache(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
-    return gpu_decode(w, d, partition_size)
+    return gpu_decode(w, d, num_workers)
 
 
 def oracle_pools(w):

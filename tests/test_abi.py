@@ -54,12 +54,12 @@ NULL = None
 
 def dec(L, **kw):
     args = dict(out=1, q=1, k=1, v=1, tab=1, lens=1, scale=0.125, hkv=8, S=4, hq=32, D=128,
-                bs=16, mb=8, nb=100, maxctx=100, part=0, ws=NULL, wsb=0)
+                bs=16, mb=8, nb=100, maxctx=100, workers=64, ws=NULL, wsb=0)
     args.update(kw)
     a = args
     return L.pa_decode(a["out"], a["q"], a["k"], a["v"], a["tab"], a["lens"], a["scale"],
                        a["hkv"], a["S"], a["hq"], a["D"], a["bs"], a["mb"], a["nb"], a["maxctx"],
-                       a["part"], a["ws"], a["wsb"], NULL)
+                       a["workers"], a["ws"], a["wsb"], NULL)
 
 
 def test_decode_argument_errors(L):
@@ -70,29 +70,25 @@ def test_decode_argument_errors(L):
     assert dec(L, hq=64) == E.PA_ERR_UNSUPPORTED             # G = 8
     assert dec(L, maxctx=129) == E.PA_ERR_INVALID_ARG        # > 8 blocks * 16
     assert dec(L, S=-1) == E.PA_ERR_INVALID_ARG
-    assert dec(L, part=100) == E.PA_ERR_INVALID_ARG          # not a multiple of 64
+    assert dec(L, workers=-3) == E.PA_ERR_INVALID_ARG
     assert dec(L, scale=float("nan")) == E.PA_ERR_INVALID_ARG
     assert dec(L, out=NULL) == E.PA_ERR_INVALID_ARG
     assert dec(L, S=0, out=NULL) == E.PA_OK                  # empty batch: no-op
-    # a split launch needs a workspace
-    assert dec(L, maxctx=128, part=64) == E.PA_ERR_WORKSPACE
-    need = L.pa_decode_workspace_size(4, 32, 8, 128, 128, 64)
-    assert need == 4 * 32 * 2 * 2 * 4 + 4 * 32 * 2 * 128 * 4 or need >= 4 * 32 * 2 * 130 * 4
-    assert dec(L, maxctx=128, part=64, ws=256, wsb=need - 1) == E.PA_ERR_WORKSPACE
-    assert dec(L, maxctx=128, part=64, ws=257, wsb=need) == E.PA_ERR_WORKSPACE  # misaligned
+    # a decode always needs its workspace
+    assert dec(L) == E.PA_ERR_WORKSPACE
+    need = L.pa_decode_workspace_size(4, 8, 128, 64)
+    assert dec(L, ws=256, wsb=need - 1) == E.PA_ERR_WORKSPACE
+    assert dec(L, ws=257, wsb=need) == E.PA_ERR_WORKSPACE    # misaligned
 
 
 def test_workspace_sizes(L):
-    assert L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 4096) == 0     # unsplit
-    assert L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 2048) == 0
-    big = L.pa_decode_workspace_size(16, 32, 8, 128, 32768, 512)
-    assert big >= 16 * 32 * 64 * 130 * 4
-    assert L.pa_decode_workspace_size(-1, 32, 8, 128, 10, 0) == 0
-    assert L.pa_decode_partition_size(64, 8, 2048) % 64 == 0
-    assert L.pa_decode_partition_size(-1, 8, 2048) < 0
-    # the automatic choice never exceeds 1024 partitions
-    p = L.pa_decode_partition_size(1, 1, 2_000_000)
-    assert -(-2_000_000 // p) <= 1024
+    # counters for 64 x 8 runs, then 2 slots per worker of 4 rows x (2 + 128) floats
+    need = L.pa_decode_workspace_size(64, 8, 128, 2048)
+    assert need >= 64 * 8 * 4 + 2 * 2048 * 4 * 130 * 4
+    assert need < 64 * 8 * 4 + 2 * 2048 * 4 * 130 * 4 + 1024
+    assert L.pa_decode_workspace_size(64, 8, 64, 2048) < need
+    assert L.pa_decode_workspace_size(-1, 8, 128, 16) == 0
+    assert L.pa_decode_workspace_size(4, 8, 128, -2) == 0
 
 
 def test_cache_op_argument_errors(L):

@@ -1,5 +1,5 @@
 """Full-size decode batches on the GPU, in the launch configuration the
-benchmark times (automatic partition size), against the oracle.
+benchmark times (automatic worker count), against the oracle.
 
 Pools are compared bit for bit after the copy-on-write and the append; the
 attention output is compared on every sequence, or on a sample of sequences

@@ -1,8 +1,8 @@
 """Parity of the HIP path (through the C-ABI) with the CPU oracle, on the GPU.
 
-Small cases span several 64-token groups, several partitions and ragged
-tails; edge cases cover empty rows, single tokens, block and partition
-boundaries, NaN/+-65504 tails and stale tails.  Full-size decode batches are
+Small cases span several 64-token units, many ways of cutting the work
+between workers and ragged tails; edge cases cover empty rows, single tokens,
+block and unit boundaries, NaN/+-65504 tails and stale tails.  Full-size decode batches are
 in test_gpu_full.py.
 """
 import numpy as np
@@ -20,11 +20,11 @@ pytestmark = pytest.mark.gpu
 EDGE_LENS = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 1025]
 
 
-def run_case(w, partition_size=0, label=""):
+def run_case(w, num_workers=0, label=""):
     log(f"case {label}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"maxctx={w.max_context_len} part={partition_size}")
+        f"maxctx={w.max_context_len} workers={num_workers}")
     d = to_device(w)
-    out = gpu_step(w, d, partition_size)
+    out = gpu_step(w, d, num_workers)
     kc, vc = oracle_pools(w)
     assert_pools_equal(d, kc, vc, label)
     ref = oracle_decode(w, kc, vc)
@@ -39,15 +39,17 @@ def test_tiny_step():
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 4, 64), (12, 4, 128), (32, 8, 128),
                                       (8, 8, 128), (16, 4, 128), (2, 1, 64)])
-@pytest.mark.parametrize("part", [0, 64, 256, 4096])
-def test_decode_shapes_and_partitions(Hq, Hkv, D, part):
+@pytest.mark.parametrize("workers", [0, 1, 7, 64, 5000])
+def test_decode_shapes_and_work_splits(Hq, Hkv, D, workers):
+    """workers=1: one wave does everything; 5000: more workers than units, so
+    every 64-token unit is its own share and every sequence is merged."""
     w = wl.make_workload("edge", 100 + Hq + D, Hq, Hkv, D, context_lens=EDGE_LENS)
-    run_case(w, part, f"edge Hq{Hq} Hkv{Hkv} D{D} part{part}")
+    run_case(w, workers, f"edge Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
 
 
 def test_ragged_random_lengths_many_seqs():
     w = wl.make_workload("ragged", 201, 32, 8, 128, len_range=(1, 700), num_seqs=40)
-    run_case(w, 128, "ragged 40 seqs part128")
+    run_case(w, 96, "ragged 40 seqs 96 workers")
 
 
 def test_stale_tails():
@@ -59,12 +61,12 @@ def test_peaky_softmax():
     """scale x 8: weights close to one-hot, the running max moves a lot."""
     w = wl.make_workload("peaky", 203, 32, 8, 128, len_range=(100, 900), num_seqs=8,
                          scale=8.0 / np.sqrt(128))
-    run_case(w, 128, "peaky")
+    run_case(w, 24, "peaky")
 
 
 def test_zero_length_rows():
     w = wl.make_workload("zero", 204, 8, 2, 64, context_lens=[0, 5, 0, 70])
-    out, _ = run_case(w, 64, "zero-length rows")
+    out, _ = run_case(w, 3, "zero-length rows")
     assert (out[0] == 0).all() and (out[2] == 0).all()
 
 
@@ -90,7 +92,7 @@ def test_constant_values_give_that_constant():
     w.v_cache[...] = np.broadcast_to(c[None, None, None, :, None], w.v_cache.shape)
     w.v_new[...] = c
     d = to_device(w)
-    out = gpu_step(w, d, 64)
+    out = gpu_step(w, d, 16)
     assert np.array_equal(out.view(np.uint16),
                           np.broadcast_to(c, out.shape).view(np.uint16))
 
@@ -98,7 +100,7 @@ def test_constant_values_give_that_constant():
 def test_permuted_placement_bit_identical_on_gpu():
     w = wl.make_workload("perm", 208, 32, 8, 128, len_range=(1, 600), num_seqs=10)
     d = to_device(w)
-    a = gpu_step(w, d, 128)
+    a = gpu_step(w, d, 40)
     perm = np.random.default_rng(3).permutation(w.num_blocks)
     kc = torch.empty_like(d["k_cache"])
     vc = torch.empty_like(d["v_cache"])
@@ -107,7 +109,7 @@ def test_permuted_placement_bit_identical_on_gpu():
     tab = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
     d2 = dict(d, k_cache=kc, v_cache=vc, block_tables=dev(tab),
               out=torch.empty_like(d["out"]))
-    b = gpu_decode(w, d2, 128)
+    b = gpu_decode(w, d2, 40)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
@@ -115,7 +117,7 @@ def test_shared_vs_private_bit_identical_on_gpu():
     w = wl.make_workload("share", 209, 32, 8, 128, num_seqs=8, prefix_groups=1, prefix_len=128,
                          suffix_range=(16, 100))
     d = to_device(w)
-    a = gpu_step(w, d, 64)
+    a = gpu_step(w, d, 32)
     # private copies of every block each sequence reads
     rows = []
     nxt = w.num_blocks
@@ -130,18 +132,18 @@ def test_shared_vs_private_bit_identical_on_gpu():
     kc = torch.cat([d["k_cache"], d["k_cache"][src]])
     vc = torch.cat([d["v_cache"], d["v_cache"][src]])
     d2 = dict(d, k_cache=kc, v_cache=vc, block_tables=dev(tab), out=torch.empty_like(d["out"]))
-    b = gpu_decode(w, d2, 64)
+    b = gpu_decode(w, d2, 32)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
 def test_split_vs_unsplit():
     w = wl.make_workload("split", 210, 32, 8, 128, len_range=(600, 3000), num_seqs=6)
     d = to_device(w)
-    a = gpu_step(w, d, 64)
-    b = gpu_decode(w, dict(d, out=torch.empty_like(d["out"])), 4096)
+    a = gpu_step(w, d, 4096)
+    b = gpu_decode(w, dict(d, out=torch.empty_like(d["out"])), 1)
     kc, vc = oracle_pools(w)
     ref = oracle_decode(w, kc, vc)
-    compare(a, ref, "split 64")
+    compare(a, ref, "split 4096 workers")
     compare(b, ref, "unsplit")
     compare(a, b.astype(np.float64), "split vs unsplit")
 
@@ -149,8 +151,8 @@ def test_split_vs_unsplit():
 def test_lengths_above_bound_are_clamped():
     w = wl.make_workload("clamp", 211, 4, 4, 64, context_lens=[30, 90], max_context_bound=128)
     d = to_device(w)
-    gpu_step(w, d, 64)
-    out = gpu_decode(w, d, 64, max_context_len=60)
+    gpu_step(w, d, 5)
+    out = gpu_decode(w, d, 5, max_context_len=60)
     kc, vc = oracle_pools(w)
     ref = oracle.decode(w.q, kc, vc, w.block_tables, np.minimum(w.context_lens, 60), w.scale, 4)
     compare(out, ref, "clamped")
@@ -191,7 +193,11 @@ def test_empty_batch_and_errors_on_gpu():
                        None, 0, stream) == pk.PA_OK
     with pytest.raises(pk.PagedKVError):
         pk.pa_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                     d["context_lens"], 0.1, 2, max_context_len=10, partition_size=96)
+                     d["context_lens"], 0.1, 2, max_context_len=10, num_workers=-1)
+    with pytest.raises(pk.PagedKVError):         # workspace too small
+        pk.pa_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                     d["context_lens"], 0.1, 2, max_context_len=10,
+                     workspace=torch.zeros(64, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
 
 
@@ -209,3 +215,24 @@ def test_side_stream():
     kc, vc = oracle_pools(w)
     compare(d["out"].cpu().numpy(), oracle_decode(w, kc, vc), "side stream")
 
+
+
+def test_workspace_reuse_leaves_counters_zero():
+    """Every call leaves the arrival counters at zero: the same workspace serves
+    consecutive calls, also with a different batch shape."""
+    w1 = wl.make_workload("reuse1", 216, 32, 8, 128, len_range=(300, 900), num_seqs=7)
+    w2 = wl.make_workload("reuse2", 217, 32, 8, 128, len_range=(1, 500), num_seqs=5)
+    workers = 50
+    ws = pk.new_workspace(7, 8, 128, workers)
+    for rep in range(3):
+        for w in (w1, w2):
+            d = to_device(w)
+            if w.block_mapping.shape[0]:
+                pk.pa_copy_blocks(d["k_cache"], d["v_cache"], d["block_mapping"])
+            pk.pa_reshape_and_cache(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"],
+                                    d["slot_mapping"])
+            out = gpu_decode(w, d, workers, workspace=ws)
+            kc, vc = oracle_pools(w)
+            compare(out, oracle_decode(w, kc, vc), f"reuse {w.name} rep{rep}")
+            counters = ws[: 7 * 8 * 4].view(torch.int32).cpu().numpy()
+            assert (counters == 0).all()
