@@ -14,7 +14,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kBlockSize = 16;   // token slots per block
 constexpr int kChunk = 8;        // fp16 elements per 16-byte chunk
 constexpr int kGroupTokens = 64; // tokens one wave handles per step of its loop
-constexpr int kWorkersPerCU = 8;  // decode waves per compute unit (2 per SIMD)
+constexpr int kWorkersPerCU = 2;  // decode waves per compute unit
 constexpr int kMaxWorkers = 1 << 20;
 
 // Decode workspace: one arrival counter per (sequence, KV head) run, then two
