@@ -12,7 +12,9 @@ Prints one JSON line:
   value        bytes the step must move / step time, GB/s
   roofline     the decode kernel (one launch: balanced persistent workers with
                the merge of cut sequences fused) timed with HIP events on its
-               stream: algorithmic decode bytes / mean launch duration vs 8 TB/s
+               stream: algorithmic decode bytes / mean launch duration vs 8 TB/s;
+               `traffic` is the HBM bytes per launch from the committed
+               rocprofv3 counter summary (profiles/), null if the kernel changed
   cpu_baseline the CPU oracle on this host on one whole step of the same batch
 """
 import argparse
@@ -41,7 +43,37 @@ def parse():
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run `steps` plain device copies of this many MiB (an elementwise "
+                         "kernel reading and writing known bytes, to calibrate HBM counters)")
     return ap.parse_args()
+
+
+def copy_probe(args):
+    import torch
+    n = args.copy_probe_mb << 20
+    src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "launches": args.steps}), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode dispatch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or None when
+    there are none for this workload or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return int(round(rec["traffic_bytes_per_dispatch"]))
 
 
 def cpu_baseline(w, budget_s):
@@ -76,6 +108,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mb:
+        copy_probe(args)
+        return
     import torch
     from paged_kv_cache_59_amd import binding as pk
     from paged_kv_cache_59_amd import workloads as wl
@@ -154,7 +189,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
             "kernel": "decode_kernel",
             "mean_us": round(dec_mean_s * 1e6, 3),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
