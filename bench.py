@@ -128,7 +128,7 @@ def main():
     replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     workers = args.num_workers or pk.pa_decode_num_workers()
-    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, workers)
+    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, workers)
     stream = torch.cuda.current_stream()
     has_copy = w.block_mapping.shape[0] > 0
 

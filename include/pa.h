@@ -104,19 +104,21 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
 
 /*
  * Number of decode workers (wavefronts of 64 lanes) pa_decode uses when it is
- * passed num_workers == 0: 8 per compute unit of the current HIP device.
+ * passed num_workers == 0: 2 per compute unit of the current HIP device.
  * Returns a negative PA_ERR_* code if the device cannot be queried.
  */
 int32_t pa_decode_num_workers(void);
 
 /*
- * Workspace bytes pa_decode needs for these sizes; num_workers as for
- * pa_decode (0 = automatic, on the current device).  Returns 0 for invalid
- * sizes.  The workspace holds one arrival counter per (sequence, KV head) and
- * two partial-result slots per worker.
+ * Workspace bytes pa_decode needs for these sizes; max_context_len and
+ * num_workers as for pa_decode (0 workers = automatic, on the current
+ * device).  Returns 0 for invalid sizes.  The workspace holds one arrival
+ * counter per (sequence, KV head), the claim counters of the dynamic work
+ * and the partial results of sequences cut between workers.  Batches above
+ * 4096 sequences need no more than 4096 do (they run as several launches).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t num_workers);
+                                int32_t max_context_len, int32_t num_workers);
 
 /*
  * Decode attention through the block table ([AQ] "PagedAttention: a block
@@ -141,15 +143,19 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *                     max_blocks_per_seq*16
  *   num_workers       0 = automatic (pa_decode_num_workers()); else the number
  *                     of persistent wavefronts that share the work.  Every
- *                     (sequence, KV head) is cut into 64-token units and the
- *                     workers take equal contiguous shares of all units; a
- *                     sequence cut between workers is merged by the last of
- *                     them to finish (log-sum-exp rescaling).  1 = no cuts.
- *   workspace         device buffer of at least pa_decode_workspace_size(...)
- *                     bytes, 256-byte aligned, ZERO-FILLED before its first
- *                     use; each call leaves its counters at zero again, so a
- *                     workspace is reusable without clearing.  Two calls that
- *                     overlap in time must not share one workspace.
+ *                     (sequence, KV head) is cut into 64-token units; the
+ *                     first three quarters of each such run go into equal
+ *                     contiguous shares, one per worker, and the rest into
+ *                     small chunks (1, 1, 2, 4, 8.. units from the run's end)
+ *                     that workers claim as they finish, largest first.  A
+ *                     sequence cut into several pieces is merged by the last
+ *                     piece to finish (log-sum-exp rescaling).
+ *   workspace         device buffer of at least pa_decode_workspace_size(
+ *                     num_seqs, num_kv_heads, head_dim, max_context_len,
+ *                     num_workers) bytes, 256-byte aligned, ZERO-FILLED before
+ *                     its first use; each call leaves its counters at zero
+ *                     again, so a workspace is reusable without clearing.  Two
+ *                     calls that overlap in time must not share one workspace.
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.

@@ -27,6 +27,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics as written: the atomic optimizer rewrites them
+    # into a form whose result is awaited at once, stalling the decode pipeline
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

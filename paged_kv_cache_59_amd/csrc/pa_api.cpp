@@ -4,12 +4,13 @@
 #include "pa.h"
 
 #include <cmath>
+#include <cstdlib>
 
 #include "pa_internal.h"
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 constexpr int kMaxGroup = 4;   // query heads per KV head the decode kernel holds
 constexpr int kMaxGridYZ = 65535;
 
@@ -31,6 +32,15 @@ int32_t auto_workers() {
   const int32_t w = ((cus * pa::kWorkersPerCU + 7) / 8) * 8;
   if (dev >= 0 && dev < 64) cache[dev] = w;
   return w;
+}
+
+// Static share of each run, in sixteenths: the default, or the value of
+// PA_DECODE_STATIC_SIXTEENTHS (clamped to 0..16) when it is set.
+int static_sixteenths() {
+  const char* e = std::getenv("PA_DECODE_STATIC_SIXTEENTHS");
+  if (!e || !*e) return pa::kStaticSixteenths;
+  const int v = std::atoi(e);
+  return v < 0 ? 0 : v > 16 ? 16 : v;
 }
 
 // Workers to use, or a negative PA code.
@@ -95,11 +105,12 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
 int32_t pa_decode_num_workers(void) { return auto_workers(); }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t num_workers) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+                                int32_t max_context_len, int32_t num_workers) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   const int32_t w = resolve_workers(num_workers);
   if (w <= 0) return 0;
-  return pa::decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, w);
+  const int64_t s = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
+  return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, max_context_len, w);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -120,22 +131,23 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
+  // one launch takes at most kMaxSeqsPerLaunch sequences; its 64-token units
+  // (all heads) must fit a 32-bit index
+  const int64_t per_launch = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
+  if (per_launch * num_kv_heads * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
+    return PA_ERR_UNSUPPORTED;
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
-  const size_t need = pa::decode_workspace_bytes(num_seqs, num_kv_heads, head_dim, w);
+  const size_t need =
+      pa::decode_workspace_bytes(per_launch, num_kv_heads, head_dim, max_context_len, w);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
-  a.ws = pa::decode_workspace_carve(workspace, num_seqs, num_kv_heads, w);
-  a.out = static_cast<pa::half_t*>(out);
-  a.q = static_cast<const pa::half_t*>(q);
+  a.ws = pa::decode_workspace_carve(workspace, per_launch, num_kv_heads, max_context_len, w);
   a.k_cache = static_cast<const pa::half_t*>(k_cache);
   a.v_cache = static_cast<const pa::half_t*>(v_cache);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
-  a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
@@ -143,8 +155,20 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_workers = w;
+  a.static_sixteenths = static_sixteenths();
   (void)hipGetLastError();
-  return pa::launch_decode(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  // launches on one stream run in order, so they share the workspace
+  for (int64_t s0 = 0; s0 < num_seqs; s0 += per_launch) {
+    const int64_t n = num_seqs - s0 < per_launch ? num_seqs - s0 : per_launch;
+    const int64_t row = s0 * num_q_heads * head_dim;
+    a.out = static_cast<pa::half_t*>(out) + row;
+    a.q = static_cast<const pa::half_t*>(q) + row;
+    a.block_tables = block_tables + s0 * max_blocks_per_seq;
+    a.context_lens = context_lens + s0;
+    a.num_seqs = (int)n;
+    if (pa::launch_decode(a, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -11,19 +11,27 @@
 //
 // Design (the pages give none; decode reads every K/V byte once, so HBM
 // bandwidth bounds it):
-//  * Work balance.  Each (sequence, KV head) pair is a run of 64-token units
-//    (4 blocks each).  All runs are laid end to end in (sequence, head) order
-//    and a fixed grid of persistent workers (one wave each, 8 per compute
-//    unit) takes equal contiguous shares, so ragged lengths cost nothing in
-//    tail.  Each worker finds its share from a prefix sum of the lengths that
-//    it computes itself (no host knowledge of the lengths is needed).
-//  * A run cut between workers is finished by the last of them to arrive: each
-//    writes (max, sum, unnormalised output) to the workspace, bumps a counter,
-//    and the one that sees the count complete merges with the log-sum-exp
-//    rescale and resets the counter.  One launch per decode.
-//  * Consecutive workers are placed on one XCD (workgroups are handed to the 8
-//    XCDs in turn), so neighbouring runs, e.g. sequences sharing prefix blocks,
-//    meet in the same L2.
+//  * Units and segments.  Each (sequence, KV head) pair is a run of 64-token
+//    units (4 blocks each); all runs are laid end to end in (sequence, head)
+//    order.  A fixed grid of persistent workers (one wave each) shares them:
+//    the first part of the units is cut into one static segment per worker,
+//    the rest into small dynamic segments that workers claim from counters
+//    (one pool per XCD group) when they near the end of their current segment.  Workers that stream
+//    faster (HBM channels, XCD placement) thus take more of the tail, and all
+//    finish within about one segment of each other.  Each worker finds units
+//    through a prefix sum of the lengths it keeps in LDS; the host never
+//    reads the lengths.
+//  * A run cut between segments is merged by the last of its pieces to
+//    arrive: each piece writes (max, sum, unnormalised output) through to
+//    memory, bumps the run's counter two loop iterations later (by then the
+//    stores have completed: vector memory operations of a wave complete in
+//    issue order and the wave has waited on younger loads), and the piece
+//    that completes the count merges with the log-sum-exp rescale and resets
+//    the counter.  Merges therefore happen inside the stream, not after it.
+//    One launch per decode.
+//  * Consecutive static segments run on one XCD (workgroups are handed to
+//    the 8 XCDs in turn), so neighbouring runs, e.g. sequences sharing prefix
+//    blocks, meet in the same L2.
 //  * The grouped query heads of one KV head (G <= 4) are the 4 rows of the
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
@@ -33,7 +41,7 @@
 //    four contiguous 256-byte runs) and feeds them as the B operand, so the
 //    dot products reduce inside the MFMA, with no cross-lane sums.
 //  * Online softmax: running max per head (wave max per unit, DPP within rows
-//    of 16), per-lane partial sums (one wave sum per run).
+//    of 16), per-lane partial sums (one wave sum per run piece).
 //  * The fp16 probabilities are transposed through 512 bytes of LDS so lane
 //    4c+g holds head g's weights of tokens 4c..4c+3; the MFMA broadcast
 //    (CBSZ=4, ABID=c) hands that quad to all 16 blocks.
@@ -41,10 +49,10 @@
 //    8 consecutive tokens of one dim in 16 bytes, so for a fixed (block, half)
 //    the 64 lanes read 1 KiB contiguous.
 //  * Software pipeline: the next unit's K loads are issued once this unit's
-//    logits are formed, its V loads once this unit's P.V is done; every unit
-//    but a run's last issues the same 32 loads (block ids past the run's end
-//    re-read its last block) so the hardware wait counts stay exact.  K and V
-//    are read with non-temporal loads (each byte is used once).
+//    logits are formed, its V loads once this unit's P.V is done, the table
+//    entries two units ahead one iteration earlier still; every unit issues
+//    the same loads (block ids past a run's end re-read its last block).  K
+//    and V are read with non-temporal loads (each byte is used once).
 //  * Positions at or past the length are removed by selection (logit -inf,
 //    V element 0), never by multiplication, so NaN or huge values in the
 //    unused tail of the last block cannot leak.
@@ -56,24 +64,14 @@ namespace pa {
 
 namespace {
 
+constexpr int kClaimLead = 2;  // claim the next segment this many units before the current one ends
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
@@ -90,14 +88,26 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
-// Max over the 64 lanes, in every lane: DPP within each row of 16 (swap
-// pairs, swap pairs of pairs, mirror halves, mirror the row), then the four
-// row results read out as scalars.
-__device__ __forceinline__ float wave_max(float x) {
+// Max within each row of 16 lanes, in every lane of the row (DPP: swap pairs,
+// swap pairs of pairs, mirror halves, mirror the row).
+__device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
   x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
   x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
   x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
+// Max over the 64 lanes, in every lane: the four row results read out as scalars.
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
@@ -106,11 +116,8 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // Sum over the 64 lanes, in every lane (same pattern as wave_max).
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
@@ -127,13 +134,27 @@ __device__ __forceinline__ half8_t load_nt(const half_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(p));
 }
 
-// The work share of worker w among nw over `total` units: [begin(w), begin(w+1)).
-__device__ __forceinline__ int64_t share_begin(int64_t w, int64_t nw, int64_t total) {
-  return w * total / nw;
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
 }
-// The worker whose share holds unit u.
-__device__ __forceinline__ int64_t share_owner(int64_t u, int64_t nw, int64_t total) {
-  return ((u + 1) * nw - 1) / total;
+
+// Loads and stores of the partial results, coherent across XCDs: stores write
+// through to memory, loads bypass the caches (system scope, sc0 sc1).
+__device__ __forceinline__ void store_through(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float load_through(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// 16 bytes at byte offset `off` of the buffer starting at `base` (uniform).
+__device__ __forceinline__ float4_t load_through16(const float* base, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 17);  // sc0 sc1
 }
 
 }  // namespace
@@ -142,10 +163,15 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
+  constexpr int kF = D / 16;           // floats per lane of one partial in a merge
   constexpr int64_t kTile = (int64_t)kBlockSize * D;
-  constexpr int kLenRegs = 4;          // lengths of the first 256 sequences stay in registers
   static_assert(kChunks * kChunk == D && kSets * 64 == D, "head_dim must be 64 or 128");
-  static_assert(kLenRegs == 4, "four length registers");
+
+  // [S] head units (per KV head) before sequence s, [S] its length, then the
+  // dynamic classes' first chunks
+  extern __shared__ int seq_lds[];
+  __shared__ half_t p_lds[4 * 64];
+  __shared__ __attribute__((aligned(16))) half_t q_lds[4 * D];
 
   const int lane = threadIdx.x;
   const int nw = gridDim.x;
@@ -156,24 +182,31 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int G = Hq / Hkv;
+  int* const off_lds = seq_lds;
+  int* const len_lds = seq_lds + S;
+  int* const cls_lds = seq_lds + 2 * S;
 
-  auto clamp_len = [&](int c) { return min(max(c, 0), a.max_context_len); };
   auto units_for = [](int c) { return (c + kGroupTokens - 1) / kGroupTokens; };
+  const int F = a.static_sixteenths;
+  auto tail_of = [&](int n) { return n - ((n * F) >> 4); };  // dynamic units of a run of n
 
-  // ---- lengths: total units; zero the rows of empty sequences ------------
-  // clamped length of sequence 64*k + lane, k < kLenRegs (separate variables,
-  // never an indexed array: that would live in scratch memory)
-  int len0 = 0, len1 = 0, len2 = 0, len3 = 0;
-  int64_t seq_units = 0;  // sum over sequences of ceil(len / 64)
-  for (int c0 = 0, k = 0; c0 < S; c0 += 64, ++k) {
+  // ---- lengths into LDS; zero the rows of empty sequences ----------------
+  // off_lds[s]: head units (per KV head) of the sequences before s
+  int carry = 0, total_n = 0, b_max = 0;  // uniform
+  for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
-    const int c = s < S ? clamp_len(a.context_lens[s]) : 0;
-    if (k == 0) len0 = c;
-    if (k == 1) len1 = c;
-    if (k == 2) len2 = c;
-    if (k == 3) len3 = c;
+    const int c = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
     const int n = units_for(c);
-    seq_units += wave_sum_int(n);
+    const int b = tail_of(n);
+    const int hd = n - b;
+    const int incl = wave_inclusive_scan(hd, lane);
+    if (s < S) {
+      off_lds[s] = carry + incl - hd;
+      len_lds[s] = c;
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+    total_n += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
+    b_max = max(b_max, uniform(wave_max_int(b)));
     uint64_t empty = __ballot(s < S && n == 0 && (s % nw) == w);
     while (empty) {
       const int se = c0 + __builtin_ctzll(empty);
@@ -182,88 +215,245 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
       for (int e = lane; e < Hq * D; e += 64) o[e] = (half_t)0.0f;
     }
   }
-  // clamped length of sequence s (s uniform; the result is uniform): from
-  // registers when it can
-  auto len_of = [&](int s) {
-    const int k = s >> 6, l = s & 63;
-    int c;
-    if (k == 0) c = __builtin_amdgcn_readlane(len0, l);
-    else if (k == 1) c = __builtin_amdgcn_readlane(len1, l);
-    else if (k == 2) c = __builtin_amdgcn_readlane(len2, l);
-    else if (k == 3) c = __builtin_amdgcn_readlane(len3, l);
-    else c = clamp_len(a.context_lens[s]);
-    return __builtin_amdgcn_readfirstlane(c);
-  };
+  const int U = total_n * Hkv;  // all units (the host bounds this below 2^31)
+  if (U == 0) return;
+  const int P = min(nw, U);  // active workers: one static share each
+  if (w >= P) return;
+  const int U1 = carry * Hkv;  // static units (the runs' heads)
 
-  // the sums are equal in every lane; say so, so that all the work-share
-  // arithmetic below is scalar
-  seq_units = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(seq_units >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)seq_units));
-  const int64_t total = seq_units * Hkv;
-  if (total == 0) return;
-  const int64_t nwa = min((int64_t)nw, total);  // active workers: each gets >= 1 unit
-  if (w >= nwa) return;
-  const int64_t u_begin = share_begin(w, nwa, total);
-  const int64_t u_end = share_begin(w + 1, nwa, total);
-
-  // ---- the unit u_begin: its sequence by a prefix sum of the units --------
-  // units of sequence s are [Hkv*O_s, Hkv*O_{s+1}), ordered (head, unit)
-  struct Cursor {
-    int s, h, g, n_s, len;
-    int64_t o_s;  // units of the sequences before s
-  };
-  Cursor cur{};
+  // ---- dynamic chunks of the tails -------------------------------------------
+  // Class c of a tail of b units is the chunk [b - E(c+1), b - E(c)) counted
+  // from the tail's start, E(c) = 0, 1, 2, 4, 8, 8+M, 8+2M, ... (sizes 1, 1,
+  // 2, 4, M, M, ...; the first chunk of the tail may be shorter).  Claim order
+  // is class-major, largest class first, (sequence, head) within a class.
+  const int M = b_max > 8 ? max(8, (b_max - 8 + kMaxClasses - 5) / (kMaxClasses - 4)) : 8;
+  const int ncls = tail_chunks(b_max, M);  // classes present
+  auto E = [&](int c) { return c <= 2 ? c : c == 3 ? 4 : 8 + M * (c - 4); };
+  // cls_lds[c]: first dynamic chunk of class c (classes start in decreasing
+  // c, so class ncls-1 starts at 0); cls_lds[ncls]: all dynamic chunks.
+  // Built from a histogram of the sequences' last classes.
+  for (int c = lane; c <= ncls; c += 64) cls_lds[c] = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    const int s = c0 + lane;
+    if (s < S) {
+      const int nc = tail_chunks(tail_of(units_for(len_lds[s])), M);
+      if (nc > 0) atomicAdd(&cls_lds[nc - 1], 1);
+    }
+  }
+  __syncthreads();
+  // in order k = ncls-1-c: sequences having class c = an inclusive scan of
+  // the histogram; class starts = an exclusive scan of those counts times Hkv
   {
-    const int64_t key = u_begin / Hkv;
-    int64_t base = 0;
-    for (int c0 = 0, k = 0; c0 < S; c0 += 64, ++k) {
-      const int s = c0 + lane;
-      const int c = k == 0 ? len0 : k == 1 ? len1 : k == 2 ? len2 : k == 3 ? len3
-                  : (s < S ? clamp_len(a.context_lens[s]) : 0);
-      const int n = s < S ? units_for(c) : 0;
-      const int incl = wave_inclusive_scan(n, lane);
-      const uint64_t hit = __ballot(s < S && base + incl > key);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        cur.s = __builtin_amdgcn_readfirstlane(c0 + l);
-        cur.n_s = __builtin_amdgcn_readfirstlane(__shfl(n, l));
-        cur.len = __builtin_amdgcn_readfirstlane(__shfl(c, l));
-        const int64_t o = base + __builtin_amdgcn_readfirstlane(__shfl(incl, l)) - cur.n_s;
-        cur.o_s = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(o >> 32)) << 32) |
-                            (uint32_t)__builtin_amdgcn_readfirstlane((int)o));
-        break;
+    int have_carry = 0, start_carry = 0;
+    for (int k0 = 0; k0 < ncls; k0 += 64) {
+      const int k = k0 + lane, c = ncls - 1 - k;
+      const int hist = k < ncls ? cls_lds[c] : 0;
+      const int have = have_carry + wave_inclusive_scan(hist, lane);
+      const int size = k < ncls ? have * Hkv : 0;
+      const int incl = wave_inclusive_scan(size, lane);
+      if (k < ncls) cls_lds[c] = start_carry + incl - size;
+      have_carry = __builtin_amdgcn_readlane(have, 63);
+      start_carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) cls_lds[ncls] = start_carry;
+  }
+  __syncthreads();  // the LDS tables are complete
+  const int nd = uniform(cls_lds[ncls]);
+  const bool dyn = nd > 0;
+  auto cls_start = [&](int c) { return uniform(cls_lds[c]); };
+
+  // ---- static shares -----------------------------------------------------------
+  // share j < Q: head units [j*U1/Q, (j+1)*U1/Q) in (sequence, head, unit)
+  // order; Q <= P so that no share is empty (workers Q.. start by claiming)
+  const int Q = min(P, U1);
+  const bool narrow = (int64_t)U1 * Q < ((int64_t)1 << 31);  // 32-bit share arithmetic suffices
+  auto share_begin = [&](int j) -> int {
+    return narrow ? (int)((unsigned)(j * U1) / (unsigned)Q) : (int)((int64_t)j * U1 / Q);
+  };
+  auto share_of = [&](int u) -> int {  // the share holding head unit u
+    return narrow ? (int)((unsigned)((u + 1) * Q - 1) / (unsigned)U1)
+                  : (int)(((int64_t)(u + 1) * Q - 1) / U1);
+  };
+  const int R = S * Hkv;  // runs; slots [0, R) hold the first piece of each run's head
+
+  // ---- sequences by prefix sums and by class membership ------------------------
+  // the sequence holding head index `key`: the last s with off[s] <= key (a
+  // 64-ary search over the LDS prefix sums)
+  auto find_head = [&](int key) {
+    int stride = 1;
+    while (stride * 64 < S) stride *= 64;
+    int lo = 0;
+    while (true) {
+      const int idx = lo + lane * stride;
+      const bool ok = idx < S && off_lds[idx] <= key;
+      lo += (__popcll(__ballot(ok)) - 1) * stride;
+      if (stride == 1) break;
+      stride >>= 6;
+    }
+    return uniform(lo);
+  };
+  auto tail_of_seq = [&](int s) { return tail_of(units_for(len_lds[s])); };  // per lane
+  // sequences before s whose tail exceeds e units (they have class c with E(c) = e)
+  auto rank_tail = [&](int s, int e) {
+    int r = 0;
+    for (int c0 = 0; c0 < s; c0 += 64) {
+      const int t = c0 + lane;
+      r += __popcll(__ballot(t < s && tail_of_seq(min(t, S - 1)) > e));
+    }
+    return uniform(r);
+  };
+  // the i-th sequence (from 0) whose tail exceeds e units
+  auto select_tail = [&](int i, int e) {
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int t = c0 + lane;
+      const bool q = t < S && tail_of_seq(min(t, S - 1)) > e;
+      const uint64_t m = __ballot(q);
+      const int cnt = __popcll(m);
+      if (i < cnt) {
+        const uint64_t hit = __ballot(q && __popcll(m & ((1ull << lane) - 1)) == i);
+        return uniform(c0 + __builtin_ctzll(hit));
       }
-      base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+      i -= cnt;
     }
-  }
-  if (cur.n_s == 0) return;  // unreachable for consistent lengths; never divide by 0
-  {
-    const int64_t r = u_begin - (int64_t)Hkv * cur.o_s;
-    cur.h = (int)(r / cur.n_s);
-    cur.g = (int)(r - (int64_t)cur.h * cur.n_s);
-  }
-  // the unit after c in (sequence, head, unit) order; empty sequences skipped
-  auto advance = [&](Cursor c) {
-    if (c.g + 1 < c.n_s) {
+    return S - 1;  // unreachable for i < class size
+  };
+
+  // ---- cursors over units --------------------------------------------------
+  struct Cursor {
+    int s, h, g;   // sequence, KV head, unit of the run
+    int glim;      // end (exclusive) of the current stretch of this run in the segment
+    int n_s, len;  // units and length of s
+    int seg;       // segment: static share (< Q) or P + dynamic chunk
+    int left;      // units of the segment from this one on
+    bool valid;    // false past the worker's last unit (then a copy of it)
+  };
+  auto set_seq = [&](Cursor& c, int s) {
+    c.s = s;
+    c.len = uniform(len_lds[s]);
+    c.n_s = units_for(c.len);
+  };
+  // head unit u of share j
+  auto locate_share = [&](int u, int j) {
+    Cursor c;
+    set_seq(c, find_head(u / Hkv));
+    const int hd = c.n_s - tail_of(c.n_s);
+    const int r = u - Hkv * uniform(off_lds[c.s]);
+    c.h = r / hd;
+    c.g = r - c.h * hd;
+    c.glim = hd;
+    c.seg = j;
+    c.left = share_begin(j + 1) - u;
+    c.valid = true;
+    return c;
+  };
+  // the first unit of dynamic chunk d
+  auto locate_chunk = [&](int d) {
+    // its class: the smallest c whose start is <= d (starts fall with c)
+    int cl = 0;
+    for (int c0 = 0; c0 < ncls; c0 += 64) {
+      const int c = c0 + lane;
+      cl += __popcll(__ballot(c < ncls && cls_lds[c] > d));
+    }
+    cl = uniform(cl);
+    const int j = d - cls_start(cl);
+    Cursor c;
+    set_seq(c, select_tail(j / Hkv, E(cl)));
+    c.h = j - (j / Hkv) * Hkv;
+    const int b = tail_of(c.n_s), hd = c.n_s - b;
+    c.g = hd + max(0, b - E(cl + 1));
+    c.glim = hd + b - E(cl);
+    c.seg = P + d;
+    c.left = c.glim - c.g;
+    c.valid = true;
+    return c;
+  };
+  // the unit after c inside its segment: the next unit of the run, else the
+  // head of the next run (shares only: a chunk lies inside one run)
+  auto step = [&](Cursor c) {
+    --c.left;
+    if (c.g + 1 < c.glim) {
       ++c.g;
-    } else if (c.h + 1 < Hkv) {
-      ++c.h;
-      c.g = 0;
-    } else {
-      c.o_s += c.n_s;
-      c.h = 0;
-      c.g = 0;
-      do {
-        ++c.s;
-        c.len = c.s < S ? len_of(c.s) : 0;
-        c.n_s = units_for(c.len);
-      } while (c.n_s == 0 && c.s < S);
+      return c;
     }
+    c.g = 0;
+    if (c.h + 1 < Hkv) {
+      ++c.h;
+    } else {
+      c.h = 0;
+      int s = c.s;
+      do {
+        s = min(s + 1, S - 1);
+        set_seq(c, s);
+      } while (c.n_s - tail_of(c.n_s) == 0 && s + 1 < S);
+    }
+    c.glim = c.n_s - tail_of(c.n_s);
     return c;
   };
 
-  __shared__ half_t p_lds[4 * 64];
-  __shared__ __attribute__((aligned(16))) half_t q_lds[4 * D];
+  // Dynamic claims.  Same-address atomics serialise in the memory system, so
+  // the dynamic chunks form NPOOL pools with counters of their own: pool x
+  // holds the chunks d with d % NPOOL == x.  Worker w's home pool is
+  // w * NPOOL / P (for a full grid, its XCD); it claims there until a claim
+  // fails, then from the next pool until a claim fails.  Every pool is thus
+  // visited by its home workers and its left neighbour's, each failing on it
+  // exactly once, so a pool sees n_x + F_x claims in all; the one that draws
+  // value n_x + F_x - 1 is the last and resets the counter for the next call.
+  const int npool = min(kClaimPools, P);
+  auto pool_first = [&](int x) { return (x * P + npool - 1) / npool; };  // first worker of pool x
+  auto pool_homes = [&](int x) { return pool_first(x + 1) - pool_first(x); };
+  const int home = (int)(((int64_t)w * npool) / P);
+  const int stages = npool > 1 ? 2 : 1;
+  int stage = 0;             // 0: home pool, 1: next pool, stages: done
+  int claim_v = 0;           // lane 0: the value of the outstanding claim
+  bool claim_out = false;
+  auto pool_of = [&](int st) { return st == 0 ? home : (home + 1) % npool; };
+  auto issue_claim = [&]() {
+    if (lane == 0)
+      claim_v = __hip_atomic_fetch_add(a.ws.claims + pool_of(stage) * kClaimStride, 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    claim_out = true;
+  };
+  // a claim issued now and awaited at once (only where none was issued ahead)
+  auto fresh_claim = [&]() {
+    int t = 0;
+    if (lane == 0)
+      t = __hip_atomic_fetch_add(a.ws.claims + pool_of(stage) * kClaimStride, 1,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readlane(t, 0);
+  };
+  // the claimed chunk, or nd when none is left.  A claim issued ahead (at
+  // least one loop iteration earlier) lives in its own register, so the wait
+  // for its value covers only that atomic, not the loads issued since.
+  auto take_claim = [&]() -> int {
+    int v = claim_out ? __builtin_amdgcn_readlane(claim_v, 0) : fresh_claim();
+    claim_out = false;
+    while (true) {
+      const int x = pool_of(stage);
+      const int n_x = x < nd ? (nd - x + npool - 1) / npool : 0;
+      const int f_x = pool_homes(x) + (npool > 1 ? pool_homes((x + npool - 1) % npool) : 0);
+      if (v == n_x + f_x - 1 && lane == 0)
+        __hip_atomic_store(a.ws.claims + x * kClaimStride, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (v >= 0 && v < n_x) return v * npool + x;
+      if (++stage >= stages) return nd;
+      v = fresh_claim();  // the next pool (once per worker)
+    }
+  };
+  auto next = [&](Cursor c) -> Cursor {
+    if (!c.valid) return c;
+    if (c.left > 1) return step(c);
+    const int d = dyn ? take_claim() : nd;
+    if (d >= nd) {
+      c.valid = false;
+      return c;
+    }
+    return locate_chunk(d);
+  };
+  auto maybe_claim = [&](const Cursor& c) {
+    if (dyn && stage < stages && !claim_out && c.valid && c.left <= kClaimLead) issue_claim();
+  };
+
   const int my_blk = lane >> 4;  // which of a unit's 4 blocks holds this lane's token
   const int g_lane = lane & 3;   // q head of the group this lane's MFMA row carries
   const int64_t block_stride = (int64_t)Hkv * kTile;
@@ -323,7 +513,98 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // per-run softmax state
+  // ---- merge of a cut run ----------------------------------------------------
+  // The run r = (s, kvh) has np parts: first its head's pieces in shares
+  // wa..wb (piece 0 starts the head: slot r; piece p > 0 starts share wa+p:
+  // slot R + wa + p), then its tail's chunks of classes 0 .. nc-1 (chunk d in
+  // slot R + P + d).
+  struct Parts {
+    int s, kvh, n_sh, wa, nc, b;
+  };
+  auto run_parts = [&](int s, int kvh) {
+    Parts r;
+    r.s = s;
+    r.kvh = kvh;
+    const int n = units_for(uniform(len_lds[s]));
+    r.b = tail_of(n);
+    const int hd = n - r.b;
+    r.nc = tail_chunks(r.b, M);
+    r.n_sh = 0;
+    r.wa = 0;
+    if (hd > 0) {
+      const int ua = Hkv * uniform(off_lds[s]) + kvh * hd;  // the head's first unit
+      r.wa = share_of(ua);
+      r.n_sh = share_of(ua + hd - 1) - r.wa + 1;
+    }
+    return r;
+  };
+  auto slot_of = [&](const Parts& r, int p) -> int64_t {
+    if (p < r.n_sh) return p == 0 ? (int64_t)r.s * Hkv + r.kvh : (int64_t)R + r.wa + p;
+    const int c = p - r.n_sh;
+    return (int64_t)R + P + cls_start(c) + Hkv * rank_tail(r.s, E(c)) + r.kvh;
+  };
+  // Lane 16*gq + pq handles head gq: it loads (max, sum) of part p0 + pq and,
+  // for every part of the batch, output dims pq*kF .. +kF of head gq.  The
+  // parts of a batch load together (one round trip); batches combine with the
+  // running-max rescale.  Writes the output rows and resets the counter.
+  auto merge = [&](auto batch, int s, int kvh) {
+    constexpr int B = decltype(batch)::value;
+    const Parts r = run_parts(s, kvh);
+    const int np = r.n_sh + r.nc;
+    const int gq = lane >> 4, pq = lane & 15;
+    float acc[kF];
+#pragma unroll
+    for (int j = 0; j < kF; ++j) acc[j] = 0.0f;
+    float mx = -INFINITY, lsum = 0.0f;
+    for (int p0 = 0; p0 < np; p0 += B) {
+      const int nb = min(B, np - p0);
+      const bool valid = pq < nb && gq < G;
+      // slot of part p0 + pq in lane pq of every row (parts past the batch
+      // repeat its last); the slot arithmetic runs on uniform values
+      int sl = 0;
+      for (int qi = 0; qi < nb; ++qi) {
+        const int sq = (int)slot_of(r, p0 + qi);
+        if (pq == qi || (qi == nb - 1 && pq > qi)) sl = sq;
+      }
+      const float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
+      const float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
+      float ov[B][kF];
+#pragma unroll
+      for (int qi = 0; qi < B; ++qi) {
+        const float* base = a.ws.o + (int64_t)__builtin_amdgcn_readlane(sl, qi) * 4 * D;
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) {
+          const float4_t x = load_through16(base, ((gq & 3) * D + pq * kF + st * 4) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[qi][st * 4 + e] = x[e];
+        }
+      }
+      const float m_new = fmaxf(mx, row_max16(m_p));
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(mx - m_new);
+      const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
+      lsum = lsum * alpha + wt * l_p;
+      mx = m_new;
+#pragma unroll
+      for (int j = 0; j < kF; ++j) acc[j] *= alpha;
+#pragma unroll
+      for (int qi = 0; qi < B; ++qi) {
+        const float wq = __shfl(wt, (lane & 48) | qi);  // 0 for qi >= nb
+#pragma unroll
+        for (int j = 0; j < kF; ++j) acc[j] += wq * ov[qi][j];
+      }
+    }
+    const float inv = 1.0f / row_sum16(lsum);
+    if (gq < G) {
+      half_t* o = a.out + ((int64_t)s * Hq + kvh * G + gq) * D + pq * kF;
+#pragma unroll
+      for (int j = 0; j < kF; ++j) o[j] = (half_t)(acc[j] * inv);
+    }
+    if (lane == 0)  // ready for the next call
+      __hip_atomic_store(a.ws.counters + (int64_t)s * Hkv + kvh, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // per-piece softmax state
   float m_run[4], l_lane[4];
   float4_t acc_o[kSets];
   auto reset_run = [&]() {
@@ -336,20 +617,40 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  // cut runs of this share (its first and its last), merged after the stream
-  int cut_n = 0;
-  int cut_s[2] = {0, 0}, cut_h[2] = {0, 0}, cut_ns[2] = {0, 0};
-  int64_t cut_os[2] = {0, 0};
+  // Cut pieces whose arrival is still to be counted: e1 ended in the previous
+  // iteration, e2 two iterations ago (counted in this one), e3 was counted in
+  // the previous iteration (its counter value arr3 decides the merge now).
+  struct Pend {
+    int s, h;
+    bool valid;
+  };
+  Pend e1{0, 0, false}, e2{0, 0, false}, e3{0, 0, false};
+  int arr2 = 0, arr3 = 0;  // lane 0: counter values before this worker's arrival
+  auto count_arrival = [&](const Pend& e) {
+    return __hip_atomic_fetch_add(a.ws.counters + (int64_t)e.s * Hkv + e.h, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto arrived_last = [&](const Pend& e, int arr) {
+    const Parts r = run_parts(e.s, e.h);
+    return __builtin_amdgcn_readlane(arr, 0) == r.n_sh + r.nc - 1;
+  };
 
   // ---- prologue: first unit's loads, next unit's table entries ------------
   // Lookahead: cur is computed, nxt has its K/V loads in flight and its ids in
-  // pb_nxt, nxt2 has its table entries loading into tbl_nxt2.  Past the end of
-  // the share the cursors stay on the last unit (harmless re-reads).
-  const int64_t n_units = u_end - u_begin;
-  Cursor nxt = cur;
-  if (n_units > 1) nxt = advance(cur);
-  Cursor nxt2 = nxt;
-  if (n_units > 2) nxt2 = advance(nxt);
+  // pb_nxt, nxt2 has its table entries loading into tbl_nxt2.
+  // the first unit: the start of this worker's share, else its first claim
+  Cursor cur{};
+  cur.valid = false;
+  if (w < Q) {
+    cur = locate_share(share_begin(w), w);
+  } else if (dyn) {
+    const int d = take_claim();
+    if (d < nd) cur = locate_chunk(d);
+  }
+  if (!cur.valid) return;  // no work for this worker (its claims have all failed)
+  Cursor nxt = next(cur);
+  Cursor nxt2 = next(nxt);
+  maybe_claim(nxt2);
   int pb_cur[4], pb_nxt[4];
   const int tbl_cur = load_table(cur);
   int tbl_nxt = load_table(nxt);
@@ -365,13 +666,16 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   store_q();
   __syncthreads();
   reset_run();
-  int piece_first_g = cur.g;  // first unit of the current run in this share
-  bool first_piece = true;
+  int piece_g0 = cur.g;  // unit of the run where the piece began
+  bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
-  for (int64_t ui = 0; ui < n_units; ++ui) {
-    const bool last_unit = ui + 1 == n_units;
-    // the next unit's loads go to nxt (the current unit again past the share)
+  while (cur.valid) {
     const int t0 = cur.g * kGroupTokens;
+    // q rows of a piece that starts here.  Their load was issued one
+    // iteration ago, before this unit's K: waiting for it here costs nothing,
+    // as the logits wait for that K anyway.
+    if (q_pending) store_q();
+    q_pending = false;
 
     // logits: S[g][token lane] = q_g . K_token  (rows = heads, columns = tokens)
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -381,11 +685,20 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
     }
+    // The K loads just waited for were issued after e2's partial stores, so
+    // those stores have completed: count e2's arrival.
+    __builtin_amdgcn_sched_barrier(0);
+    if (e2.valid && lane == 0) arr2 = count_arrival(e2);
+    __builtin_amdgcn_sched_barrier(0);
     // table entries two units ahead, then the next unit's K and q
     const int tbl_nxt2 = load_table(nxt2);
     blocks_of(tbl_nxt, pb_nxt);
     load_k(nxt, pb_nxt);
     load_q(nxt);
+    // the unit after nxt2, computed while this unit's V is in flight (finding
+    // a newly claimed chunk takes a few LDS round trips)
+    const Cursor nxt3 = next(nxt2);
+    maybe_claim(nxt3);
 
     // online softmax over these 64 positions
     const bool live = (t0 + lane) < cur.len;
@@ -439,14 +752,18 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     load_v(nxt, pb_nxt);
     __syncthreads();
 
-    // ---- end of a run piece: finish it ---------------------------------
-    const bool run_ends = last_unit || cur.g + 1 == cur.n_s;
-    if (run_ends) {
+    // ---- the merge owed by the piece counted in the previous iteration --
+    if (e3.valid && arrived_last(e3, arr3))
+      merge(std::integral_constant<int, 4>{}, e3.s, e3.h);
+
+    // ---- end of a piece: a run ends or the segment ends ------------------
+    Pend e0{0, 0, false};
+    if (cur.g + 1 == cur.glim || cur.left == 1) {
       float l_tot[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) l_tot[g] = (g < G) ? wave_sum_dpp(l_lane[g]) : 1.0f;
-      if (piece_first_g == 0 && cur.g + 1 == cur.n_s) {
-        // the whole run is this worker's
+      for (int g = 0; g < 4; ++g) l_tot[g] = (g < G) ? wave_sum(l_lane[g]) : 1.0f;
+      if (piece_g0 == 0 && cur.g + 1 == cur.n_s) {
+        // the whole run is in this piece
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (g < G) {
@@ -457,10 +774,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
           }
         }
       } else {
-        // partial: slot 2w for this worker's first run, 2w+1 for its last,
-        // written through to memory (system-scope relaxed stores) so a worker
-        // on another XCD can read it; merged after the stream
-        const int64_t slot = 2 * (int64_t)w + (first_piece ? 0 : 1);
+        // a cut piece: the start of a run's head in slot r, a piece that
+        // starts share j mid-head in slot R + j, dynamic chunk d in slot
+        // R + P + d; written through to memory and counted two iterations later
+        const int64_t slot = (cur.seg < P && piece_g0 == 0) ? (int64_t)cur.s * Hkv + cur.h
+                                                             : (int64_t)R + cur.seg;
         float* po = a.ws.o + slot * 4 * D;
         float* pml = a.ws.ml + slot * 8;
 #pragma unroll
@@ -468,152 +786,85 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
           if (g < G) {
 #pragma unroll
             for (int st = 0; st < kSets; ++st)
-              __hip_atomic_store(po + g * D + st * 64 + lane, acc_o[st][g], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_SYSTEM);
+              store_through(po + g * D + st * 64 + lane, acc_o[st][g]);
             if (lane == 0) {
-              __hip_atomic_store(pml + 2 * g, m_run[g], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_SYSTEM);
-              __hip_atomic_store(pml + 2 * g + 1, l_tot[g], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_SYSTEM);
+              store_through(pml + 2 * g, m_run[g]);
+              store_through(pml + 2 * g + 1, l_tot[g]);
             }
           }
         }
-        const int ci = cut_n < 2 ? cut_n : 1;
-        cut_s[ci] = cur.s;
-        cut_h[ci] = cur.h;
-        cut_ns[ci] = cur.n_s;
-        cut_os[ci] = cur.o_s;
-        cut_n = ci + 1;
+        e0 = Pend{cur.s, cur.h, true};
       }
       reset_run();
-      first_piece = false;
-      piece_first_g = 0;
-      store_q();  // q rows of the next run (the current run's q reads are done)
+      q_pending = true;
+      piece_g0 = nxt.g;
     }
 
     // ---- shift the lookahead -------------------------------------------
+    e3 = e2;
+    arr3 = arr2;
+    e2 = e1;
+    e1 = e0;
     cur = nxt;
     nxt = nxt2;
     tbl_nxt = tbl_nxt2;
-    if (ui + 3 < n_units) nxt2 = advance(nxt2);
+    nxt2 = nxt3;
     __syncthreads();
   }
 
-  // ---- counters and merges of the cut runs ---------------------------------
-  if (cut_n == 0) return;
+  // ---- the pieces still to be counted, and their merges -------------------
   __builtin_amdgcn_s_waitcnt(0);  // every partial store above has completed
-  for (int ci = 0; ci < cut_n; ++ci) {
-    const int s = cut_s[ci], kvh = cut_h[ci], n_s = cut_ns[ci];
-    const int64_t ua = (int64_t)Hkv * cut_os[ci] + (int64_t)kvh * n_s;  // the run's first unit
-    const int64_t wa = share_owner(ua, nwa, total);
-    const int64_t wb = share_owner(ua + n_s - 1, nwa, total);
-    int* counter = a.ws.counters + (int64_t)s * Hkv + kvh;
-    int arrived = 0;
-    if (lane == 0)
-      arrived = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    arrived = __shfl(arrived, 0);
-    if (arrived != (int)(wb - wa)) continue;
-    // last to arrive: merge the run's np partials.  Part p (0-based) is worker
-    // wa + p's slot: its last-run slot for p = 0 unless the run starts its
-    // share, its first-run slot otherwise.  Reads bypass the caches.
-    auto ld = [](const float* p) {
-      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    };
-    const int np = (int)(wb - wa + 1);
-    const bool wa_first = ua == share_begin(wa, nwa, total);
-    auto slot_of = [&](int p) { return 2 * (wa + p) + ((p == 0 && !wa_first) ? 1 : 0); };
-    // Parts in batches of 16: lane 4p+g loads part p's (max, sum) of head g
-    // and, with them, every lane loads the batch's output vectors (all these
-    // loads are independent: one round trip per batch).  Batches combine
-    // with the running-max rescale.
-    const int gq = lane & 3;
-    float mx = -INFINITY, lsum = 0.0f;  // per head gq
-    float acc[4][kSets];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int st = 0; st < kSets; ++st) acc[g][st] = 0.0f;
-    for (int p0 = 0; p0 < np; p0 += 16) {
-      const int p = p0 + (lane >> 2);
-      const bool valid = p < np && gq < G;
-      const int64_t sp = slot_of(valid ? p : p0);
-      const float m_p = valid ? ld(a.ws.ml + sp * 8 + 2 * gq) : -INFINITY;
-      const float l_p = valid ? ld(a.ws.ml + sp * 8 + 2 * gq + 1) : 0.0f;
-      const int nq = min(16, np - p0);
-      float ov[16][4][kSets];
-#pragma unroll
-      for (int qi = 0; qi < 16; ++qi) {
-        const int64_t sq = slot_of(p0 + min(qi, nq - 1));
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int st = 0; st < kSets; ++st)
-            ov[qi][g][st] = (qi < nq && g < G)
-                                ? ld(a.ws.o + sq * 4 * D + g * D + st * 64 + lane) : 0.0f;
-      }
-      // batch max per head, rescale what was accumulated, add the batch
-      float bm = m_p;
-#pragma unroll
-      for (int o = 4; o < 64; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
-      const float m_new = fmaxf(mx, bm);
-      const float alpha = fast_exp2(mx - m_new);   // 0 for the first batch
-      const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
-      lsum = lsum * alpha + wt * l_p;
-      mx = m_new;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g < G) {
-          const float al = __shfl(alpha, g);
-#pragma unroll
-          for (int st = 0; st < kSets; ++st) acc[g][st] *= al;
-#pragma unroll
-          for (int qi = 0; qi < 16; ++qi) {
-            const float wq = __shfl(wt, 4 * qi + g);
-#pragma unroll
-            for (int st = 0; st < kSets; ++st) acc[g][st] += wq * ov[qi][g][st];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 4; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o);  // per head
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < G) {
-        const float inv = 1.0f / __shfl(lsum, g);
-        half_t* o = a.out + ((int64_t)s * Hq + kvh * G + g) * D;
-#pragma unroll
-        for (int st = 0; st < kSets; ++st) o[st * 64 + lane] = (half_t)(acc[g][st] * inv);
-      }
-    }
-    if (lane == 0)  // ready for the next call
-      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int arr1 = 0;
+  if (lane == 0) {
+    if (e2.valid) arr2 = count_arrival(e2);
+    if (e1.valid) arr1 = count_arrival(e1);
   }
+  if (e3.valid && arrived_last(e3, arr3))
+    merge(std::integral_constant<int, 16>{}, e3.s, e3.h);
+  if (e2.valid && arrived_last(e2, arr2))
+    merge(std::integral_constant<int, 16>{}, e2.s, e2.h);
+  if (e1.valid && arrived_last(e1, arr1))
+    merge(std::integral_constant<int, 16>{}, e1.s, e1.h);
 }
 
-size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
-  const size_t cnt = ((size_t)(S * Hkv) * sizeof(int) + 255) & ~(size_t)255;
-  const size_t ml = ((size_t)(2 * workers * 8) * sizeof(float) + 255) & ~(size_t)255;
-  return cnt + ml + (size_t)(2 * workers * 4 * D) * sizeof(float);
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+int64_t decode_max_slots(int64_t S, int64_t Hkv, int64_t max_len, int64_t workers) {
+  // a run's tail has at most all its units; M >= 8 and the class cap bound its chunks
+  const int64_t n = (max_len + kGroupTokens - 1) / kGroupTokens;
+  const int64_t chunks = n > 8 + 8 * (int64_t)(kMaxClasses - 4) ? kMaxClasses : tail_chunks((int)n, 8);
+  return S * Hkv + workers + S * Hkv * chunks;
 }
 
-DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t workers) {
-  const size_t cnt = ((size_t)(S * Hkv) * sizeof(int) + 255) & ~(size_t)255;
-  const size_t ml = ((size_t)(2 * workers * 8) * sizeof(float) + 255) & ~(size_t)255;
+size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t max_len, int64_t workers) {
+  const int64_t slots = decode_max_slots(S, Hkv, max_len, workers);
+  return align256((size_t)(S * Hkv) * sizeof(int)) + kClaimBytes +
+         align256((size_t)(slots * 8) * sizeof(float)) + (size_t)(slots * 4 * D) * sizeof(float);
+}
+
+DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t max_len,
+                                       int64_t workers) {
+  const int64_t slots = decode_max_slots(S, Hkv, max_len, workers);
+  const size_t cnt = align256((size_t)(S * Hkv) * sizeof(int));
+  const size_t ml = align256((size_t)(slots * 8) * sizeof(float));
   char* p = reinterpret_cast<char*>(base);
   DecodeWorkspace w;
   w.counters = reinterpret_cast<int*>(p);
-  w.ml = reinterpret_cast<float*>(p + cnt);
-  w.o = reinterpret_cast<float*>(p + cnt + ml);
+  w.claims = reinterpret_cast<int*>(p + cnt);
+  w.ml = reinterpret_cast<float*>(p + cnt + kClaimBytes);
+  w.o = reinterpret_cast<float*>(p + cnt + kClaimBytes + ml);
   return w;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_workers);
+  const size_t lds = ((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64), lds, stream, a);
   else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64), lds, stream, a);
   return hipGetLastError();
 }
 

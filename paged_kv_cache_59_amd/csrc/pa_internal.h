@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pa {
@@ -11,23 +12,56 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBlockSize = 16;   // token slots per block
-constexpr int kChunk = 8;        // fp16 elements per 16-byte chunk
-constexpr int kGroupTokens = 64; // tokens one wave handles per step of its loop
+constexpr int kBlockSize = 16;    // token slots per block
+constexpr int kChunk = 8;         // fp16 elements per 16-byte chunk
+constexpr int kGroupTokens = 64;  // tokens one wave handles per step of its loop (a "unit")
 constexpr int kWorkersPerCU = 2;  // decode waves per compute unit
-constexpr int kMaxWorkers = 1 << 20;
+constexpr int kMaxWorkers = 1 << 16;
+// Sequences one decode launch takes (their unit offsets and lengths sit in
+// LDS, 8 bytes each); the host splits larger batches into several launches.
+constexpr int kMaxSeqsPerLaunch = 4096;
 
-// Decode workspace: one arrival counter per (sequence, KV head) run, then two
-// partial slots per worker, each holding for 4 query-head rows a (max, sum)
-// pair and a D-vector of unnormalised fp32 output.
+// Work split of one decode launch (see decode_kernel).  Every (sequence, KV
+// head) run of n 64-token units keeps its first floor(n * F / 16) units (its
+// head) in the static part, cut into one equal share per worker; the rest of
+// the run (its tail) is cut, from its end, into dynamic chunks of 1, 1, 2, 4
+// and then M units ("classes" 0, 1, 2, 3, 4, ...), that workers claim largest
+// class first.  M >= 8 keeps the classes below kMaxClasses.  F defaults to
+// kStaticSixteenths (all static: measured fastest while the claims' atomics
+// share the streaming wave's in-order memory queue); the environment variable
+// PA_DECODE_STATIC_SIXTEENTHS (0..16) overrides it per call.
+constexpr int kStaticSixteenths = 16;
+constexpr int kMaxClasses = 256;
+
+// Claim counters of the dynamic chunks: kClaimPools of them, kClaimStride
+// ints (4 KiB) apart so that they sit in different memory channels.
+constexpr int kClaimPools = 8;
+constexpr int kClaimStride = 1024;
+constexpr size_t kClaimBytes = (size_t)kClaimPools * kClaimStride * sizeof(int);
+
+// Dynamic chunks of one run with a tail of b units when the top chunks are M
+// units long.
+__host__ __device__ inline int tail_chunks(int b, int M) {
+  return b <= 2 ? b : b <= 4 ? 3 : b <= 8 ? 4 : 4 + (b - 8 + M - 1) / M;
+}
+
+// Decode workspace: one arrival counter per (sequence, KV head) run, the
+// claim counters of the dynamic chunks, then the partial slots: one per run
+// (the first piece of its head), one per worker (a piece that starts its
+// share) and one per dynamic chunk, each holding for 4 query-head rows a
+// (max, sum) pair and a D-vector of unnormalised fp32 output.
 struct DecodeWorkspace {
   int* counters;  // [S][Hkv], zero between calls
-  float* ml;      // [2*workers][4][2]
-  float* o;       // [2*workers][4][D]
+  int* claims;    // [kClaimPools * kClaimStride], zero between calls
+  float* ml;      // [slots][4][2]
+  float* o;       // [slots][4][D]
 };
 
-size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
-DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t workers);
+// Partial slots a launch over S sequences of at most max_len tokens can use.
+int64_t decode_max_slots(int64_t S, int64_t Hkv, int64_t max_len, int64_t workers);
+size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t max_len, int64_t workers);
+DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t max_len,
+                                       int64_t workers);
 
 hipError_t launch_reshape_and_cache(const half_t* k, const half_t* v, half_t* k_cache,
                                     half_t* v_cache, const int64_t* slot_mapping,
@@ -50,10 +84,12 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int64_t num_blocks;
   int max_context_len;
-  int num_workers;  // grid size: persistent waves sharing the work
+  int num_workers;        // grid size: persistent waves sharing the work
+  int static_sixteenths;  // static share of each run, in sixteenths (0..16)
   DecodeWorkspace ws;
 };
 
+// One launch over a.num_seqs <= kMaxSeqsPerLaunch sequences.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -47,6 +47,36 @@ def test_decode_shapes_and_work_splits(Hq, Hkv, D, workers):
     run_case(w, workers, f"edge Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
 
 
+@pytest.mark.parametrize("sixteenths", [0, 8, 12])
+@pytest.mark.parametrize("Hq,Hkv,D,workers", [(32, 8, 128, 0), (8, 8, 128, 37), (4, 4, 64, 512),
+                                              (8, 2, 64, 3)])
+def test_dynamic_tail_chunks(monkeypatch, sixteenths, Hq, Hkv, D, workers):
+    """Runs split into a static head and dynamic tail chunks claimed at run
+    time (PA_DECODE_STATIC_SIXTEENTHS < 16): every run is then cut, and its
+    pieces merged, whatever the number of workers."""
+    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", str(sixteenths))
+    w = wl.make_workload("tails", 300 + sixteenths + Hq + D, Hq, Hkv, D,
+                         context_lens=EDGE_LENS + [2048, 3000, 4100])
+    run_case(w, workers, f"tails F{sixteenths} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
+
+
+def test_dynamic_tail_chunks_workspace_reuse(monkeypatch):
+    """Claim counters and arrival counters are left at zero by every call."""
+    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", "10")
+    w = wl.make_workload("tails-reuse", 330, 32, 8, 128, len_range=(1, 3000), num_seqs=20)
+    ws = pk.new_workspace(20, 8, 128, w.max_context_len, 64)
+    d = to_device(w)
+    pk.pa_reshape_and_cache(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+    kc, vc = oracle_pools(w)
+    ref = oracle_decode(w, kc, vc)
+    for rep in range(3):
+        out = gpu_decode(w, d, 64, workspace=ws)
+        compare(out, ref, f"tails reuse rep{rep}")
+        counters = ws[: 20 * 8 * 4].view(torch.int32).cpu().numpy()
+        claims = ws[768:768 + 8 * 4096].view(torch.int32)[::1024].cpu().numpy()
+        assert (counters == 0).all() and (claims == 0).all()
+
+
 def test_ragged_random_lengths_many_seqs():
     w = wl.make_workload("ragged", 201, 32, 8, 128, len_range=(1, 700), num_seqs=40)
     run_case(w, 96, "ragged 40 seqs 96 workers")
@@ -223,7 +253,7 @@ def test_workspace_reuse_leaves_counters_zero():
     w1 = wl.make_workload("reuse1", 216, 32, 8, 128, len_range=(300, 900), num_seqs=7)
     w2 = wl.make_workload("reuse2", 217, 32, 8, 128, len_range=(1, 500), num_seqs=5)
     workers = 50
-    ws = pk.new_workspace(7, 8, 128, workers)
+    ws = pk.new_workspace(7, 8, 128, max(w1.max_context_len, w2.max_context_len), workers)
     for rep in range(3):
         for w in (w1, w2):
             d = to_device(w)
@@ -236,3 +266,18 @@ def test_workspace_reuse_leaves_counters_zero():
             compare(out, oracle_decode(w, kc, vc), f"reuse {w.name} rep{rep}")
             counters = ws[: 7 * 8 * 4].view(torch.int32).cpu().numpy()
             assert (counters == 0).all()
+            # the 8 claim counters of the dynamic segments follow the arrival
+            # counters (256-byte aligned), 4 KiB apart
+            claims = ws[256:256 + 8 * 4096].view(torch.int32)[::1024].cpu().numpy()
+            assert (claims == 0).all()
+
+
+def test_batch_above_one_launch():
+    """More sequences than one launch takes: the host splits the batch into
+    launches that share the workspace."""
+    w = wl.make_workload("wide", 218, 2, 1, 64, len_range=(1, 40), num_seqs=4100)
+    d = to_device(w)
+    out = gpu_step(w, d, 0)
+    kc, vc = oracle_pools(w)
+    seqs = np.r_[0:40, 4050:4100]
+    compare(out[seqs], oracle_decode(w, kc, vc, seqs), "4100 sequences")
