@@ -103,8 +103,10 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                    int32_t block_size, int64_t num_blocks, hipStream_t stream);
 
 /*
- * Number of decode workers (wavefronts of 64 lanes) pa_decode uses when it is
- * passed num_workers == 0: 2 per compute unit of the current HIP device.
+ * Number of decode workers pa_decode uses when it is passed num_workers == 0:
+ * 2 per compute unit of the current HIP device.  A worker is one workgroup of
+ * three 64-lane wavefronts: one streams K and V, one writes and merges the
+ * partial results of cut sequences, one claims dynamic work.
  * Returns a negative PA_ERR_* code if the device cannot be queried.
  */
 int32_t pa_decode_num_workers(void);
@@ -143,13 +145,15 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *                     max_blocks_per_seq*16
  *   num_workers       0 = automatic (pa_decode_num_workers()); else the number
  *                     of persistent wavefronts that share the work.  Every
- *                     (sequence, KV head) is cut into 64-token units; the
- *                     first three quarters of each such run go into equal
- *                     contiguous shares, one per worker, and the rest into
- *                     small chunks (1, 1, 2, 4, 8.. units from the run's end)
- *                     that workers claim as they finish, largest first.  A
- *                     sequence cut into several pieces is merged by the last
- *                     piece to finish (log-sum-exp rescaling).
+ *                     (sequence, KV head) is cut into 64-token units that
+ *                     go into equal contiguous shares, one per worker.  With
+ *                     the environment variable PA_DECODE_STATIC_SIXTEENTHS
+ *                     = F (0..15), only the first F/16 of each run is
+ *                     shared out; the rest is cut into small chunks (1, 1,
+ *                     2, 4, 8.. units from the run's end) that workers claim
+ *                     as they finish, largest first.  A sequence cut into
+ *                     several pieces is merged by the last piece to finish
+ *                     (log-sum-exp rescaling).
  *   workspace         device buffer of at least pa_decode_workspace_size(
  *                     num_seqs, num_kv_heads, head_dim, max_context_len,
  *                     num_workers) bytes, 256-byte aligned, ZERO-FILLED before

@@ -64,7 +64,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kClaimLead = 2;  // claim the next segment this many units before the current one ends
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -136,6 +135,13 @@ __device__ __forceinline__ half8_t load_nt(const half_t* p) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// A compiler-only ordering point for LDS exchanged between the waves of a
+// workgroup.  The DS instructions of one wave execute in program order, so
+// keeping the compiler from reordering (or caching) the accesses is enough;
+// volatile or fenced accesses would instead make the compiler wait for every
+// outstanding memory operation, draining the streamer's K/V pipeline.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ int wave_max_int(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
@@ -160,7 +166,7 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
   constexpr int kF = D / 16;           // floats per lane of one partial in a merge
@@ -172,8 +178,22 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   extern __shared__ int seq_lds[];
   __shared__ half_t p_lds[4 * 64];
   __shared__ __attribute__((aligned(16))) half_t q_lds[4 * D];
+  // streamer -> merger: cut pieces, a ring of kRing entries
+  __shared__ float ring_o[kRing][4 * D];
+  __shared__ float ring_ml[kRing][8];
+  __shared__ int ring_meta[kRing][4];  // sequence, KV head, partial slot
+  // claimer -> streamer: claimed chunks (nd = none left) with their first unit
+  // already located: chunk, sequence, KV head, unit, end unit
+  __shared__ int claim_q[kClaimDepth][8];
+  __shared__ int ctl[8];  // ring produced/consumed, claims produced/consumed, streamer done
 
-  const int lane = threadIdx.x;
+  // Wave 0 streams the units.  Every operation whose latency would stall a
+  // wave's in-order memory queue is taken by a helper wave: wave 1 writes cut
+  // pieces through, counts their arrivals and merges; wave 2 claims dynamic
+  // chunks when the streamer asks and locates them.
+  const int role = threadIdx.x >> 6;
+  const bool streamer = role == 0;
+  const int lane = threadIdx.x & 63;
   const int nw = gridDim.x;
   // consecutive logical workers on one XCD (workgroup i runs on XCD i % 8)
   const int w = (nw % 8 == 0) ? (int)(blockIdx.x % 8) * (nw / 8) + (int)(blockIdx.x / 8)
@@ -200,14 +220,14 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     const int b = tail_of(n);
     const int hd = n - b;
     const int incl = wave_inclusive_scan(hd, lane);
-    if (s < S) {
+    if (streamer && s < S) {
       off_lds[s] = carry + incl - hd;
       len_lds[s] = c;
     }
     carry += __builtin_amdgcn_readlane(incl, 63);
     total_n += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
     b_max = max(b_max, uniform(wave_max_int(b)));
-    uint64_t empty = __ballot(s < S && n == 0 && (s % nw) == w);
+    uint64_t empty = streamer ? __ballot(s < S && n == 0 && (s % nw) == w) : 0;
     while (empty) {
       const int se = c0 + __builtin_ctzll(empty);
       empty &= empty - 1;
@@ -232,11 +252,14 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   // cls_lds[c]: first dynamic chunk of class c (classes start in decreasing
   // c, so class ncls-1 starts at 0); cls_lds[ncls]: all dynamic chunks.
   // Built from a histogram of the sequences' last classes.
-  for (int c = lane; c <= ncls; c += 64) cls_lds[c] = 0;
+  if (streamer) {
+    for (int c = lane; c <= ncls; c += 64) cls_lds[c] = 0;
+    if (lane < 8) ctl[lane] = 0;
+  }
   __syncthreads();
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
-    if (s < S) {
+    if (streamer && s < S) {
       const int nc = tail_chunks(tail_of(units_for(len_lds[s])), M);
       if (nc > 0) atomicAdd(&cls_lds[nc - 1], 1);
     }
@@ -244,7 +267,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   // in order k = ncls-1-c: sequences having class c = an inclusive scan of
   // the histogram; class starts = an exclusive scan of those counts times Hkv
-  {
+  if (streamer) {
     int have_carry = 0, start_carry = 0;
     for (int k0 = 0; k0 < ncls; k0 += 64) {
       const int k = k0 + lane, c = ncls - 1 - k;
@@ -326,6 +349,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     int n_s, len;  // units and length of s
     int seg;       // segment: static share (< Q) or P + dynamic chunk
     int left;      // units of the segment from this one on
+    int seglen;    // units of the segment
     bool valid;    // false past the worker's last unit (then a copy of it)
   };
   auto set_seq = [&](Cursor& c, int s) {
@@ -344,6 +368,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     c.glim = hd;
     c.seg = j;
     c.left = share_begin(j + 1) - u;
+    c.seglen = c.left;
     c.valid = true;
     return c;
   };
@@ -365,6 +390,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     c.glim = hd + b - E(cl);
     c.seg = P + d;
     c.left = c.glim - c.g;
+    c.seglen = c.left;
     c.valid = true;
     return c;
   };
@@ -404,54 +430,63 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   auto pool_homes = [&](int x) { return pool_first(x + 1) - pool_first(x); };
   const int home = (int)(((int64_t)w * npool) / P);
   const int stages = npool > 1 ? 2 : 1;
-  int stage = 0;             // 0: home pool, 1: next pool, stages: done
-  int claim_v = 0;           // lane 0: the value of the outstanding claim
-  bool claim_out = false;
   auto pool_of = [&](int st) { return st == 0 ? home : (home + 1) % npool; };
-  auto issue_claim = [&]() {
-    if (lane == 0)
-      claim_v = __hip_atomic_fetch_add(a.ws.claims + pool_of(stage) * kClaimStride, 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    claim_out = true;
+  auto lds_ld = [](const int* p) {
+    lds_order();
+    const int v = *p;
+    lds_order();
+    return uniform(v);
   };
-  // a claim issued now and awaited at once (only where none was issued ahead)
-  auto fresh_claim = [&]() {
-    int t = 0;
-    if (lane == 0)
-      t = __hip_atomic_fetch_add(a.ws.claims + pool_of(stage) * kClaimStride, 1,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_amdgcn_readlane(t, 0);
+  auto lds_st = [&](int* p, int v) {
+    lds_order();
+    if (lane == 0) *p = v;
+    lds_order();
   };
-  // the claimed chunk, or nd when none is left.  A claim issued ahead (at
-  // least one loop iteration earlier) lives in its own register, so the wait
-  // for its value covers only that atomic, not the loads issued since.
-  auto take_claim = [&]() -> int {
-    int v = claim_out ? __builtin_amdgcn_readlane(claim_v, 0) : fresh_claim();
-    claim_out = false;
-    while (true) {
-      const int x = pool_of(stage);
-      const int n_x = x < nd ? (nd - x + npool - 1) / npool : 0;
-      const int f_x = pool_homes(x) + (npool > 1 ? pool_homes((x + npool - 1) % npool) : 0);
-      if (v == n_x + f_x - 1 && lane == 0)
-        __hip_atomic_store(a.ws.claims + x * kClaimStride, 0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      if (v >= 0 && v < n_x) return v * npool + x;
-      if (++stage >= stages) return nd;
-      v = fresh_claim();  // the next pool (once per worker)
+  // (streamer) claims are made by the claimer wave on request, as late as the
+  // lookahead allows, so that they follow the streamer's actual progress
+  int cq_cons = 0, requested = 0;
+  auto request_claims = [&](int outstanding) {
+    if (requested - cq_cons < outstanding) {
+      requested = cq_cons + outstanding;
+      lds_st(&ctl[kCtlClaimsWanted], requested);
     }
+  };
+  // (streamer) the next claimed chunk from the claimer's queue, already
+  // located; an invalid cursor when none is left
+  auto take_claim = [&]() -> Cursor {
+    request_claims(1);
+    Cursor c{};
+    c.valid = false;
+    for (int spin = 0; lds_ld(&ctl[kCtlClaimsMade]) == cq_cons; ++spin) {
+      if (spin == kSpinLimit) return c;  // never reached: the claimer answers every request
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const int* e = claim_q[cq_cons % kClaimDepth];
+    lds_order();
+    const int d = uniform(e[0]);
+    c.s = uniform(e[1]);
+    c.h = uniform(e[2]);
+    c.g = uniform(e[3]);
+    c.glim = uniform(e[4]);
+    c.len = uniform(e[5]);
+    lds_order();
+    lds_st(&ctl[kCtlClaimsTaken], ++cq_cons);
+    c.n_s = units_for(c.len);
+    c.seg = P + d;
+    c.left = c.glim - c.g;
+    c.seglen = c.left;
+    c.valid = d < nd;
+    return c;
   };
   auto next = [&](Cursor c) -> Cursor {
     if (!c.valid) return c;
     if (c.left > 1) return step(c);
-    const int d = dyn ? take_claim() : nd;
-    if (d >= nd) {
-      c.valid = false;
-      return c;
+    if (dyn) {
+      const Cursor n = take_claim();
+      if (n.valid) return n;
     }
-    return locate_chunk(d);
-  };
-  auto maybe_claim = [&](const Cursor& c) {
-    if (dyn && stage < stages && !claim_out && c.valid && c.left <= kClaimLead) issue_claim();
+    c.valid = false;
+    return c;
   };
 
   const int my_blk = lane >> 4;  // which of a unit's 4 blocks holds this lane's token
@@ -617,23 +652,138 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  // Cut pieces whose arrival is still to be counted: e1 ended in the previous
-  // iteration, e2 two iterations ago (counted in this one), e3 was counted in
-  // the previous iteration (its counter value arr3 decides the merge now).
-  struct Pend {
-    int s, h;
-    bool valid;
-  };
-  Pend e1{0, 0, false}, e2{0, 0, false}, e3{0, 0, false};
-  int arr2 = 0, arr3 = 0;  // lane 0: counter values before this worker's arrival
-  auto count_arrival = [&](const Pend& e) {
-    return __hip_atomic_fetch_add(a.ws.counters + (int64_t)e.s * Hkv + e.h, 1, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto arrived_last = [&](const Pend& e, int arr) {
-    const Parts r = run_parts(e.s, e.h);
-    return __builtin_amdgcn_readlane(arr, 0) == r.n_sh + r.nc - 1;
-  };
+  // ---- the claimer wave -------------------------------------------------------
+  if (role == 2) {
+    // Claims.  Same-address atomics serialise in the memory system, so the
+    // dynamic chunks form NPOOL pools with counters of their own (pool x:
+    // chunks d with d % NPOOL == x).  This worker's home pool is w*NPOOL/P
+    // (for a full grid, its XCD); it claims there until a claim fails, then
+    // from the next pool until a claim fails.  Every pool is thus visited by
+    // its home workers and its left neighbour's, each failing on it exactly
+    // once, so pool x sees n_x + F_x claims in all; the one that draws value
+    // n_x + F_x - 1 is the last and resets the counter for the next call.
+    int stage = 0, made = 0;
+    bool claiming = dyn;
+    for (int idle = 0; claiming && idle < kSpinLimit;) {
+      if (made >= lds_ld(&ctl[kCtlClaimsWanted])) {
+        if (lds_ld(&ctl[kCtlDone])) break;
+        __builtin_amdgcn_s_sleep(1);
+        ++idle;
+        continue;
+      }
+      idle = 0;
+      int d = nd;
+      while (stage < stages) {
+        const int x = pool_of(stage);
+        int t = 0;
+        if (lane == 0)
+          t = __hip_atomic_fetch_add(a.ws.claims + x * kClaimStride, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        const int v = __builtin_amdgcn_readlane(t, 0);
+        const int n_x = x < nd ? (nd - x + npool - 1) / npool : 0;
+        const int f_x = pool_homes(x) + (npool > 1 ? pool_homes((x + npool - 1) % npool) : 0);
+        if (v == n_x + f_x - 1 && lane == 0)
+          __hip_atomic_store(a.ws.claims + x * kClaimStride, 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (v >= 0 && v < n_x) {
+          d = v * npool + x;
+          break;
+        }
+        ++stage;
+      }
+      claiming = d < nd;
+      int* e = claim_q[made % kClaimDepth];
+      if (d < nd) {
+        const Cursor c = locate_chunk(d);
+        lds_order();
+        if (lane == 0) {
+          e[1] = c.s;
+          e[2] = c.h;
+          e[3] = c.g;
+          e[4] = c.glim;
+          e[5] = c.len;
+        }
+      }
+      lds_st(&e[0], d);
+      lds_st(&ctl[kCtlClaimsMade], ++made);
+    }
+    return;
+  }
+
+  // ---- the merger wave --------------------------------------------------------
+  if (!streamer) {
+    // The merger works in rounds: take every finished piece from the ring (up
+    // to kRing); write them through to their slots; wait once; count all
+    // their arrivals at once (one lane each); wait once; merge the runs whose
+    // last piece it holds.  Two memory round trips per round, however many
+    // pieces.
+    int cons = 0;
+    for (int idle = 0; idle < kSpinLimit;) {
+      const int avail = min(lds_ld(&ctl[kCtlRingMade]) - cons, kRing);
+      if (avail == 0) {
+        // the streamer writes its last entry before its done flag: once the
+        // flag is seen, one more look at the ring is final
+        if (lds_ld(&ctl[kCtlDone]) && cons == lds_ld(&ctl[kCtlRingMade])) break;
+        __builtin_amdgcn_s_sleep(2);
+        ++idle;
+        continue;
+      }
+      idle = 0;
+      // the pieces: into registers, release their entries, write them through
+      int ps[kRing], ph[kRing];
+      int64_t pslot[kRing];
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        if (i < avail) {
+          const int k = (cons + i) % kRing;
+          ps[i] = lds_ld(&ring_meta[k][0]);
+          ph[i] = lds_ld(&ring_meta[k][1]);
+          pslot[i] = lds_ld(&ring_meta[k][2]);
+          float pv[4][kSets];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int st = 0; st < kSets; ++st) pv[g][st] = ring_o[k][g * D + st * 64 + lane];
+          const float pml = lane < 8 ? ring_ml[k][lane] : 0.0f;
+          float* po = a.ws.o + pslot[i] * 4 * D;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            if (g < G)
+#pragma unroll
+              for (int st = 0; st < kSets; ++st)
+                store_through(po + g * D + st * 64 + lane, pv[g][st]);
+          if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml);
+        }
+      }
+      cons += avail;
+      lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
+      __builtin_amdgcn_s_waitcnt(0);      // the slots are written through before they are counted
+      // arrivals: lane i counts piece i
+      int arr = 0;
+      if (lane < avail) {
+        int si = ps[0], hi = ph[0];
+#pragma unroll
+        for (int i = 1; i < kRing; ++i)
+          if (lane == i) si = ps[i], hi = ph[i];
+        arr = __hip_atomic_fetch_add(a.ws.counters + (int64_t)si * Hkv + hi, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        if (i < avail) {
+          const Parts r = run_parts(ps[i], ph[i]);
+          if (__builtin_amdgcn_readlane(arr, i) == r.n_sh + r.nc - 1)
+            merge(std::integral_constant<int, 16>{}, ps[i], ph[i]);
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- the streamer wave -----------------------------------------------------
+  int ring_made = 0;
+  // the streamer is done: merger and claimer finish what is queued and stop
+  auto finish = [&]() { lds_st(&ctl[kCtlDone], 1); };
 
   // ---- prologue: first unit's loads, next unit's table entries ------------
   // Lookahead: cur is computed, nxt has its K/V loads in flight and its ids in
@@ -644,13 +794,14 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   if (w < Q) {
     cur = locate_share(share_begin(w), w);
   } else if (dyn) {
-    const int d = take_claim();
-    if (d < nd) cur = locate_chunk(d);
+    cur = take_claim();
   }
-  if (!cur.valid) return;  // no work for this worker (its claims have all failed)
+  if (!cur.valid) {  // no work for this worker (its claims have all failed)
+    finish();
+    return;
+  }
   Cursor nxt = next(cur);
   Cursor nxt2 = next(nxt);
-  maybe_claim(nxt2);
   int pb_cur[4], pb_nxt[4];
   const int tbl_cur = load_table(cur);
   int tbl_nxt = load_table(nxt);
@@ -664,7 +815,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   load_v(cur, pb_cur);
   __builtin_amdgcn_sched_barrier(0);
   store_q();
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
   reset_run();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
@@ -685,10 +836,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
     }
-    // The K loads just waited for were issued after e2's partial stores, so
-    // those stores have completed: count e2's arrival.
-    __builtin_amdgcn_sched_barrier(0);
-    if (e2.valid && lane == 0) arr2 = count_arrival(e2);
+    // keep the next unit's address work below the logits: hoisted above
+    // them it would wait for this unit's whole K (and table) first
     __builtin_amdgcn_sched_barrier(0);
     // table entries two units ahead, then the next unit's K and q
     const int tbl_nxt2 = load_table(nxt2);
@@ -698,7 +847,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     // the unit after nxt2, computed while this unit's V is in flight (finding
     // a newly claimed chunk takes a few LDS round trips)
     const Cursor nxt3 = next(nxt2);
-    maybe_claim(nxt3);
+    // ask for the chunk after nxt3's segment two units ahead (two ahead for
+    // dynamic chunks of one or two units, which pass in an iteration or two)
+    if (dyn && nxt3.valid && nxt3.left <= 2)
+      request_claims((nxt3.seg >= P && nxt3.seglen <= 2) ? 2 : 1);
 
     // online softmax over these 64 positions
     const bool live = (t0 + lane) < cur.len;
@@ -734,7 +886,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
           }
     }
 
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     // lane 4c+g: weights of head g for tokens 4c..4c+3
     const half4_t pfrag =
         *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * 64 + (lane >> 2) * 4);
@@ -750,14 +902,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
       }
     });
     load_v(nxt, pb_nxt);
-    __syncthreads();
-
-    // ---- the merge owed by the piece counted in the previous iteration --
-    if (e3.valid && arrived_last(e3, arr3))
-      merge(std::integral_constant<int, 4>{}, e3.s, e3.h);
+    __builtin_amdgcn_wave_barrier();
 
     // ---- end of a piece: a run ends or the segment ends ------------------
-    Pend e0{0, 0, false};
     if (cur.g + 1 == cur.glim || cur.left == 1) {
       float l_tot[4];
 #pragma unroll
@@ -774,26 +921,32 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
           }
         }
       } else {
-        // a cut piece: the start of a run's head in slot r, a piece that
-        // starts share j mid-head in slot R + j, dynamic chunk d in slot
-        // R + P + d; written through to memory and counted two iterations later
-        const int64_t slot = (cur.seg < P && piece_g0 == 0) ? (int64_t)cur.s * Hkv + cur.h
-                                                             : (int64_t)R + cur.seg;
-        float* po = a.ws.o + slot * 4 * D;
-        float* pml = a.ws.ml + slot * 8;
+        // a cut piece: the start of a run's head goes to slot r, a piece that
+        // starts share j mid-head to slot R + j, dynamic chunk d to slot
+        // R + P + d.  It is handed to the merger through the LDS ring (wait
+        // while the ring is full, which the merger rarely lets happen).
+        const int slot = (cur.seg < P && piece_g0 == 0) ? cur.s * Hkv + cur.h : R + cur.seg;
+        for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
+             ++spin)
+          __builtin_amdgcn_s_sleep(1);
+        const int k = ring_made % kRing;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (g < G) {
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int st = 0; st < kSets; ++st)
-              store_through(po + g * D + st * 64 + lane, acc_o[st][g]);
-            if (lane == 0) {
-              store_through(pml + 2 * g, m_run[g]);
-              store_through(pml + 2 * g + 1, l_tot[g]);
-            }
-          }
+          for (int st = 0; st < kSets; ++st)
+            ring_o[k][g * D + st * 64 + lane] = acc_o[st][g];
+        if (lane < 8) {  // (max, sum) of head lane/2
+          const int gi = lane >> 1;
+          const float mv = gi == 0 ? m_run[0] : gi == 1 ? m_run[1] : gi == 2 ? m_run[2] : m_run[3];
+          const float lv = gi == 0 ? l_tot[0] : gi == 1 ? l_tot[1] : gi == 2 ? l_tot[2] : l_tot[3];
+          ring_ml[k][lane] = (lane & 1) ? lv : mv;
         }
-        e0 = Pend{cur.s, cur.h, true};
+        if (lane == 0) {
+          ring_meta[k][0] = cur.s;
+          ring_meta[k][1] = cur.h;
+          ring_meta[k][2] = slot;
+        }
+        lds_st(&ctl[kCtlRingMade], ++ring_made);
       }
       reset_run();
       q_pending = true;
@@ -801,30 +954,14 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
     }
 
     // ---- shift the lookahead -------------------------------------------
-    e3 = e2;
-    arr3 = arr2;
-    e2 = e1;
-    e1 = e0;
     cur = nxt;
     nxt = nxt2;
     tbl_nxt = tbl_nxt2;
     nxt2 = nxt3;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- the pieces still to be counted, and their merges -------------------
-  __builtin_amdgcn_s_waitcnt(0);  // every partial store above has completed
-  int arr1 = 0;
-  if (lane == 0) {
-    if (e2.valid) arr2 = count_arrival(e2);
-    if (e1.valid) arr1 = count_arrival(e1);
-  }
-  if (e3.valid && arrived_last(e3, arr3))
-    merge(std::integral_constant<int, 16>{}, e3.s, e3.h);
-  if (e2.valid && arrived_last(e2, arr2))
-    merge(std::integral_constant<int, 16>{}, e2.s, e2.h);
-  if (e1.valid && arrived_last(e1, arr1))
-    merge(std::integral_constant<int, 16>{}, e1.s, e1.h);
+  finish();
 }
 
 namespace {
@@ -862,9 +999,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.num_workers);
   const size_t lds = ((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64), lds, stream, a);
+    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, a);
   else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64), lds, stream, a);
+    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, a);
   return hipGetLastError();
 }
 

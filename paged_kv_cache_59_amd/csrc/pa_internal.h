@@ -39,6 +39,18 @@ constexpr int kClaimPools = 8;
 constexpr int kClaimStride = 1024;
 constexpr size_t kClaimBytes = (size_t)kClaimPools * kClaimStride * sizeof(int);
 
+// LDS exchange between a decode workgroup's three waves: cut pieces the
+// streamer hands to the merger (a ring of kRing), chunks the claimer has
+// claimed for the streamer (at most kClaimDepth queued, claimed on the
+// streamer's request), and the control words.
+constexpr int kRing = 4;
+constexpr int kClaimDepth = 2;
+enum { kCtlRingMade = 0, kCtlRingTaken, kCtlClaimsMade, kCtlClaimsTaken, kCtlClaimsWanted, kCtlDone };
+// Bound on every wait between the waves (about 0.5 s of s_sleep): a wait
+// that long means a broken invariant, and the kernel then ends with wrong
+// results rather than never.
+constexpr int kSpinLimit = 1 << 23;
+
 // Dynamic chunks of one run with a tail of b units when the top chunks are M
 // units long.
 __host__ __device__ inline int tail_chunks(int b, int M) {
