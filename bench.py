@@ -11,8 +11,11 @@ serve a step from the previous one's reads.
 Prints one JSON line:
   value        bytes the step must move / step time, GB/s
   roofline     the decode kernel (one launch: balanced persistent workers with
-               the merge of cut sequences fused) timed with HIP events on its
-               stream: algorithmic decode bytes / mean launch duration vs 8 TB/s;
+               the merge of cut sequences fused) timed with HIP events bound to
+               the kernel on its stream: algorithmic decode bytes / mean kernel
+               duration vs 8 TB/s, over a second pass of the same steps
+               (`call_mean_us`: events recorded around the call in the timed
+               region, which add queueing and dispatch latency);
                `traffic` is the HBM bytes per launch from the committed
                rocprofv3 counter summary (profiles/), null if the kernel changed
   cpu_baseline the CPU oracle on this host on one whole step of the same batch
@@ -132,7 +135,7 @@ def main():
     stream = torch.cuda.current_stream()
     has_copy = w.block_mapping.shape[0] > 0
 
-    def step(i, ev=None):
+    def step(i, ev=None, kernel_ev=None):
         kc, vc = replicas[i % R]
         if has_copy:
             pk.pa_copy_blocks(kc, vc, pairs)
@@ -140,7 +143,8 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         pk.pa_decode(out, q, kc, vc, tab, lens, float(w.scale), w.num_kv_heads,
-                     max_context_len=w.max_context_len, num_workers=workers, workspace=ws)
+                     max_context_len=w.max_context_len, num_workers=workers, workspace=ws,
+                     kernel_events=kernel_ev)
         if ev is not None:
             ev[1].record(stream)
 
@@ -148,7 +152,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronised on both sides
+    # timed region: exactly `steps` steps, synchronised on both sides, with
+    # events recorded around each decode call (they include queueing and
+    # dispatch latency)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -157,7 +163,23 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # kernel durations: the same `steps` steps again, right after, with events
+    # bound to the decode kernel itself (pa_decode_timed: its own start and
+    # end, the duration rocprofv3's kernel trace reports).  Binding costs the
+    # launch a few microseconds of host-side dispatch, so it stays out of the
+    # wall-clock region above.  torch creates an event at its first record.
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in kev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.steps + i, kernel_ev=kev[i])
+    torch.cuda.synchronize()
+    dec_ms = np.array([a.elapsed_time(b) for a, b in kev])
 
     ms_per_step = wall * 1e3 / args.steps
     step_bytes = w.decode_bytes() + w.append_bytes() + w.copy_bytes()
@@ -192,8 +214,14 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
             "kernel": "decode_kernel",
             "mean_us": round(dec_mean_s * 1e6, 3),
+            "median_us": round(float(np.median(dec_ms)) * 1e3, 3),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
             "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
+            "timing": "HIP events bound to the decode kernel (hipExtLaunchKernel), over "
+                      "the timed steps run again right after the wall-clock region",
+            "call_mean_us": round(float(call_ms.mean()) * 1e3, 3),
+            "call_frac": round(w.decode_bytes() / (float(call_ms.mean()) * 1e-3) / 1e9
+                               / HBM_PEAK_GBS, 4),
         },
         "cpu_baseline": None,
     }

@@ -172,6 +172,23 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * pa_decode with timing: identical work and results; in addition the caller's
+ * events (created with timing enabled, either may be NULL) are bound to the
+ * kernel itself through hipExtLaunchKernel, so hipEventElapsedTime(start,
+ * stop) is the decode kernel's execution time (first launch's start to last
+ * launch's end for batches above 4096 sequences), without the queueing and
+ * dispatch latency that events recorded around the call also include.  For
+ * profiling callers; num_seqs == 0 leaves both events untouched.
+ */
+int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
 /* Text for a PA_* code (static storage, never NULL). */
 const char* pa_strerror(int code);
 

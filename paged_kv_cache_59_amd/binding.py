@@ -24,7 +24,8 @@ PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
-EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_workspace_size",
+EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_timed",
+            "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
 
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32,
                             i32, i64, i32, i32, vp, sz, vp]
     L.pa_decode.restype = ctypes.c_int
+    L.pa_decode_timed.argtypes = L.pa_decode.argtypes + [vp, vp]
+    L.pa_decode_timed.restype = ctypes.c_int
     L.pa_strerror.argtypes = [ctypes.c_int]
     L.pa_strerror.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -152,13 +155,18 @@ def new_workspace(num_seqs, num_kv_heads, head_dim, max_context_len, num_workers
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
-              max_context_len=None, num_workers=0, workspace=None, stream=None):
+              max_context_len=None, num_workers=0, workspace=None, stream=None,
+              kernel_events=None):
     """Paged decode attention; writes out [S, Hq, D] fp16 and returns it.
 
     ``max_context_len`` is the host-known bound of ``context_lens``; when None
     the table width bound ``max_blocks_per_seq * 16`` is used.  ``workspace``
     is a zero-filled uint8 GPU tensor of pa_decode_workspace_size(...) bytes
     (reusable across calls that do not overlap); when None a fresh one is made.
+    ``kernel_events`` = (start, stop) timing-enabled torch.cuda.Events, each
+    recorded at least once before (torch creates the HIP event at its first
+    record), calls pa_decode_timed: start.elapsed_time(stop) is then the
+    kernel's own execution time.
     """
     _dev(out, "out", torch.float16)
     _dev(q, "q", torch.float16)
@@ -182,10 +190,15 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
     _dev(workspace, "workspace", torch.uint8)
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
-    code = lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                           block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv,
-                           S, hq, d, BLOCK_SIZE, mb, nb, int(max_context_len),
-                           int(num_workers), workspace.data_ptr(), workspace.numel(),
-                           _stream(q, stream))
-    _check(code, "pa_decode")
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv, S, hq, d,
+            BLOCK_SIZE, mb, nb, int(max_context_len), int(num_workers), workspace.data_ptr(),
+            workspace.numel(), _stream(q, stream))
+    if kernel_events is None:
+        _check(lib().pa_decode(*args), "pa_decode")
+    else:
+        start, stop = kernel_events
+        if not start.cuda_event or not stop.cuda_event:
+            raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
+        _check(lib().pa_decode_timed(*args, start.cuda_event, stop.cuda_event), "pa_decode_timed")
     return out

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 301;  // 0.3.1
 constexpr int kMaxGroup = 4;   // query heads per KV head the decode kernel holds
 constexpr int kMaxGridYZ = 65535;
 
@@ -113,12 +113,13 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, max_context_len, w);
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, float scale,
-              int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-              int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-              int32_t max_context_len, int32_t num_workers, void* workspace,
-              size_t workspace_bytes, hipStream_t stream) {
+int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || !std::isfinite(scale))
     return PA_ERR_INVALID_ARG;
@@ -166,9 +167,23 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.block_tables = block_tables + s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
     a.num_seqs = (int)n;
-    if (pa::launch_decode(a, stream) != hipSuccess) return PA_ERR_HIP;
+    hipEvent_t start = s0 == 0 ? kernel_start : nullptr;
+    hipEvent_t stop = s0 + n >= num_seqs ? kernel_stop : nullptr;
+    if (pa::launch_decode(a, stream, start, stop) != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+              int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+              int32_t max_context_len, int32_t num_workers, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+  return pa_decode_timed(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         num_kv_heads, num_seqs, num_q_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, max_context_len, num_workers, workspace,
+                         workspace_bytes, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -58,6 +58,8 @@
 //    unused tail of the last block cannot leak.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -176,8 +178,12 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   // [S] head units (per KV head) before sequence s, [S] its length, then the
   // dynamic classes' first chunks
   extern __shared__ int seq_lds[];
-  __shared__ half_t p_lds[4 * 64];
-  __shared__ __attribute__((aligned(16))) half_t q_lds[4 * D];
+  // Rows padded so that the 4 rows of one access fall in different LDS banks
+  // (unpadded, rows 128 and 256 bytes apart share banks: 4-way conflicts).
+  constexpr int kQRow = D + 8;  // halves per q row
+  constexpr int kPRow = 64 + 16;  // halves per softmax-weight row
+  __shared__ __attribute__((aligned(16))) half_t p_lds[4 * kPRow];
+  __shared__ __attribute__((aligned(16))) half_t q_lds[4 * kQRow];
   // streamer -> merger: cut pieces, a ring of kRing entries
   __shared__ float ring_o[kRing][4 * D];
   __shared__ float ring_ml[kRing][8];
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   auto store_q = [&]() {
     if (q_row < 4) {
       const half8_t v = q_row < G ? qreg : half8_t{};
-      *reinterpret_cast<half8_t*>(q_lds + q_row * D + q_chunk * kChunk) = v;
+      *reinterpret_cast<half8_t*>(q_lds + q_row * kQRow + q_chunk * kChunk) = v;
     }
   };
 
@@ -832,7 +838,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g_lane * D + c * kChunk);
+      const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g_lane * kQRow + c * kChunk);
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
     }
@@ -867,7 +873,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
         for (int st = 0; st < kSets; ++st) acc_o[st][g] *= alpha;
         m_run[g] = m_new;
       }
-      p_lds[g * 64 + lane] = ph;
+      p_lds[g * kPRow + lane] = ph;
     }
 
     // positions past the end (tail of the last block, and re-read blocks past
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     // lane 4c+g: weights of head g for tokens 4c..4c+3
     const half4_t pfrag =
-        *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * 64 + (lane >> 2) * 4);
+        *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * kPRow + (lane >> 2) * 4);
 
     // out[g][d] += sum_t P[g][t] V[t][d]; chunk c = tokens 4c..4c+3 of the unit
     static_for<0, 16>([&](auto ic) {
@@ -995,13 +1001,22 @@ DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64
   return w;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
-  const size_t lds = ((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, a);
+  const uint32_t lds = (uint32_t)(((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int));
+  if (!start && !stop) {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, a);
+    else
+      hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, a);
+  } else {
+    // the events take the kernel's own start and end times
+    if (a.head_dim == 128)
+      hipExtLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, start, stop, 0, a);
+  }
   return hipGetLastError();
 }
 

@@ -101,7 +101,9 @@ struct DecodeArgs {
   DecodeWorkspace ws;
 };
 
-// One launch over a.num_seqs <= kMaxSeqsPerLaunch sequences.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// One launch over a.num_seqs <= kMaxSeqsPerLaunch sequences.  Non-null
+// events are bound to the kernel itself (its start and end times).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop);
 
 }  // namespace pa

@@ -281,3 +281,35 @@ def test_batch_above_one_launch():
     kc, vc = oracle_pools(w)
     seqs = np.r_[0:40, 4050:4100]
     compare(out[seqs], oracle_decode(w, kc, vc, seqs), "4100 sequences")
+
+
+@pytest.mark.parametrize("num_seqs", [9, 4100])
+def test_timed_decode_matches_and_times_the_kernel(num_seqs):
+    """pa_decode_timed does the same work as pa_decode (bit-identical output)
+    and binds the events to the kernel: its duration is positive and no
+    longer than that of events recorded around the call.  4100 sequences take
+    two launches: the events then span both."""
+    w = wl.make_workload("timed", 219, 8, 2, 64, len_range=(1, 700 if num_seqs < 100 else 40),
+                         num_seqs=num_seqs)
+    d = to_device(w)
+    pk.pa_reshape_and_cache(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+    plain = gpu_decode(w, d).copy()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[2].record(stream)
+    ev[3].record(stream)
+    d["out"].zero_()
+    ev[0].record(stream)
+    pk.pa_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                 d["context_lens"], float(w.scale), w.num_kv_heads,
+                 max_context_len=w.max_context_len, kernel_events=(ev[2], ev[3]))
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    timed = d["out"].cpu().numpy()
+    assert np.array_equal(plain.view(np.uint16), timed.view(np.uint16))
+    kernel_ms, call_ms = ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[1])
+    log(f"timed decode S={num_seqs}: kernel {kernel_ms * 1e3:.1f} us, call {call_ms * 1e3:.1f} us")
+    assert 0.0 < kernel_ms <= call_ms * 1.001 + 1e-3
+    kc, vc = oracle_pools(w)
+    seqs = np.r_[0:9] if num_seqs < 100 else np.r_[0:20, num_seqs - 20:num_seqs]
+    compare(timed[seqs], oracle_decode(w, kc, vc, seqs), "timed decode")
