@@ -15,3 +15,4 @@ from .paged_attention import (  # noqa: F401
     logical_v_blocks,
     kv_bytes_per_token,
 )
+from .chunked_prefill import prefill, prefill_flops  # noqa: F401
