@@ -189,6 +189,43 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                     hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
+/*
+ * Multi-query paged attention: each sequence's chunk of new query tokens
+ * attends causally to its paged context -- chunked prefill ("KV Cache in
+ * Serving Engines", section 3 "New Problem: Long Prefills Pause Decoding")
+ * and the continuation after a prefix-cache hit (same page, section 4;
+ * "PagedAttention and Continuous Batching Explained (2026)", "Prefix
+ * caching").  The chunk's K and V must already be in the cache
+ * (pa_reshape_and_cache).  With n = context_lens[s] and n_q its chunk length,
+ * chunk row i sits at position p = n - n_q + i and, for query head h with KV
+ * head kh = h / G,
+ *
+ *   out[t][h] = softmax_j( scale * q[t][h] . K_s[kh][j] ) V_s[kh][j],
+ *               j = 0 .. p,   t = query_start[s] + i.
+ *
+ * A decode step is the case n_q = 1.
+ *
+ *   out, q            fp16 [num_tokens][num_q_heads][head_dim]
+ *   query_start       int32 [num_seqs + 1], device memory, non-decreasing from 0:
+ *                     rows query_start[s] .. query_start[s+1]-1 are sequence s's chunk
+ *   num_tokens        rows of q and out (query_start[num_seqs] when consistent)
+ *   block_tables, context_lens, scale, pools: as for pa_decode (context_lens
+ *                     clamped to [0, max_context_len])
+ *   max_query_len     host-known upper bound of every chunk length, at most
+ *                     max_context_len; 0 = nothing to do
+ * Any G = num_q_heads / num_kv_heads is accepted.  A chunk longer than its
+ * context or than max_query_len, or reaching past num_tokens, is a broken
+ * precondition: its rows are left unwritten (nothing outside q and out is
+ * touched).  Accumulation is fp32; softmax weights enter the value product
+ * rounded to fp16; out is rounded to nearest even.  No workspace.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int32_t num_tokens, float scale,
+               int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+               int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+               int32_t max_context_len, int32_t max_query_len, hipStream_t stream);
+
 /* Text for a PA_* code (static storage, never NULL). */
 const char* pa_strerror(int code);
 

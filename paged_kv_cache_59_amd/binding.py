@@ -25,7 +25,7 @@ PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_timed",
-            "pa_decode_workspace_size",
+            "pa_prefill", "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
 
@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_timed.argtypes = L.pa_decode.argtypes + [vp, vp]
     L.pa_decode_timed.restype = ctypes.c_int
+    L.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32, i32, i32,
+                             i32, i32, i64, i32, i32, vp]
+    L.pa_prefill.restype = ctypes.c_int
     L.pa_strerror.argtypes = [ctypes.c_int]
     L.pa_strerror.restype = ctypes.c_char_p
     L.pa_version.argtypes = []
@@ -201,4 +204,46 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
         if not start.cuda_event or not stop.cuda_event:
             raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
         _check(lib().pa_decode_timed(*args, start.cuda_event, stop.cuda_event), "pa_decode_timed")
+    return out
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               num_kv_heads, max_context_len=None, max_query_len=None, stream=None):
+    """Multi-query paged attention (chunked prefill); writes out [T, Hq, D] fp16.
+
+    ``query_start`` is an int32 GPU tensor of num_seqs + 1 row offsets into q;
+    each sequence's chunk is the last positions of its context, already
+    appended to the cache.  ``max_context_len`` / ``max_query_len`` are
+    host-known bounds (defaults: the table width and min(T, that)).
+    """
+    _dev(out, "out", torch.float16)
+    _dev(q, "q", torch.float16)
+    _dev(k_cache, "k_cache", torch.float16)
+    _dev(v_cache, "v_cache", torch.float16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(query_start, "query_start", torch.int32)
+    nb, hkv, d = _cache_geometry(k_cache, v_cache)
+    if hkv != int(num_kv_heads):
+        raise ValueError("num_kv_heads does not match k_cache")
+    T, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_tokens, num_q_heads, head_dim]")
+    S = int(context_lens.numel())
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], "
+                         "query_start [num_seqs + 1]")
+    mb = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = mb * BLOCK_SIZE
+    if max_query_len is None:
+        max_query_len = min(int(T), int(max_context_len))
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    code = lib().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            block_tables.data_ptr(), context_lens.data_ptr(),
+                            query_start.data_ptr(), int(T), float(scale), hkv, S, hq, d,
+                            BLOCK_SIZE, mb,
+                            nb, int(max_context_len), int(max_query_len), _stream(q, stream))
+    _check(code, "pa_prefill")
     return out

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 301;  // 0.3.1
+constexpr int kVersion = 400;  // 0.4.0
 constexpr int kMaxGroup = 4;   // query heads per KV head the decode kernel holds
 constexpr int kMaxGridYZ = 65535;
 
@@ -184,6 +184,50 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                          num_kv_heads, num_seqs, num_q_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, max_context_len, num_workers, workspace,
                          workspace_bytes, stream, nullptr, nullptr);
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int32_t num_tokens, float scale,
+               int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+               int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+               int32_t max_context_len, int32_t max_query_len, hipStream_t stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || max_query_len < 0 ||
+      !std::isfinite(scale))
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (block_size != PA_BLOCK_SIZE || !head_dim_supported(head_dim)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE ||
+      max_query_len > max_context_len)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_query_len == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t tile_groups = ceil_div(ceil_div((int64_t)max_query_len * G, 32), 4);
+  if ((int64_t)num_seqs * num_kv_heads * tile_groups + 7 > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  pa::PrefillArgs a{};
+  a.out = static_cast<pa::half_t*>(out);
+  a.q = static_cast<const pa::half_t*>(q);
+  a.k_cache = static_cast<const pa::half_t*>(k_cache);
+  a.v_cache = static_cast<const pa::half_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_tokens = num_tokens;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.max_query_len = max_query_len;
+  a.tile_groups = (int)tile_groups;
+  (void)hipGetLastError();
+  return pa::launch_prefill(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -106,4 +106,26 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                          hipEvent_t stop);
 
+// Multi-query paged attention (chunked prefill).  One wave per tile of 32
+// rows of one (sequence, KV head); a workgroup holds 4 such tiles, and
+// tile_groups workgroups cover the longest chunk: ceil(max_query_len * G / 128).
+struct PrefillArgs {
+  half_t* out;
+  const half_t* q;
+  const half_t* k_cache;
+  const half_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int num_tokens;    // rows of q and out
+  float scale_log2;  // softmax scale times log2(e)
+  int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_context_len, max_query_len;
+  int tile_groups;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace pa

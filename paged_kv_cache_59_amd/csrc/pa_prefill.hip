@@ -1,0 +1,237 @@
+// Multi-query paged attention for gfx950: a chunk of new query tokens per
+// sequence attends causally to the sequence's paged context (chunked prefill,
+// and the continuation after a prefix-cache hit).
+//
+// Sources (web pages, by title and section):
+//  - "KV Cache in Serving Engines: PagedAttention, Continuous Batching, and
+//    Prefix Caching", section 3 "New Problem: Long Prefills Pause Decoding":
+//    a long prefill is cut into chunks spread over steps; section 4 "Prefix
+//    Caching": blocks found in the cache skip their prefill.
+//  - "PagedAttention and Continuous Batching Explained (2026)", "Prefix
+//    caching": on a hit only the tokens after the cached full blocks remain;
+//    "FAQ": the attention itself is the ordinary one.
+// A chunk of n_q rows is the last n_q positions of the sequence's context
+// (their K/V already appended); the row at position p sees positions 0..p.
+//
+// Work: one wave computes a tile of 32 rows of one (sequence, KV head) --
+// rows enumerate (chunk token, query head of the group) -- against the keys
+// 0 .. (its last row's position), 32 keys per step:
+//   S^T = K . Q^T  (v_mfma_f32_16x16x32_f16, A = 16 keys x 32 dims of K,
+//                   B = 32 dims x 16 rows of Q^T)
+//   O^T += V^T . P^T (A = 16 dims x 32 keys of V^T, B = 32 keys x 16 rows)
+// With lane l = 16 j + c: the A/B operand of lane l covers k-slots
+// 8j..8j+7 of row/column c, and the result of lane l is rows 4j..4j+3 of
+// column c.  Key k-row m of S^T sub-tile kt is loaded as key
+// 8 (m / 4) + 4 kt + m % 4 of the 32-key step, so lane l's 8 logits of its
+// row c are the keys 8j..8j+7 in order: exactly its P^T operand.  Those are
+// 8 consecutive tokens of one 8-token V group, so its V^T operand is one
+// 16-byte load, and the O^T result of lane l is its own row c, the row whose
+// softmax state it holds.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half8_t ld16(const half_t* p) {
+  return *reinterpret_cast<const half8_t*>(p);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+  constexpr int KS = D / 32;             // 32-dim steps of the contraction over D
+  constexpr int DT = D / 16;             // 16-dim tiles of the output
+  constexpr int64_t kTile = (int64_t)kBlockSize * D;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;  // column of the MFMA operands / results: this lane's row
+  const int j = lane >> 4;    // k-slot group
+
+  // blocks of one (sequence, KV head) run on one XCD (workgroup i -> XCD i % 8)
+  const int nb_total = gridDim.x;
+  const int b = (nb_total % 8 == 0) ? (int)(blockIdx.x % 8) * (nb_total / 8) + (int)(blockIdx.x / 8)
+                                    : (int)blockIdx.x;
+  const int sh = b / a.tile_groups;
+  if (sh >= a.num_seqs * a.num_kv_heads) return;
+  const int s = sh / a.num_kv_heads;
+  const int h = sh - s * a.num_kv_heads;
+  const int tile = (b - sh * a.tile_groups) * 4 + wave;
+
+  const int Hq = a.num_q_heads;
+  const int G = Hq / a.num_kv_heads;
+  const int t0 = a.query_start[s];
+  const int nq = a.query_start[s + 1] - t0;
+  const int len = min(max(a.context_lens[s], 0), a.max_context_len);
+  // an empty chunk, or one that breaks a precondition (longer than its
+  // context or than the bound, or rows outside q): nothing to do
+  if (nq <= 0 || nq > len || nq > a.max_query_len || t0 < 0 || t0 + nq > a.num_tokens) return;
+  const int rows = nq * G;
+  if (tile * 32 >= rows) return;
+
+  // this lane's two rows (sub-tiles rt = 0, 1)
+  int tok[2], grp[2], pos[2];
+  bool valid[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = tile * 32 + rt * 16 + c16;
+    valid[rt] = r < rows;
+    const int rr = valid[rt] ? r : rows - 1;
+    tok[rt] = rr / G;
+    grp[rt] = rr - tok[rt] * G;
+    pos[rt] = valid[rt] ? len - nq + tok[rt] : -1;
+  }
+  const int last_row = min(tile * 32 + 31, rows - 1);
+  const int pos_max = len - nq + last_row / G;
+  const int nsteps = pos_max / 32 + 1;  // 32-key steps covering keys 0 .. pos_max
+
+  // Q^T operands, held for the whole loop
+  half8_t qf[2][KS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const half_t* qp = a.q + ((int64_t)(t0 + tok[rt]) * Hq + h * G + grp[rt]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld16(qp + ks * 32 + j * 8);
+  }
+
+  const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int last_blk = (len + kBlockSize - 1) / kBlockSize - 1;
+  const int64_t hoff = (int64_t)h * kTile;
+  const int64_t bstride = (int64_t)a.num_kv_heads * kTile;
+  auto phys_of = [&](int lb) -> int64_t {
+    const int e = row[min(lb, last_blk)];
+    return (e >= 0 && e < a.num_blocks) ? e : 0;  // a broken table entry reads block 0
+  };
+  // key of this lane's K rows in S^T sub-tile kt: 8 (c16 / 4) + 4 kt + c16 % 4
+  const int kq = 8 * (c16 >> 2) + (c16 & 3);
+  half8_t kf[2][KS], vf[DT];
+  auto load_step = [&](int st, half8_t (&k)[2][KS], half8_t (&v)[DT]) {
+    const int64_t p0 = phys_of(2 * st), p1 = phys_of(2 * st + 1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = kq + 4 * kt;  // < 32
+      const half_t* kp = a.k_cache + (key < 16 ? p0 : p1) * bstride + hoff + (key & 15) * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) k[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * 16 * 8);
+    }
+    // V^T operand: keys 8j..8j+7 = block j / 2, 8-token group j % 2
+    const half_t* vp = a.v_cache + ((j < 2) ? p0 : p1) * bstride + hoff + (int64_t)(j & 1) * D * 8;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
+  };
+
+  float4v o[2][DT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_lane[2] = {0.0f, 0.0f};
+
+  load_step(0, kf, vf);
+  for (int st = 0; st < nsteps; ++st) {
+    half8_t kc[2][KS], vc[DT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kc[kt][ks] = kf[kt][ks];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vc[dt] = vf[dt];
+    if (st + 1 < nsteps) load_step(st + 1, kf, vf);  // next step's K/V in flight
+    // positions past the context (the last block's tail: any bits, NaN
+    // included, and re-read blocks past it) get V := 0 by selection; their
+    // logits are removed below, and 0 * NaN would not be 0
+    if (st * 32 + 32 > len) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool dead = st * 32 + 8 * j + e >= len;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vc[dt][e] = dead ? (half_t)0.0f : vc[dt][e];
+      }
+    }
+
+    half8_t pf[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float4v sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sacc[kt] = mfma16x16x32(kc[kt][ks], qf[rt][ks], sacc[kt]);
+      }
+      // logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row
+      float z[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kp = st * 32 + 8 * j + e;
+        z[e] = kp <= pos[rt] ? sacc[e >> 2][e & 3] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, z[e]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run[rt], mt);
+      const bool none = m_new == -INFINITY;  // no key seen yet (or an invalid row)
+      const float alpha = none ? 1.0f : exp2_fast(m_run[rt] - m_new);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const half_t ph = none ? (half_t)0.0f : (half_t)exp2_fast(z[e] - m_new);
+        pf[rt][e] = ph;
+        lsum += (float)ph;
+      }
+      l_lane[rt] = l_lane[rt] * alpha + lsum;
+      m_run[rt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vc[dt], pf[rt], o[rt][dt]);
+  }
+
+  // out[row][dims 16 dt + 4 j .. +3] = O^T / l
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = l_lane[rt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!valid[rt]) continue;
+    const float inv = 1.0f / l;
+    half_t* op = a.out + ((int64_t)(t0 + tok[rt]) * Hq + h * G + grp[rt]) * D + 4 * j;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      half4_t r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (half_t)(o[rt][dt][i] * inv);
+      *reinterpret_cast<half4_t*>(op + dt * 16) = r;
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.tile_groups;
+  const int64_t padded = (blocks + 7) / 8 * 8;
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)padded), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)padded), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -415,3 +415,143 @@ def make_named(name: str, **overrides) -> Workload:
     kw = dict(WORKLOADS[name])
     kw.update(overrides)
     return make_workload(name, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Multi-query (chunked prefill) inputs
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    """One step of chunked prefill: each sequence's context already holds its
+    first ``context_lens - chunk_lens`` positions; this step appends the
+    chunk's K/V at the next positions and its queries attend causally."""
+    name: str
+    seed: int
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: np.float32
+    q: np.ndarray               # fp16 [T, Hq, D], chunks packed in sequence order
+    k_cache: np.ndarray         # fp16 [NB, Hkv, D/8, 16, 8]
+    v_cache: np.ndarray         # fp16 [NB, Hkv, 2, D, 8]
+    block_tables: np.ndarray    # int32 [S, MB]
+    context_lens: np.ndarray    # int32 [S], including the chunk
+    query_start: np.ndarray     # int32 [S + 1]
+    k_new: np.ndarray           # fp16 [T, Hkv, D], the chunk's keys
+    v_new: np.ndarray           # fp16 [T, Hkv, D]
+    slot_mapping: np.ndarray    # int64 [T]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_query_len(self) -> int:
+        return int(np.diff(self.query_start).max()) if self.num_seqs else 0
+
+    def kv_bytes_per_token_layer(self) -> int:
+        return 2 * self.num_kv_heads * self.head_dim * 2
+
+
+def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=None,
+                          chunk_lens=None, num_seqs=None, cached_range=None, chunk=None,
+                          pool_factor=1.25, scale=None) -> PrefillWorkload:
+    """Chunks of ``chunk_lens`` query tokens ending contexts of ``context_lens``
+    (or: ``num_seqs`` sequences with ``rng.integers`` cached lengths in
+    ``cached_range`` plus a fixed ``chunk``).  Draws, in order: cached lengths
+    (if drawn), the pool permutation, K pool, V pool, q, the chunk's k and v.
+    Blocks no table references and the chunk's own slots (until the append)
+    are NaN; slots past the context in its last block hold canaries."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    if context_lens is None:
+        lo, hi = cached_range
+        cached = rng.integers(lo, hi + 1, size=num_seqs).astype(np.int64)
+        nqs = np.full(num_seqs, chunk, dtype=np.int64)
+        lens = cached + nqs
+    else:
+        lens = np.asarray(context_lens, dtype=np.int64)
+        nqs = np.asarray(chunk_lens, dtype=np.int64)
+    assert (nqs >= 0).all() and (nqs <= lens).all()
+    S = lens.size
+    MB = max(1, -(-int(lens.max()) // BLOCK_SIZE))
+    needed = int(sum(-(-int(n) // BLOCK_SIZE) for n in lens))
+    NB = max(1, math.ceil(pool_factor * needed))
+    perm = rng.permutation(NB)
+    bm = BlockManager(NB, free_order=perm)
+    slots = []
+    for s in range(S):
+        bm.allocate(s, int(lens[s] - nqs[s]))
+        for _ in range(int(nqs[s])):
+            slot, cow = bm.append_token(s)
+            assert cow is None
+            slots.append(slot)
+    tables = bm.table_array(range(S), MB)
+    T = int(nqs.sum())
+    k_cache = np.empty((NB, Hkv, D // CHUNK, BLOCK_SIZE, CHUNK), dtype=np.float16)
+    v_cache = np.empty((NB, Hkv, BLOCK_SIZE // CHUNK, D, CHUNK), dtype=np.float16)
+    _fill_normal_fp16(rng, k_cache)
+    _fill_normal_fp16(rng, v_cache)
+    q = np.empty((T, Hq, D), dtype=np.float16)
+    _fill_normal_fp16(rng, q)
+    k_new = np.empty((T, Hkv, D), dtype=np.float16)
+    v_new = np.empty((T, Hkv, D), dtype=np.float16)
+    _fill_normal_fp16(rng, k_new)
+    _fill_normal_fp16(rng, v_new)
+    ku, vu = k_cache.view(np.uint16), v_cache.view(np.uint16)
+    referenced = np.zeros(NB, dtype=bool)
+    for s in range(S):
+        referenced[bm.tables[s]] = True
+    ku[~referenced] = FP16_NAN
+    vu[~referenced] = FP16_NAN
+    for slot in slots:
+        _set_slot_bits(ku, vu, slot // BLOCK_SIZE, slot % BLOCK_SIZE, FP16_NAN)
+    for s in range(S):
+        n = int(lens[s])
+        if n % BLOCK_SIZE:
+            blk = bm.tables[s][n // BLOCK_SIZE]
+            for o in range(n % BLOCK_SIZE, BLOCK_SIZE):
+                _set_slot_bits(ku, vu, blk, o, _CANARIES[o % 3])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return PrefillWorkload(
+        name=name, seed=seed, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+        num_blocks=NB, max_blocks_per_seq=MB, scale=np.float32(scale), q=q,
+        k_cache=k_cache, v_cache=v_cache, block_tables=tables,
+        context_lens=lens.astype(np.int32),
+        query_start=np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32),
+        k_new=k_new, v_new=v_new, slot_mapping=np.asarray(slots, dtype=np.int64),
+        meta={"pool_factor": pool_factor})
+
+
+PREFILL_WORKLOADS = {
+    # tiny: chunks that start a sequence, a single token, one crossing a block
+    # boundary, one shorter than its context
+    "prefill_tiny": dict(seed=11, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                         context_lens=[5, 16, 40, 100], chunk_lens=[5, 1, 17, 64], scale=1.0 / 8.0),
+    # chunked prefill on the Llama-3.1-8B layer shape: 16 sequences each adding
+    # a 512-token chunk (one of the chunk sizes the ttlab page measures) to a
+    # cached context uniform in [0, 3584] tokens
+    "chunked_prefill_llama": dict(seed=12, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                  num_seqs=16, cached_range=(0, 3584), chunk=512),
+    # prefix-cache hit continuation (aquanode "Prefix caching" example): a
+    # 2,100-token prompt with 2,000 tokens cached leaves a 100-token chunk;
+    # 32 such sequences on the Llama-3.1-8B layer shape
+    "prefix_hit_llama": dict(seed=13, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             context_lens=[2100] * 32, chunk_lens=[100] * 32),
+}
+
+
+def make_named_prefill(name: str, **overrides) -> PrefillWorkload:
+    kw = dict(PREFILL_WORKLOADS[name])
+    kw.update(overrides)
+    return make_prefill_workload(name, **kw)
