@@ -105,6 +105,114 @@ def cpu_baseline(w, budget_s):
                       f"{w.num_seqs} sequences), NumPy"}
 
 
+PREFILL_METRIC = "multi-query paged attention (chunked prefill): achieved TFLOP/s (fraction of peak)"
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_cpu_baseline(w, budget_s):
+    """The prefill oracle (as it is) on whole sequences of the same batch, as
+    many as fit about half the budget, scaled to TFLOP/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    kc, vc = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_mapping)
+    flops, seqs, t0 = 0, 0, time.perf_counter()
+    for s in range(w.num_seqs):
+        a, b = int(w.query_start[s]), int(w.query_start[s + 1])
+        oracle.prefill(w.q[a:b], kc, vc, w.block_tables[s:s + 1], w.context_lens[s:s + 1],
+                       np.array([0, b - a], np.int32), w.scale, w.num_kv_heads)
+        flops += oracle.prefill_flops(w.context_lens[s:s + 1], [0, b - a], w.num_q_heads,
+                                      w.head_dim)
+        seqs += 1
+        if time.perf_counter() - t0 >= budget_s * 0.5:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "seconds": el, "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{seqs} of {w.num_seqs} sequences' chunks of {w.name} (fp64 NumPy, "
+                      "append excluded)"}
+
+
+def bench_prefill(args):
+    """One step = append of every chunk's K/V + multi-query attention.  The
+    attention is MFMA-bound (4 Hq D flops per query-key pair against 4 Hkv D
+    bytes per key), so it is priced against the fp16 MFMA peak."""
+    import torch
+    import oracle
+    from paged_kv_cache_59_amd import binding as pk
+    from paged_kv_cache_59_amd import workloads as wl
+
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    w = wl.make_named_prefill(args.workload)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, tab, lens, qs = t(w.q), t(w.block_tables), t(w.context_lens), t(w.query_start)
+    k_new, v_new, slots = t(w.k_new), t(w.v_new), t(w.slot_mapping)
+    kc, vc = t(w.k_cache), t(w.v_cache)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    flops = oracle.prefill_flops(w.context_lens, w.query_start, w.num_q_heads, w.head_dim)
+
+    def step(ev=None):
+        pk.pa_reshape_and_cache(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pk.pa_prefill(out, q, kc, vc, tab, lens, qs, float(w.scale), w.num_kv_heads,
+                      max_context_len=w.max_context_len, max_query_len=w.max_query_len)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    mean_s = float(ms.mean()) * 1e-3
+    achieved = flops / mean_s / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "tokens_per_s": round(w.num_tokens / (ms_per_step * 1e-3), 1),
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_tokens": w.num_tokens,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": 16, "max_context_len": w.max_context_len,
+            "max_query_len": w.max_query_len, "seed": w.seed, "accumulate": "f32",
+            "flops": flops,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None, "kernel": "prefill_kernel",
+            "mean_us": round(mean_s * 1e6, 3),
+            "median_us": round(float(np.median(ms)) * 1e3, 3),
+            "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 3),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 3),
+            "timing": "HIP events recorded around each prefill call on its stream",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -113,6 +221,10 @@ def main():
         sys.exit(2)
     if args.copy_probe_mb:
         copy_probe(args)
+        return
+    from paged_kv_cache_59_amd import workloads as wl_names
+    if args.workload in wl_names.PREFILL_WORKLOADS:
+        bench_prefill(args)
         return
     import torch
     from paged_kv_cache_59_amd import binding as pk

@@ -51,7 +51,7 @@ __device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c)
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 32;             // 32-dim steps of the contraction over D
   constexpr int DT = D / 16;             // 16-dim tiles of the output
   constexpr int64_t kTile = (int64_t)kBlockSize * D;
@@ -118,19 +118,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   // key of this lane's K rows in S^T sub-tile kt: 8 (c16 / 4) + 4 kt + c16 % 4
   const int kq = 8 * (c16 >> 2) + (c16 & 3);
   half8_t kf[2][KS], vf[DT];
-  auto load_step = [&](int st, half8_t (&k)[2][KS], half8_t (&v)[DT]) {
+  // K and V of step st (table entries clamped to the sequence's last block)
+  auto load_k = [&](int st) {
     const int64_t p0 = phys_of(2 * st), p1 = phys_of(2 * st + 1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kq + 4 * kt;  // < 32
       const half_t* kp = a.k_cache + (key < 16 ? p0 : p1) * bstride + hoff + (key & 15) * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) k[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * 16 * 8);
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * 16 * 8);
     }
+  };
+  auto load_v = [&](int st) {
     // V^T operand: keys 8j..8j+7 = block j / 2, 8-token group j % 2
-    const half_t* vp = a.v_cache + ((j < 2) ? p0 : p1) * bstride + hoff + (int64_t)(j & 1) * D * 8;
+    const int64_t pv = phys_of(2 * st + (j >> 1));
+    const half_t* vp = a.v_cache + pv * bstride + hoff + (int64_t)(j & 1) * D * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) v[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
   };
 
   float4v o[2][DT];
@@ -141,16 +145,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_lane[2] = {0.0f, 0.0f};
 
-  load_step(0, kf, vf);
+  // Pipeline: step st+1's K is issued once step st's logits are done with
+  // kf, its V once step st's value product is done with vf; the loads then
+  // fly under the softmax and the other product.
+  load_k(0);
+  load_v(0);
   for (int st = 0; st < nsteps; ++st) {
-    half8_t kc[2][KS], vc[DT];
+    const bool more = st + 1 < nsteps;
+    // logits of both row sub-tiles, then the next step's K
+    float4v sacc[2][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kc[kt][ks] = kf[kt][ks];
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[rt][kt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vc[dt] = vf[dt];
-    if (st + 1 < nsteps) load_step(st + 1, kf, vf);  // next step's K/V in flight
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[rt][kt] = mfma16x16x32(kf[kt][ks], qf[rt][ks], sacc[rt][kt]);
+      }
+    if (more) load_k(st + 1);
+
     // positions past the context (the last block's tail: any bits, NaN
     // included, and re-read blocks past it) get V := 0 by selection; their
     // logits are removed below, and 0 * NaN would not be 0
@@ -159,27 +173,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       for (int e = 0; e < 8; ++e) {
         const bool dead = st * 32 + 8 * j + e >= len;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vc[dt][e] = dead ? (half_t)0.0f : vc[dt][e];
+        for (int dt = 0; dt < DT; ++dt) vf[dt][e] = dead ? (half_t)0.0f : vf[dt][e];
       }
     }
 
     half8_t pf[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      float4v sacc[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[kt] = mfma16x16x32(kc[kt][ks], qf[rt][ks], sacc[kt]);
-      }
       // logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row
       float z[8];
       float mt = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kp = st * 32 + 8 * j + e;
-        z[e] = kp <= pos[rt] ? sacc[e >> 2][e & 3] * a.scale_log2 : -INFINITY;
+        z[e] = kp <= pos[rt] ? sacc[rt][e >> 2][e & 3] * a.scale_log2 : -INFINITY;
         mt = fmaxf(mt, z[e]);
       }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -202,7 +209,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vc[dt], pf[rt], o[rt][dt]);
+      for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vf[dt], pf[rt], o[rt][dt]);
+    if (more) load_v(st + 1);
   }
 
   // out[row][dims 16 dt + 4 j .. +3] = O^T / l
