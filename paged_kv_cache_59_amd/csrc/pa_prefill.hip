@@ -44,6 +44,18 @@ __device__ __forceinline__ half8_t ld16(const half_t* p) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// sum of the 8 halves of v, accumulated in fp32 (v_dot2_f32_f16 against ones)
+__device__ __forceinline__ float sum8(half8_t v) {
+  const half2v one = {(half_t)1.0f, (half_t)1.0f};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2(half2v{v[2 * i], v[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+
 __device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -55,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 32;             // 32-dim steps of the contraction over D
   constexpr int DT = D / 16;             // 16-dim tiles of the output
   constexpr int64_t kTile = (int64_t)kBlockSize * D;
+  constexpr float kStale = 8.0f;         // see the rescale below
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -95,6 +108,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     pos[rt] = valid[rt] ? len - nq + tok[rt] : -1;
   }
   const int last_row = min(tile * 32 + 31, rows - 1);
+  const int pos_first = len - nq + (tile * 32) / G;  // the tile's first (smallest) position
   const int pos_max = len - nq + last_row / G;
   const int nsteps = pos_max / 32 + 1;  // 32-key steps covering keys 0 .. pos_max
 
@@ -111,16 +125,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int last_blk = (len + kBlockSize - 1) / kBlockSize - 1;
   const int64_t hoff = (int64_t)h * kTile;
   const int64_t bstride = (int64_t)a.num_kv_heads * kTile;
+  // physical block of logical block lb (clamped to the sequence's last): a
+  // scalar load, whose wait (lgkmcnt) does not drain the K/V loads in flight
   auto phys_of = [&](int lb) -> int64_t {
-    const int e = row[min(lb, last_blk)];
+    const int e = row[__builtin_amdgcn_readfirstlane(min(lb, last_blk))];
     return (e >= 0 && e < a.num_blocks) ? e : 0;  // a broken table entry reads block 0
   };
   // key of this lane's K rows in S^T sub-tile kt: 8 (c16 / 4) + 4 kt + c16 % 4
   const int kq = 8 * (c16 >> 2) + (c16 & 3);
   half8_t kf[2][KS], vf[DT];
-  // K and V of step st (table entries clamped to the sequence's last block)
-  auto load_k = [&](int st) {
-    const int64_t p0 = phys_of(2 * st), p1 = phys_of(2 * st + 1);
+  // K and V of a step held in blocks p0 (keys 0..15) and p1 (keys 16..31)
+  auto load_k = [&](int64_t p0, int64_t p1) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kq + 4 * kt;  // < 32
@@ -129,10 +144,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * 16 * 8);
     }
   };
-  auto load_v = [&](int st) {
+  auto load_v = [&](int64_t p0, int64_t p1) {
     // V^T operand: keys 8j..8j+7 = block j / 2, 8-token group j % 2
-    const int64_t pv = phys_of(2 * st + (j >> 1));
-    const half_t* vp = a.v_cache + pv * bstride + hoff + (int64_t)(j & 1) * D * 8;
+    const half_t* vp = a.v_cache + (j < 2 ? p0 : p1) * bstride + hoff + (int64_t)(j & 1) * D * 8;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
   };
@@ -148,10 +162,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // Pipeline: step st+1's K is issued once step st's logits are done with
   // kf, its V once step st's value product is done with vf; the loads then
   // fly under the softmax and the other product.
-  load_k(0);
-  load_v(0);
+  {
+    const int64_t p0 = phys_of(0), p1 = phys_of(1);
+    load_k(p0, p1);
+    load_v(p0, p1);
+  }
   for (int st = 0; st < nsteps; ++st) {
-    const bool more = st + 1 < nsteps;
+    // every step issues the same loads (the last one re-reads its own blocks,
+    // which hit L2), so the hardware wait counts stay exact across the loop;
+    // the next step's table entries load under this step's logits
+    const int nxt = min(st + 1, nsteps - 1);
+    const int64_t pn0 = phys_of(2 * nxt), pn1 = phys_of(2 * nxt + 1);
     // logits of both row sub-tiles, then the next step's K
     float4v sacc[2][2];
 #pragma unroll
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           sacc[rt][kt] = mfma16x16x32(kf[kt][ks], qf[rt][ks], sacc[rt][kt]);
       }
-    if (more) load_k(st + 1);
+    load_k(pn0, pn1);
 
     // positions past the context (the last block's tail: any bits, NaN
     // included, and re-read blocks past it) get V := 0 by selection; their
@@ -177,40 +198,51 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
     }
 
+    // logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row, in
+    // log2 units; keys past a row's position are removed (only the steps that
+    // reach past the tile's first position can hold such keys)
+    float z[2][8], mt[2];
+    const bool masked = st * 32 + 31 > pos_first;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      mt[rt] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        z[rt][e] = sacc[rt][e >> 2][e & 3] * a.scale_log2;
+        if (masked) z[rt][e] = st * 32 + 8 * j + e <= pos[rt] ? z[rt][e] : -INFINITY;
+        mt[rt] = fmaxf(mt[rt], z[rt][e]);
+      }
+      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16));
+      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32));
+    }
+    // The reference max m_run is raised only when a row's max passes it by
+    // more than kStale (log2 units); otherwise the weights exp2(z - m_run)
+    // stay below 2^kStale, well inside fp16, and O and l need no rescale.
+    // The result O / l does not depend on the reference.
+    if (__any(mt[0] > m_run[0] + kStale || mt[1] > m_run[1] + kStale)) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float m_new = fmaxf(m_run[rt], mt[rt]);
+        const float alpha = m_run[rt] == -INFINITY ? 0.0f : exp2_fast(m_run[rt] - m_new);
+        l_lane[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+        m_run[rt] = m_new;
+      }
+    }
     half8_t pf[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      // logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row
-      float z[8];
-      float mt = -INFINITY;
+      const bool none = m_run[rt] == -INFINITY;  // no key seen yet (an invalid row)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kp = st * 32 + 8 * j + e;
-        z[e] = kp <= pos[rt] ? sacc[rt][e >> 2][e & 3] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, z[e]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run[rt], mt);
-      const bool none = m_new == -INFINITY;  // no key seen yet (or an invalid row)
-      const float alpha = none ? 1.0f : exp2_fast(m_run[rt] - m_new);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const half_t ph = none ? (half_t)0.0f : (half_t)exp2_fast(z[e] - m_new);
-        pf[rt][e] = ph;
-        lsum += (float)ph;
-      }
-      l_lane[rt] = l_lane[rt] * alpha + lsum;
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+      for (int e = 0; e < 8; ++e) pf[rt][e] = none ? (half_t)0.0f : (half_t)exp2_fast(z[rt][e] - m_run[rt]);
+      l_lane[rt] += sum8(pf[rt]);
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vf[dt], pf[rt], o[rt][dt]);
-    if (more) load_v(st + 1);
+    load_v(pn0, pn1);
   }
 
   // out[row][dims 16 dt + 4 j .. +3] = O^T / l
