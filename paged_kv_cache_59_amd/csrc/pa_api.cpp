@@ -206,7 +206,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
     return PA_ERR_INVALID_ARG;
   const int64_t G = num_q_heads / num_kv_heads;
   const int64_t tile_groups = ceil_div(ceil_div((int64_t)max_query_len * G, 32), 4);
-  if ((int64_t)num_seqs * num_kv_heads * tile_groups + 7 > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+  if (((int64_t)num_seqs * num_kv_heads + 7) / 8 * 8 * tile_groups > 0x7fffffff)
+    return PA_ERR_UNSUPPORTED;
   pa::PrefillArgs a{};
   a.out = static_cast<pa::half_t*>(out);
   a.q = static_cast<const pa::half_t*>(q);

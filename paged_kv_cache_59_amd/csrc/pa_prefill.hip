@@ -74,15 +74,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int c16 = lane & 15;  // column of the MFMA operands / results: this lane's row
   const int j = lane >> 4;    // k-slot group
 
-  // blocks of one (sequence, KV head) run on one XCD (workgroup i -> XCD i % 8)
-  const int nb_total = gridDim.x;
-  const int b = (nb_total % 8 == 0) ? (int)(blockIdx.x % 8) * (nb_total / 8) + (int)(blockIdx.x / 8)
-                                    : (int)blockIdx.x;
-  const int sh = b / a.tile_groups;
+  // Workgroup i runs on XCD i % 8.  (sequence, KV head) pairs are dealt to
+  // the XCDs round-robin (XCD x takes pairs x, x + 8, ...), so that the KV
+  // heads of one sequence -- equal work -- spread over the XCDs while all
+  // workgroups of one pair share one L2; within a pair the tile groups go
+  // last first, the ones with the most keys (causal) dispatched first.
+  const int xcd = (int)(blockIdx.x % 8);
+  const int m = (int)(blockIdx.x / 8);
+  const int sh = 8 * (m / a.tile_groups) + xcd;
   if (sh >= a.num_seqs * a.num_kv_heads) return;
   const int s = sh / a.num_kv_heads;
   const int h = sh - s * a.num_kv_heads;
-  const int tile = (b - sh * a.tile_groups) * 4 + wave;
+  const int tile = (a.tile_groups - 1 - m % a.tile_groups) * 4 + wave;
 
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
@@ -265,8 +268,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.num_seqs * a.num_kv_heads * a.tile_groups;
-  const int64_t padded = (blocks + 7) / 8 * 8;
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+  const int64_t padded = (pairs + 7) / 8 * 8 * a.tile_groups;  // 8 XCDs x pairs/8 x tile groups
   if (a.head_dim == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)padded), dim3(256), 0, stream, a);
   else
