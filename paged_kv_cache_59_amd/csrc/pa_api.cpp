@@ -217,7 +217,11 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.context_lens = context_lens;
   a.query_start = query_start;
   a.num_tokens = num_tokens;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
+  // the kernel takes a positive factor: a negative scale becomes a sign flip
+  // of q (exact), and a zero one a factor far below any logit's resolution
+  const double sl2 = std::fabs((double)scale) * 1.4426950408889634;  // log2(e) = 1 / ln 2
+  a.scale_log2 = (float)(sl2 > 1e-30 ? sl2 : 1e-30);
+  a.negate_q = scale < 0.0f ? 1 : 0;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

@@ -118,7 +118,8 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* query_start;
   int num_tokens;    // rows of q and out
-  float scale_log2;  // softmax scale times log2(e)
+  float scale_log2;  // |softmax scale| times log2(e), at least 1e-30
+  int negate_q;      // the scale is negative: q enters with its sign flipped
   int num_seqs, num_q_heads, num_kv_heads, head_dim;
   int max_blocks_per_seq;
   int64_t num_blocks;

@@ -45,6 +45,7 @@ __device__ __forceinline__ half8_t ld16(const half_t* p) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 // sum of the 8 halves of v, accumulated in fp32 (v_dot2_f32_f16 against ones)
 __device__ __forceinline__ float sum8(half8_t v) {
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int DT = D / 16;             // 16-dim tiles of the output
   constexpr int64_t kTile = (int64_t)kBlockSize * D;
   constexpr float kStale = 8.0f;         // see the rescale below
+  constexpr float kFloor = -1.0e30f;     // initial reference max (log2 units)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -121,7 +123,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   for (int rt = 0; rt < 2; ++rt) {
     const half_t* qp = a.q + ((int64_t)(t0 + tok[rt]) * Hq + h * G + grp[rt]) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld16(qp + ks * 32 + j * 8);
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[rt][ks] = ld16(qp + ks * 32 + j * 8);
+      if (a.negate_q) qf[rt][ks] = -qf[rt][ks];  // exact: a sign flip
+    }
   }
 
   const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
@@ -159,7 +164,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  // Reference max per row, log2 units.  It starts at a finite floor far
+  // below any logit, so exp2(z - m) is 0 for removed keys (z = -inf) without
+  // a select, and the first key raises it (the rescale below).
+  float m_run[2] = {kFloor, kFloor};
   float l_lane[2] = {0.0f, 0.0f};
 
   // Pipeline: step st+1's K is issued once step st's logits are done with
@@ -192,31 +200,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // positions past the context (the last block's tail: any bits, NaN
     // included, and re-read blocks past it) get V := 0 by selection; their
     // logits are removed below, and 0 * NaN would not be 0
-    if (st * 32 + 32 > len) {
+    // raw logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row.
+    // The scale c > 0 (the host folds a negative scale into q's sign) enters
+    // through the row max, max(c z) = c max(z), and the exponent's fma.
+    float z[2][8], mt[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[rt][e] = sacc[rt][e >> 2][e & 3];
+    // Only the steps that reach past the tile's first position can hold keys
+    // past a row's position (removed: z = -inf) or past the context (V := 0
+    // by selection: the last block's tail holds any bits, NaN included, and
+    // 0 * NaN would not be 0).  One uniform branch for both.
+    if (__builtin_amdgcn_readfirstlane(st * 32 + 31 > pos_first)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool dead = st * 32 + 8 * j + e >= len;
+        const int kp = st * 32 + 8 * j + e;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[dt][e] = dead ? (half_t)0.0f : vf[dt][e];
+        for (int rt = 0; rt < 2; ++rt) z[rt][e] = kp <= pos[rt] ? z[rt][e] : -INFINITY;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[dt][e] = kp >= len ? (half_t)0.0f : vf[dt][e];
       }
     }
-
-    // logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row, in
-    // log2 units; keys past a row's position are removed (only the steps that
-    // reach past the tile's first position can hold such keys)
-    float z[2][8], mt[2];
-    const bool masked = st * 32 + 31 > pos_first;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       mt[rt] = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        z[rt][e] = sacc[rt][e >> 2][e & 3] * a.scale_log2;
-        if (masked) z[rt][e] = st * 32 + 8 * j + e <= pos[rt] ? z[rt][e] : -INFINITY;
-        mt[rt] = fmaxf(mt[rt], z[rt][e]);
-      }
+      for (int e = 0; e < 8; ++e) mt[rt] = fmaxf(mt[rt], z[rt][e]);
       mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16));
-      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32));
+      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32)) * a.scale_log2;
     }
     // The reference max m_run is raised only when a row's max passes it by
     // more than kStale (log2 units); otherwise the weights exp2(z - m_run)
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const float m_new = fmaxf(m_run[rt], mt[rt]);
-        const float alpha = m_run[rt] == -INFINITY ? 0.0f : exp2_fast(m_run[rt] - m_new);
+        const float alpha = exp2_fast(m_run[rt] - m_new);  // 0 when leaving the floor
         l_lane[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
@@ -236,9 +248,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     half8_t pf[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const bool none = m_run[rt] == -INFINITY;  // no key seen yet (an invalid row)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[rt][e] = none ? (half_t)0.0f : (half_t)exp2_fast(z[rt][e] - m_run[rt]);
+      for (int e = 0; e < 8; e += 2) {
+        const float2v w = {exp2_fast(__builtin_fmaf(z[rt][e], a.scale_log2, -m_run[rt])),
+                           exp2_fast(__builtin_fmaf(z[rt][e + 1], a.scale_log2, -m_run[rt]))};
+        const half2v hw = __builtin_convertvector(w, half2v);  // round to nearest even
+        pf[rt][e] = hw[0];
+        pf[rt][e + 1] = hw[1];
+      }
       l_lane[rt] += sum8(pf[rt]);
     }
 #pragma unroll

@@ -205,3 +205,18 @@ def test_prefill_full_size_sampled(name):
         rows += [t0, t0 + 1, (t0 + t1) // 2, t1 - 1]
     rows = np.unique(rows)
     compare(out[rows], oracle_rows(w, kc, vc, rows), f"{name} sampled")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_prefill_negative_and_zero_scale(scale):
+    """A negative scale enters as a sign flip of q (exact); a zero scale gives
+    every visible key the same weight: the mean of the visible V rows."""
+    w = wl.make_prefill_workload("scale", 604, 8, 2, 128, context_lens=[70, 300],
+                                 chunk_lens=[70, 45], scale=scale)
+    out = run_full_parity(w, f"scale {scale}")
+    if scale == 0.0:
+        kc, vc = oracle_pools_prefill(w)
+        k, v = oracle.gather_sequence(kc, vc, w.block_tables[0], 70, 2, 128)
+        for i in (0, 1, 69):
+            mean = v[:, :i + 1].mean(axis=1)              # [Hkv, D]
+            assert np.abs(out[i].astype(np.float64) - np.repeat(mean, 4, axis=0)).max() < 2e-3
