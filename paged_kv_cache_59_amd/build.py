@@ -20,7 +20,8 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip",
+           "pa_block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
