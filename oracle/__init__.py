@@ -7,6 +7,7 @@ from .paged_attention import (  # noqa: F401
     BLOCK_SIZE,
     reshape_and_cache,
     copy_blocks,
+    swap_blocks,
     decode,
     decode_step,
     gather_sequence,

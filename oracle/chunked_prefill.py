@@ -38,7 +38,8 @@ def query_position(n, nq, i):
     return n - nq + i
 
 
-def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_kv_heads):
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_kv_heads,
+            block_size=BLOCK_SIZE):
     """Causal attention of each sequence's query chunk, float64 [T, Hq, D].
 
     q: fp16 [T, Hq, D], the chunks of all sequences packed: rows
@@ -64,8 +65,8 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
         assert 0 <= nq <= n, "a chunk is at most the sequence's context"
         if nq == 0:
             continue
-        assert n <= tables.shape[1] * BLOCK_SIZE, "context longer than its block table"
-        kc, vc = _pa.gather_sequence(k_cache, v_cache, tables[s], n, num_kv_heads, D)
+        assert n <= tables.shape[1] * block_size, "context longer than its block table"
+        kc, vc = _pa.gather_sequence(k_cache, v_cache, tables[s], n, num_kv_heads, D, block_size)
         for i in range(nq):
             p = query_position(n, nq, i)
             for h in range(Hq):

@@ -61,50 +61,52 @@ CHUNK = 8           # fp16 elements per 16-byte chunk in the K layout / per half
 
 
 # ---------------------------------------------------------------------------
-# Layout: views of the pools as logical [num_blocks, num_kv_heads, 16, D]
+# Layout: views of the pools as logical [num_blocks, num_kv_heads, BS, D]
+# (BS = block size: 16 by default, 8 and 32 as the variants the pages name as
+# the one tunable of the kernel: "FAQ", "What block size should I use?")
 # ---------------------------------------------------------------------------
 
-def _k5(k_cache: np.ndarray, num_kv_heads: int, head_dim: int) -> np.ndarray:
-    """The K pool as its 5-d ABI shape [NB, Hkv, D/8, 16, 8] (a view)."""
-    nb = k_cache.size // (num_kv_heads * head_dim * BLOCK_SIZE)
-    return k_cache.reshape(nb, num_kv_heads, head_dim // CHUNK, BLOCK_SIZE, CHUNK)
+def _k5(k_cache: np.ndarray, num_kv_heads: int, head_dim: int, block_size=BLOCK_SIZE):
+    """The K pool as its 5-d ABI shape [NB, Hkv, D/8, BS, 8] (a view)."""
+    nb = k_cache.size // (num_kv_heads * head_dim * block_size)
+    return k_cache.reshape(nb, num_kv_heads, head_dim // CHUNK, block_size, CHUNK)
 
 
-def _v5(v_cache: np.ndarray, num_kv_heads: int, head_dim: int) -> np.ndarray:
-    """The V pool as its 5-d ABI shape [NB, Hkv, 2, D, 8] (a view)."""
-    nb = v_cache.size // (num_kv_heads * head_dim * BLOCK_SIZE)
-    return v_cache.reshape(nb, num_kv_heads, BLOCK_SIZE // CHUNK, head_dim, CHUNK)
+def _v5(v_cache: np.ndarray, num_kv_heads: int, head_dim: int, block_size=BLOCK_SIZE):
+    """The V pool as its 5-d ABI shape [NB, Hkv, BS/8, D, 8] (a view)."""
+    nb = v_cache.size // (num_kv_heads * head_dim * block_size)
+    return v_cache.reshape(nb, num_kv_heads, block_size // CHUNK, head_dim, CHUNK)
 
 
-def logical_k_blocks(k_cache, phys, num_kv_heads, head_dim) -> np.ndarray:
-    """K of the listed physical blocks as [len(phys), Hkv, 16, D] (a copy).
+def logical_k_blocks(k_cache, phys, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
+    """K of the listed physical blocks as [len(phys), Hkv, BS, D] (a copy).
 
     Element (b, h, o, d) is read from k[b, h, d // 8, o, d % 8].
     """
-    k5 = _k5(k_cache, num_kv_heads, head_dim)[np.asarray(phys, dtype=np.int64)]
-    # [n, Hkv, D/8, 16, 8] -> [n, Hkv, 16, D/8, 8] -> [n, Hkv, 16, D]
-    return k5.transpose(0, 1, 3, 2, 4).reshape(len(phys), num_kv_heads, BLOCK_SIZE, head_dim)
+    k5 = _k5(k_cache, num_kv_heads, head_dim, block_size)[np.asarray(phys, dtype=np.int64)]
+    # [n, Hkv, D/8, BS, 8] -> [n, Hkv, BS, D/8, 8] -> [n, Hkv, BS, D]
+    return k5.transpose(0, 1, 3, 2, 4).reshape(len(phys), num_kv_heads, block_size, head_dim)
 
 
-def logical_v_blocks(v_cache, phys, num_kv_heads, head_dim) -> np.ndarray:
-    """V of the listed physical blocks as [len(phys), Hkv, 16, D] (a copy).
+def logical_v_blocks(v_cache, phys, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
+    """V of the listed physical blocks as [len(phys), Hkv, BS, D] (a copy).
 
     Element (b, h, o, d) is read from v[b, h, o // 8, d, o % 8].
     """
-    v5 = _v5(v_cache, num_kv_heads, head_dim)[np.asarray(phys, dtype=np.int64)]
-    # [n, Hkv, 2, D, 8] -> [n, Hkv, 2, 8, D] -> [n, Hkv, 16, D]
-    return v5.transpose(0, 1, 2, 4, 3).reshape(len(phys), num_kv_heads, BLOCK_SIZE, head_dim)
+    v5 = _v5(v_cache, num_kv_heads, head_dim, block_size)[np.asarray(phys, dtype=np.int64)]
+    # [n, Hkv, BS/8, D, 8] -> [n, Hkv, BS/8, 8, D] -> [n, Hkv, BS, D]
+    return v5.transpose(0, 1, 2, 4, 3).reshape(len(phys), num_kv_heads, block_size, head_dim)
 
 
 # ---------------------------------------------------------------------------
 # O1: append the new tokens' K/V into their slots
 # ---------------------------------------------------------------------------
 
-def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping):
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size=BLOCK_SIZE):
     """Write token t's K and V rows into slot ``slot_mapping[t]``.
 
     The cache grows by one entry per token ("TL;DR"); the entry lands in
-    physical block ``slot // 16`` at offset ``slot % 16`` (block table
+    physical block ``slot // BS`` at offset ``slot % BS`` (block table
     semantics, "PagedAttention: a block table for the KV cache").  Negative
     slots are padding and are skipped.  The write is a bit copy.
 
@@ -119,14 +121,14 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping):
     assert np.unique(live).size == live.size, "two tokens share one slot"
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
-    k5 = _k5(kc, Hkv, D)
-    v5 = _v5(vc, Hkv, D)
+    k5 = _k5(kc, Hkv, D, block_size)
+    v5 = _v5(vc, Hkv, D, block_size)
     nb = k5.shape[0]
     for t in range(T):
         s = int(slots[t])
         if s < 0:
             continue
-        b, o = divmod(s, BLOCK_SIZE)
+        b, o = divmod(s, block_size)
         assert 0 <= b < nb, "slot outside the pool"
         # K: k[b, h, d // 8, o, d % 8] = k_new[t, h, d]
         k5[b, :, :, o, :] = k[t].reshape(Hkv, D // CHUNK, CHUNK)
@@ -139,7 +141,7 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping):
 # O2: copy-on-write block copy
 # ---------------------------------------------------------------------------
 
-def copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, head_dim):
+def copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
     """For each (src, dst) pair copy the whole block, K and V, all KV heads.
 
     Copy-on-write at block granularity when a shared block must take an append
@@ -151,8 +153,8 @@ def copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, head_dim):
     pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
-    k5 = _k5(kc, num_kv_heads, head_dim)
-    v5 = _v5(vc, num_kv_heads, head_dim)
+    k5 = _k5(kc, num_kv_heads, head_dim, block_size)
+    v5 = _v5(vc, num_kv_heads, head_dim, block_size)
     nb = k5.shape[0]
     if pairs.shape[0] == 0:
         return kc, vc
@@ -172,7 +174,7 @@ def copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, head_dim):
 # O3: decode attention through the block table
 # ---------------------------------------------------------------------------
 
-def gather_sequence(k_cache, v_cache, table_row, n, num_kv_heads, head_dim):
+def gather_sequence(k_cache, v_cache, table_row, n, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
     """Rebuild one sequence's contiguous K and V, each [Hkv, n, D] float64.
 
     Logical block j lives in physical block ``table_row[j]``; only the first
@@ -180,12 +182,12 @@ def gather_sequence(k_cache, v_cache, table_row, n, num_kv_heads, head_dim):
     unused tail of the last block never enters (ttlab section 2 "Blocks and
     Block Tables": only the last block is partly filled).
     """
-    nb = -(-n // BLOCK_SIZE)
+    nb = -(-n // block_size)
     phys = np.asarray(table_row[:nb], dtype=np.int64)
-    kb = logical_k_blocks(k_cache, phys, num_kv_heads, head_dim)   # [nb, Hkv, 16, D]
-    vb = logical_v_blocks(v_cache, phys, num_kv_heads, head_dim)
-    kc = kb.transpose(1, 0, 2, 3).reshape(num_kv_heads, nb * BLOCK_SIZE, head_dim)[:, :n]
-    vc = vb.transpose(1, 0, 2, 3).reshape(num_kv_heads, nb * BLOCK_SIZE, head_dim)[:, :n]
+    kb = logical_k_blocks(k_cache, phys, num_kv_heads, head_dim, block_size)   # [nb, Hkv, BS, D]
+    vb = logical_v_blocks(v_cache, phys, num_kv_heads, head_dim, block_size)
+    kc = kb.transpose(1, 0, 2, 3).reshape(num_kv_heads, nb * block_size, head_dim)[:, :n]
+    vc = vb.transpose(1, 0, 2, 3).reshape(num_kv_heads, nb * block_size, head_dim)[:, :n]
     return kc.astype(np.float64), vc.astype(np.float64)
 
 
@@ -200,7 +202,8 @@ def attention_one_query(qv, kc, vc, scale):
     return (p @ vc) / p.sum()
 
 
-def decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads):
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
+           block_size=BLOCK_SIZE):
     """One decode step of attention for every sequence, float64 [S, Hq, D].
 
     Same attention as over contiguous K/V ("FAQ": it is not a different
@@ -222,8 +225,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads)
         n = int(lens[s])
         if n <= 0:
             continue
-        assert n <= tables.shape[1] * BLOCK_SIZE, "context longer than its block table"
-        kc, vc = gather_sequence(k_cache, v_cache, tables[s], n, num_kv_heads, D)
+        assert n <= tables.shape[1] * block_size, "context longer than its block table"
+        kc, vc = gather_sequence(k_cache, v_cache, tables[s], n, num_kv_heads, D, block_size)
         for h in range(Hq):
             kh = h // G
             out[s, h] = attention_one_query(q[s, h].astype(np.float64), kc[kh], vc[kh], scale64)
@@ -231,7 +234,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads)
 
 
 def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
-                slot_mapping, block_mapping, scale, num_kv_heads):
+                slot_mapping, block_mapping, scale, num_kv_heads, block_size=BLOCK_SIZE):
     """One whole decode step in order: copy-on-write, append, attention.
 
     The order follows the pages: a shared block is copied before the holder
@@ -239,10 +242,32 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
     the cache that includes the new token.  Returns (out, k_cache, v_cache).
     """
     D = q.shape[2]
-    kc, vc = copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, D)
-    kc, vc = reshape_and_cache(k_new, v_new, kc, vc, slot_mapping)
-    out = decode(q, kc, vc, block_tables, context_lens, scale, num_kv_heads)
+    kc, vc = copy_blocks(k_cache, v_cache, block_mapping, num_kv_heads, D, block_size)
+    kc, vc = reshape_and_cache(k_new, v_new, kc, vc, slot_mapping, block_size)
+    out = decode(q, kc, vc, block_tables, context_lens, scale, num_kv_heads, block_size)
     return out, kc, vc
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, num_kv_heads, head_dim,
+                block_size=BLOCK_SIZE):
+    """Copy whole blocks, K and V, between two pools of the same layout:
+    block src of the source pool to block dst of the destination pool.  The
+    pool that a request was preempted to (host memory) and the device pool
+    ("Continuous batching and paged attention", section "Why they depend on
+    each other": preemption by recomputation or by swap to host memory).
+    Pairs with an id outside its pool are skipped.  Returns new (dst_k, dst_v)."""
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    dk = np.array(dst_k, copy=True)
+    dv = np.array(dst_v, copy=True)
+    sk5 = _k5(np.asarray(src_k), num_kv_heads, head_dim, block_size)
+    sv5 = _v5(np.asarray(src_v), num_kv_heads, head_dim, block_size)
+    dk5 = _k5(dk, num_kv_heads, head_dim, block_size)
+    dv5 = _v5(dv, num_kv_heads, head_dim, block_size)
+    for src, dst in pairs:
+        if 0 <= src < sk5.shape[0] and 0 <= dst < dk5.shape[0]:
+            dk5[dst] = sk5[src]
+            dv5[dst] = sv5[src]
+    return dk, dv
 
 
 # ---------------------------------------------------------------------------
