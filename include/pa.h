@@ -3,7 +3,7 @@
  * (gfx950).
  *
  * The library implements the decode-step hot path of paged attention: the KV
- * cache of every sequence lives in fixed blocks of 16 token slots that may sit
+ * cache of every sequence lives in fixed blocks of token slots that may sit
  * anywhere in one shared pool, and a per-sequence block table maps logical
  * block j to its physical block.  Sources (web pages, by title and section):
  *
@@ -26,16 +26,18 @@
  * ---------------------------------------
  *  - Element types: K, V, q and out are IEEE fp16; block tables and context
  *    lengths int32; slot indices and block pairs int64; scale fp32.
- *  - Block size: 16 token slots (the only value accepted; [AQ], [TT]).
+ *  - Block size BS: 16 token slots by default ([AQ], [TT]); 8 and 32 are the
+ *    variants ([AQ] "FAQ": smaller blocks waste less of the last block but
+ *    cost more table entries).  Each entry point states the sizes it takes.
  *  - Pool layout (part of this ABI).  With NB physical blocks, Hkv KV heads
  *    and head dimension D (64 or 128):
- *        K pool: fp16 [NB][Hkv][D/8][16][8]
+ *        K pool: fp16 [NB][Hkv][D/8][BS][8]
  *                element (block b, head h, slot offset o, dim d) at
- *                ((((b*Hkv + h)*(D/8) + d/8)*16 + o)*8 + d%8)
- *        V pool: fp16 [NB][Hkv][2][D][8]
- *                element (b, h, o, d) at ((((b*Hkv + h)*2 + o/8)*D + d)*8 + o%8)
- *    so one (block, head) tile is 16*D contiguous elements in both pools.
- *  - A slot index is  physical_block * 16 + offset  (offset < 16).
+ *                ((((b*Hkv + h)*(D/8) + d/8)*BS + o)*8 + d%8)
+ *        V pool: fp16 [NB][Hkv][BS/8][D][8]
+ *                element (b, h, o, d) at ((((b*Hkv + h)*(BS/8) + o/8)*D + d)*8 + o%8)
+ *    so one (block, head) tile is BS*D contiguous elements in both pools.
+ *  - A slot index is  physical_block * BS + offset  (offset < BS).
  *  - Pointers are device pointers unless stated; all buffers are owned and
  *    allocated by the caller.  The library allocates nothing and keeps no
  *    state beyond a per-device cache of the compute-unit count; it never
@@ -65,7 +67,7 @@ extern "C" {
 enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size     */
-  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block_size not 16, G > 4   */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block size, G > 4        */
   PA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
   PA_ERR_HIP = -4,         /* a HIP call or kernel launch failed              */
 };
@@ -79,9 +81,9 @@ enum {
  *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], contiguous
  *   k_cache       K pool (layout above), v_cache V pool
  *   slot_mapping  int64 [num_tokens]; token t goes to slot slot_mapping[t];
- *                 negative = padding, skipped; >= num_blocks*16 is skipped
+ *                 negative = padding, skipped; >= num_blocks*BS is skipped
  *   Two tokens with the same non-negative slot in one call race (precondition).
- *   The write is a bit copy.  num_tokens == 0 is a no-op.
+ *   The write is a bit copy.  num_tokens == 0 is a no-op.  block_size 8, 16, 32.
  */
 int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                          const int64_t* slot_mapping, int64_t num_tokens,
@@ -96,11 +98,34 @@ int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_ca
  *   block_mapping int64 [num_pairs][2] = (src, dst), device memory
  *   Pairs with src == dst, or an id outside [0, num_blocks), are skipped.
  *   Preconditions: dsts distinct and none of them is also a src.
- *   Reference counting and the decision to copy are the caller's.
+ *   Reference counting and the decision to copy are the caller's
+ *   (pa_block_manager.h makes both).  block_size 8, 16 or 32.
  */
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                    int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * Swap: copy whole blocks, K and V, all KV heads, between two pools of the
+ * same layout -- a request's blocks out to host memory when it is preempted
+ * and back when it resumes ("Continuous batching and paged attention",
+ * "Why they depend on each other": preemption by recomputation or by swap
+ * to host memory).
+ *
+ *   src_k, src_v  source pools (src_num_blocks blocks), dst_k, dst_v the
+ *                 destination pools (dst_num_blocks); either side may be host
+ *                 memory from hipHostMalloc (pinned, device-accessible): the
+ *                 kernel reads or writes it directly over the host link
+ *   block_mapping int64 [num_pairs][2] = (src block, dst block), in device
+ *                 memory or pinned host memory
+ *   Pairs with an id outside its pool are skipped.  Destination blocks must be
+ *   distinct.  The pools must differ (within one pool use pa_copy_blocks).
+ *   block_size 8, 16 or 32.  The copy is a bit copy.
+ */
+int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int64_t* block_mapping, int64_t num_pairs, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, hipStream_t stream);
 
 /*
  * Number of decode workers pa_decode uses when it is passed num_workers == 0:

@@ -24,7 +24,8 @@ PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
-EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_timed",
+EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
+            "pa_decode_timed",
             "pa_prefill", "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.pa_reshape_and_cache.restype = ctypes.c_int
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
     L.pa_copy_blocks.restype = ctypes.c_int
+    L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, i64, vp]
+    L.pa_swap_blocks.restype = ctypes.c_int
     L.pa_decode_num_workers.argtypes = []
     L.pa_decode_num_workers.restype = i32
     L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
@@ -99,13 +102,14 @@ def _stream(t: torch.Tensor, stream):
 
 
 def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor):
-    if k_cache.dim() != 5 or k_cache.shape[3] != BLOCK_SIZE or k_cache.shape[4] != 8:
-        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_dim/8, 16, 8]")
-    nb, hkv, d8 = k_cache.shape[:3]
+    """(num_blocks, num_kv_heads, head_dim, block_size) of a K/V pool pair."""
+    if k_cache.dim() != 5 or k_cache.shape[4] != 8:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_dim/8, block_size, 8]")
+    nb, hkv, d8, bs = k_cache.shape[:4]
     d = d8 * 8
-    if tuple(v_cache.shape) != (nb, hkv, 2, d, 8):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, 2, head_dim, 8]")
-    return int(nb), int(hkv), int(d)
+    if bs % 8 or tuple(v_cache.shape) != (nb, hkv, bs // 8, d, 8):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size/8, head_dim, 8]")
+    return int(nb), int(hkv), int(d), int(bs)
 
 
 def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
@@ -113,13 +117,13 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> N
     for t, n in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n, torch.float16)
     _dev(slot_mapping, "slot_mapping", torch.int64)
-    nb, hkv, d = _cache_geometry(k_cache, v_cache)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
     T = int(slot_mapping.numel())
     if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d):
         raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
     code = lib().pa_reshape_and_cache(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(),
                                       v_cache.data_ptr(), slot_mapping.data_ptr(), T, hkv, d,
-                                      BLOCK_SIZE, nb, _stream(k_cache, stream))
+                                      bs, nb, _stream(k_cache, stream))
     _check(code, "pa_reshape_and_cache")
 
 
@@ -128,11 +132,11 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     _dev(k_cache, "k_cache", torch.float16)
     _dev(v_cache, "v_cache", torch.float16)
     _dev(block_mapping, "block_mapping", torch.int64)
-    nb, hkv, d = _cache_geometry(k_cache, v_cache)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [num_pairs, 2]")
     code = lib().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
-                                int(block_mapping.shape[0]), hkv, d, BLOCK_SIZE, nb,
+                                int(block_mapping.shape[0]), hkv, d, bs, nb,
                                 _stream(k_cache, stream))
     _check(code, "pa_copy_blocks")
 
@@ -177,7 +181,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
     _dev(v_cache, "v_cache", torch.float16)
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32)
-    nb, hkv, d = _cache_geometry(k_cache, v_cache)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
     if hkv != int(num_kv_heads):
         raise ValueError("num_kv_heads does not match k_cache")
     S, hq, dq = q.shape
@@ -187,7 +191,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], context_lens [num_seqs]")
     mb = int(block_tables.shape[1])
     if max_context_len is None:
-        max_context_len = mb * BLOCK_SIZE
+        max_context_len = mb * bs
     if workspace is None:
         workspace = new_workspace(S, hkv, d, int(max_context_len), num_workers, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
@@ -195,7 +199,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
         raise ValueError("scale must be finite")
     args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv, S, hq, d,
-            BLOCK_SIZE, mb, nb, int(max_context_len), int(num_workers), workspace.data_ptr(),
+            bs, mb, nb, int(max_context_len), int(num_workers), workspace.data_ptr(),
             workspace.numel(), _stream(q, stream))
     if kernel_events is None:
         _check(lib().pa_decode(*args), "pa_decode")
@@ -223,7 +227,7 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32)
     _dev(query_start, "query_start", torch.int32)
-    nb, hkv, d = _cache_geometry(k_cache, v_cache)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
     if hkv != int(num_kv_heads):
         raise ValueError("num_kv_heads does not match k_cache")
     T, hq, dq = q.shape
@@ -235,7 +239,7 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
                          "query_start [num_seqs + 1]")
     mb = int(block_tables.shape[1])
     if max_context_len is None:
-        max_context_len = mb * BLOCK_SIZE
+        max_context_len = mb * bs
     if max_query_len is None:
         max_query_len = min(int(T), int(max_context_len))
     if not math.isfinite(float(scale)):
@@ -243,7 +247,39 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
     code = lib().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), context_lens.data_ptr(),
                             query_start.data_ptr(), int(T), float(scale), hkv, S, hq, d,
-                            BLOCK_SIZE, mb,
+                            bs, mb,
                             nb, int(max_context_len), int(max_query_len), _stream(q, stream))
     _check(code, "pa_prefill")
     return out
+
+
+def _dev_or_pinned(t: torch.Tensor, name: str, dtype) -> None:
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor or a pinned host tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
+    """Copy blocks src -> dst between two pools (one of them may be pinned
+    host memory: preemption by swap); block_mapping int64 [P, 2] (src, dst)
+    on the GPU or pinned."""
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        _dev_or_pinned(t, n, torch.float16)
+    _dev_or_pinned(block_mapping, "block_mapping", torch.int64)
+    snb, hkv, d, bs = _cache_geometry(src_k, src_v)
+    dnb, dhkv, dd, dbs = _cache_geometry(dst_k, dst_v)
+    if (hkv, d, bs) != (dhkv, dd, dbs):
+        raise ValueError("source and destination pools differ in heads, head_dim or block size")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    dev_t = next((t for t in (src_k, dst_k) if t.is_cuda), None)
+    if dev_t is None:
+        raise ValueError("one of the pools must be on the GPU")
+    code = lib().pa_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), dst_k.data_ptr(),
+                                dst_v.data_ptr(), block_mapping.data_ptr(),
+                                int(block_mapping.shape[0]), hkv, d, bs, snb, dnb,
+                                _stream(dev_t, stream))
+    _check(code, "pa_swap_blocks")

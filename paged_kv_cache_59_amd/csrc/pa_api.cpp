@@ -10,11 +10,13 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0
+constexpr int kVersion = 500;  // 0.5.0
 constexpr int kMaxGroup = 4;   // query heads per KV head the decode kernel holds
 constexpr int kMaxGridYZ = 65535;
 
 bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
+// block sizes the cache operations take (the attention kernels: see each)
+bool block_size_supported(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -72,7 +74,8 @@ int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_ca
                          hipStream_t stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
-  if (block_size != PA_BLOCK_SIZE || !head_dim_supported(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
+    return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   const int64_t lanes = num_tokens * num_kv_heads * (head_dim / 8);
@@ -82,7 +85,7 @@ int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_ca
   const hipError_t e = pa::launch_reshape_and_cache(
       static_cast<const pa::half_t*>(k), static_cast<const pa::half_t*>(v),
       static_cast<pa::half_t*>(k_cache), static_cast<pa::half_t*>(v_cache), slot_mapping,
-      num_tokens, num_kv_heads, head_dim, num_blocks, stream);
+      num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -91,14 +94,38 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
                    hipStream_t stream) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
-  if (block_size != PA_BLOCK_SIZE || !head_dim_supported(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
+    return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
   if (num_pairs > 0x7fffffff || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  const hipError_t e = pa::launch_copy_blocks(static_cast<pa::half_t*>(k_cache),
-                                              static_cast<pa::half_t*>(v_cache), block_mapping,
-                                              num_pairs, num_kv_heads, head_dim, num_blocks, stream);
+  pa::half_t* k = static_cast<pa::half_t*>(k_cache);
+  pa::half_t* v = static_cast<pa::half_t*>(v_cache);
+  const hipError_t e = pa::launch_copy_blocks(k, v, k, v, block_mapping, num_pairs, num_kv_heads,
+                                              head_dim, block_size, num_blocks, num_blocks, true,
+                                              stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int64_t* block_mapping, int64_t num_pairs, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, hipStream_t stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || src_num_blocks <= 0 ||
+      dst_num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (src_k == dst_k || src_v == dst_v) return PA_ERR_INVALID_ARG;  // one pool: pa_copy_blocks
+  if (num_pairs > 0x7fffffff || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = pa::launch_copy_blocks(
+      static_cast<const pa::half_t*>(src_k), static_cast<const pa::half_t*>(src_v),
+      static_cast<pa::half_t*>(dst_k), static_cast<pa::half_t*>(dst_v), block_mapping, num_pairs,
+      num_kv_heads, head_dim, block_size, src_num_blocks, dst_num_blocks, false, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

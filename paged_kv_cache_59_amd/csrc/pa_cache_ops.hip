@@ -7,7 +7,10 @@
 // coming from the sequence's block table (same page, "PagedAttention: a block
 // table for the KV cache").
 // Copy: a shared block is duplicated whole before a holder appends to it
-// ("KV Cache in Serving Engines ...", section 2 "Sharing Blocks").
+// ("KV Cache in Serving Engines ...", section 2 "Sharing Blocks"); the same
+// kernel moves blocks between the device pool and a host pool for
+// preemption by swap ("Continuous batching and paged attention", "Why they
+// depend on each other").
 //
 // Both are pure data movement (bit copies), bound by HBM bandwidth and far
 // smaller than the attention read; each lane moves 16 bytes per access.
@@ -15,10 +18,11 @@
 
 namespace pa {
 
-// One lane per (token, KV head, 16-byte chunk of the head dimension).
+// One lane per (token, KV head, 16-byte chunk of the head dimension), for a
+// block size BS of 8, 16 or 32 token slots.
 // K: the chunk lands whole at k[b][h][chunk][o][0..7] (16 contiguous bytes).
 // V: its 8 elements land at v[b][h][o/8][d][o%8], one element per 16 bytes.
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const half_t* __restrict__ k, const half_t* __restrict__ v, half_t* __restrict__ k_cache,
     half_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
@@ -32,14 +36,14 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int h = rem / kChunks;
   const int c = rem - h * kChunks;
   const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_blocks * kBlockSize) return;
-  const int64_t b = slot / kBlockSize;
-  const int o = (int)(slot - b * kBlockSize);
+  if (slot < 0 || slot >= num_blocks * BS) return;
+  const int64_t b = slot / BS;
+  const int o = (int)(slot - b * BS);
   const int64_t src = (t * num_kv_heads + h) * D + c * kChunk;
-  const int64_t tile = (b * num_kv_heads + h) * (int64_t)(kBlockSize * D);
+  const int64_t tile = (b * num_kv_heads + h) * (int64_t)(BS * D);
 
   const half8_t kv = *reinterpret_cast<const half8_t*>(k + src);
-  *reinterpret_cast<half8_t*>(k_cache + tile + ((int64_t)c * kBlockSize + o) * kChunk) = kv;
+  *reinterpret_cast<half8_t*>(k_cache + tile + ((int64_t)c * BS + o) * kChunk) = kv;
 
   const half8_t vv = *reinterpret_cast<const half8_t*>(v + src);
   half_t* vdst = v_cache + tile + ((int64_t)(o / kChunk) * D + c * kChunk) * kChunk + (o % kChunk);
@@ -47,51 +51,69 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   for (int e = 0; e < kChunk; ++e) vdst[e * kChunk] = vv[e];
 }
 
-// One workgroup per (pair, KV head, K|V): the (block, head) tile is 16*D
-// contiguous elements in both pools, copied 16 bytes per lane.
-template <int D>
-__global__ __launch_bounds__(256) void copy_blocks_kernel(half_t* __restrict__ k_cache,
-                                                          half_t* __restrict__ v_cache,
-                                                          const int64_t* __restrict__ block_mapping,
-                                                          int num_kv_heads, int64_t num_blocks) {
-  constexpr int kTile = kBlockSize * D;
+// One workgroup per (pair, KV head, K|V): the (block, head) tile is BS*D
+// contiguous elements in both pools, copied 16 bytes per lane, from block
+// src of the source pools to block dst of the destination pools.  Within one
+// pool (copy-on-write) src == dst is a no-op; between two pools (swap) it is
+// an ordinary copy.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    const half_t* __restrict__ src_k, const half_t* __restrict__ src_v, half_t* __restrict__ dst_k,
+    half_t* __restrict__ dst_v, const int64_t* __restrict__ block_mapping, int num_kv_heads,
+    int64_t src_blocks, int64_t dst_blocks, int same_pool) {
+  constexpr int kTile = BS * D;
   const int64_t pair = blockIdx.x;
   const int h = blockIdx.y;
-  half_t* pool = blockIdx.z == 0 ? k_cache : v_cache;
+  const half_t* from = blockIdx.z == 0 ? src_k : src_v;
+  half_t* to = blockIdx.z == 0 ? dst_k : dst_v;
   const int64_t src = block_mapping[2 * pair];
   const int64_t dst = block_mapping[2 * pair + 1];
-  if (src == dst || src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
-  const half_t* s = pool + (src * num_kv_heads + h) * (int64_t)kTile;
-  half_t* d = pool + (dst * num_kv_heads + h) * (int64_t)kTile;
+  if ((same_pool && src == dst) || src < 0 || dst < 0 || src >= src_blocks || dst >= dst_blocks)
+    return;
+  const half_t* s = from + (src * num_kv_heads + h) * (int64_t)kTile;
+  half_t* d = to + (dst * num_kv_heads + h) * (int64_t)kTile;
   for (int i = threadIdx.x; i < kTile / kChunk; i += blockDim.x)
     reinterpret_cast<half8_t*>(d)[i] = reinterpret_cast<const half8_t*>(s)[i];
+}
+
+template <int D, int BS>
+void launch_append_t(const half_t* k, const half_t* v, half_t* k_cache, half_t* v_cache,
+                     const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                     int64_t num_blocks, hipStream_t stream) {
+  const int64_t lanes = num_tokens * num_kv_heads * (D / kChunk);
+  const unsigned grid = (unsigned)((lanes + 255) / 256);
+  hipLaunchKernelGGL((reshape_and_cache_kernel<D, BS>), dim3(grid), dim3(256), 0, stream, k, v,
+                     k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, num_blocks);
 }
 
 hipError_t launch_reshape_and_cache(const half_t* k, const half_t* v, half_t* k_cache,
                                     half_t* v_cache, const int64_t* slot_mapping,
                                     int64_t num_tokens, int num_kv_heads, int head_dim,
-                                    int64_t num_blocks, hipStream_t stream) {
-  const int64_t lanes = num_tokens * num_kv_heads * (head_dim / kChunk);
-  const unsigned grid = (unsigned)((lanes + 255) / 256);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(reshape_and_cache_kernel<128>, dim3(grid), dim3(256), 0, stream, k, v,
-                       k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, num_blocks);
-  else
-    hipLaunchKernelGGL(reshape_and_cache_kernel<64>, dim3(grid), dim3(256), 0, stream, k, v,
-                       k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, num_blocks);
+                                    int block_size, int64_t num_blocks, hipStream_t stream) {
+#define PA_APPEND(D, BS)                                                                     \
+  if (head_dim == D && block_size == BS)                                                     \
+    launch_append_t<D, BS>(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,   \
+                           num_blocks, stream);
+  PA_APPEND(128, 16) PA_APPEND(64, 16) PA_APPEND(128, 8) PA_APPEND(64, 8) PA_APPEND(128, 32)
+  PA_APPEND(64, 32)
+#undef PA_APPEND
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(half_t* k_cache, half_t* v_cache, const int64_t* block_mapping,
-                              int64_t num_pairs, int num_kv_heads, int head_dim,
-                              int64_t num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(const half_t* src_k, const half_t* src_v, half_t* dst_k,
+                              half_t* dst_v, const int64_t* block_mapping, int64_t num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int64_t src_blocks,
+                              int64_t dst_blocks, bool same_pool, hipStream_t stream) {
   const dim3 grid((unsigned)num_pairs, (unsigned)num_kv_heads, 2);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(copy_blocks_kernel<128>, grid, dim3(256), 0, stream, k_cache, v_cache,
-                       block_mapping, num_kv_heads, num_blocks);
-  else
-    hipLaunchKernelGGL(copy_blocks_kernel<64>, grid, dim3(128), 0, stream, k_cache, v_cache,
-                       block_mapping, num_kv_heads, num_blocks);
+  const int threads = block_size * head_dim / kChunk >= 256 ? 256 : block_size * head_dim / kChunk;
+#define PA_COPY(D, BS)                                                                        \
+  if (head_dim == D && block_size == BS)                                                      \
+    hipLaunchKernelGGL((copy_blocks_kernel<D, BS>), grid, dim3(threads), 0, stream, src_k,    \
+                       src_v, dst_k, dst_v, block_mapping, num_kv_heads, src_blocks,          \
+                       dst_blocks, same_pool ? 1 : 0);
+  PA_COPY(128, 16) PA_COPY(64, 16) PA_COPY(128, 8) PA_COPY(64, 8) PA_COPY(128, 32)
+  PA_COPY(64, 32)
+#undef PA_COPY
   return hipGetLastError();
 }
 

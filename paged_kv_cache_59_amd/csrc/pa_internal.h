@@ -78,11 +78,15 @@ DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64
 hipError_t launch_reshape_and_cache(const half_t* k, const half_t* v, half_t* k_cache,
                                     half_t* v_cache, const int64_t* slot_mapping,
                                     int64_t num_tokens, int num_kv_heads, int head_dim,
-                                    int64_t num_blocks, hipStream_t stream);
+                                    int block_size, int64_t num_blocks, hipStream_t stream);
 
-hipError_t launch_copy_blocks(half_t* k_cache, half_t* v_cache, const int64_t* block_mapping,
-                              int64_t num_pairs, int num_kv_heads, int head_dim,
-                              int64_t num_blocks, hipStream_t stream);
+// Whole-block copies from block src of (src_k, src_v) to block dst of
+// (dst_k, dst_v); same_pool: one pool (copy-on-write), where src == dst is a
+// no-op.
+hipError_t launch_copy_blocks(const half_t* src_k, const half_t* src_v, half_t* dst_k,
+                              half_t* dst_v, const int64_t* block_mapping, int64_t num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int64_t src_blocks,
+                              int64_t dst_blocks, bool same_pool, hipStream_t stream);
 
 struct DecodeArgs {
   half_t* out;

@@ -85,7 +85,7 @@ class BlockManager:
         return len(self.free)
 
     def slot(self, seq, pos: int) -> int:
-        """Slot index of logical position ``pos``: physical block * 16 + offset."""
+        """Slot index of logical position ``pos``: physical block * BS + offset."""
         j, off = divmod(int(pos), self.block_size)
         return self.tables[seq][j] * self.block_size + off
 
@@ -172,8 +172,8 @@ class Workload:
     max_blocks_per_seq: int
     scale: np.float32
     q: np.ndarray               # fp16 [S, Hq, D]
-    k_cache: np.ndarray         # fp16 [NB, Hkv, D/8, 16, 8]
-    v_cache: np.ndarray         # fp16 [NB, Hkv, 2, D, 8]
+    k_cache: np.ndarray         # fp16 [NB, Hkv, D/8, BS, 8]
+    v_cache: np.ndarray         # fp16 [NB, Hkv, BS/8, D, 8]
     block_tables: np.ndarray    # int32 [S, MB], -1 past the last block
     context_lens: np.ndarray    # int32 [S], includes the appended token
     k_new: np.ndarray           # fp16 [S, Hkv, D]
@@ -181,10 +181,7 @@ class Workload:
     slot_mapping: np.ndarray    # int64 [S]
     block_mapping: np.ndarray   # int64 [P, 2] (src, dst)
     meta: dict = field(default_factory=dict)
-
-    @property
-    def block_size(self) -> int:
-        return BLOCK_SIZE
+    block_size: int = BLOCK_SIZE
 
     @property
     def max_context_len(self) -> int:
@@ -207,7 +204,7 @@ class Workload:
         lens = self.context_lens.astype(np.int64)
         kv = int(lens.sum()) * self.kv_bytes_per_token_layer()
         qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * 2
-        table = int((-(-lens // BLOCK_SIZE)).sum()) * 4
+        table = int((-(-lens // self.block_size)).sum()) * 4
         return kv + qo + table + 4 * self.num_seqs
 
     def unique_kv_bytes(self) -> int:
@@ -215,9 +212,9 @@ class Workload:
         seen = set()
         for s in range(self.num_seqs):
             n = int(self.context_lens[s])
-            for pos in range(0, n, BLOCK_SIZE):
-                j = pos // BLOCK_SIZE
-                seen.add((int(self.block_tables[s, j]), min(BLOCK_SIZE, n - pos)))
+            for pos in range(0, n, self.block_size):
+                j = pos // self.block_size
+                seen.add((int(self.block_tables[s, j]), min(self.block_size, n - pos)))
         tokens = sum(t for _, t in seen)
         return tokens * self.kv_bytes_per_token_layer()
 
@@ -230,7 +227,7 @@ class Workload:
         """Bytes the copy-on-write moves: read and write whole blocks, K and V."""
         moving = int((self.block_mapping[:, 0] != self.block_mapping[:, 1]).sum()) \
             if self.block_mapping.size else 0
-        return 2 * moving * BLOCK_SIZE * self.kv_bytes_per_token_layer()
+        return 2 * moving * self.block_size * self.kv_bytes_per_token_layer()
 
 
 def _fill_normal_fp16(rng, out: np.ndarray) -> None:
@@ -249,7 +246,8 @@ def _set_slot_bits(k_u16, v_u16, block: int, offset: int, bits) -> None:
 def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=None,
                   len_range=None, num_seqs=None, max_context_bound=None, pool_factor=1.25,
                   num_blocks=None, prefix_groups=0, prefix_len=0, suffix_range=None,
-                  tail="canary", scale=None, placement="shuffled") -> Workload:
+                  tail="canary", scale=None, placement="shuffled",
+                  block_size=BLOCK_SIZE) -> Workload:
     """Build one decode step: pools, tables, lengths, q, new k/v, slots, CoW pairs.
 
     ``context_lens`` (or ``len_range`` + ``num_seqs``) give each sequence's
@@ -265,10 +263,12 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
     assert num_q_heads % num_kv_heads == 0 and head_dim % CHUNK == 0
     rng = np.random.default_rng(seed)
     Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    BS = int(block_size)
+    assert BS % CHUNK == 0
 
     # 1. lengths
     if prefix_groups:
-        assert prefix_len % BLOCK_SIZE == 0 and num_seqs % prefix_groups == 0
+        assert prefix_len % BS == 0 and num_seqs % prefix_groups == 0
         lo, hi = suffix_range
         suffix = rng.integers(lo, hi + 1, size=num_seqs)
         lens = (prefix_len + suffix).astype(np.int64)
@@ -283,22 +283,22 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
     S = lens.size
     if max_context_bound is not None:
         bound = max(bound, max_context_bound)
-    MB = max(1, -(-bound // BLOCK_SIZE))
+    MB = max(1, -(-bound // BS))
 
     # pool size
     if num_blocks is None:
         if prefix_groups:
-            shared = prefix_groups * (prefix_len // BLOCK_SIZE)
-            private = int(sum(-(-int(n) // BLOCK_SIZE) - prefix_len // BLOCK_SIZE for n in lens))
+            shared = prefix_groups * (prefix_len // BS)
+            private = int(sum(-(-int(n) // BS) - prefix_len // BS for n in lens))
             needed = shared + private + S            # + one copy-on-write spare each
         else:
-            needed = int(sum(-(-int(n) // BLOCK_SIZE) for n in lens))
+            needed = int(sum(-(-int(n) // BS) for n in lens))
         num_blocks = max(1, math.ceil(pool_factor * needed))
     NB = int(num_blocks)
 
     # 2. placement (the permutation is drawn in both modes, to keep the stream)
     perm = rng.permutation(NB)
-    bm = BlockManager(NB, free_order=perm if placement == "shuffled" else None)
+    bm = BlockManager(NB, free_order=perm if placement == "shuffled" else None, block_size=BS)
     slots = np.full(S, -1, dtype=np.int64)
     cows = []
     shadows = []
@@ -333,8 +333,8 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
     tables = bm.table_array(range(S), MB)
 
     # 3. pools
-    k_cache = np.empty((NB, Hkv, D // CHUNK, BLOCK_SIZE, CHUNK), dtype=np.float16)
-    v_cache = np.empty((NB, Hkv, BLOCK_SIZE // CHUNK, D, CHUNK), dtype=np.float16)
+    k_cache = np.empty((NB, Hkv, D // CHUNK, BS, CHUNK), dtype=np.float16)
+    v_cache = np.empty((NB, Hkv, BS // CHUNK, D, CHUNK), dtype=np.float16)
     _fill_normal_fp16(rng, k_cache)
     _fill_normal_fp16(rng, v_cache)
     # 4. queries and the appended tokens
@@ -364,10 +364,10 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
         if n == 0:
             continue
         pos = n - 1                       # the append position
-        j, off = divmod(pos, BLOCK_SIZE)
+        j, off = divmod(pos, BS)
         # the block that holds the append position before any copy
         blk = pre_tables[s][j] if j < len(pre_tables[s]) else bm.tables[s][j]
-        for o in range(off, BLOCK_SIZE):
+        for o in range(off, BS):
             if tail == "stale" and o > off:
                 continue
             _set_slot_bits(ku, vu, blk, o, _CANARIES[o % 3] if o > off else FP16_NAN)
@@ -382,6 +382,7 @@ def make_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=
         slot_mapping=slots, block_mapping=np.asarray(cows, dtype=np.int64).reshape(-1, 2),
         meta={"tail": tail, "prefix_groups": prefix_groups, "prefix_len": prefix_len,
               "pool_factor": pool_factor, "placement": placement},
+        block_size=BS,
     )
 
 
@@ -436,8 +437,8 @@ class PrefillWorkload:
     max_blocks_per_seq: int
     scale: np.float32
     q: np.ndarray               # fp16 [T, Hq, D], chunks packed in sequence order
-    k_cache: np.ndarray         # fp16 [NB, Hkv, D/8, 16, 8]
-    v_cache: np.ndarray         # fp16 [NB, Hkv, 2, D, 8]
+    k_cache: np.ndarray         # fp16 [NB, Hkv, D/8, BS, 8]
+    v_cache: np.ndarray         # fp16 [NB, Hkv, BS/8, D, 8]
     block_tables: np.ndarray    # int32 [S, MB]
     context_lens: np.ndarray    # int32 [S], including the chunk
     query_start: np.ndarray     # int32 [S + 1]
@@ -445,6 +446,7 @@ class PrefillWorkload:
     v_new: np.ndarray           # fp16 [T, Hkv, D]
     slot_mapping: np.ndarray    # int64 [T]
     meta: dict = field(default_factory=dict)
+    block_size: int = BLOCK_SIZE
 
     @property
     def num_tokens(self) -> int:
@@ -464,7 +466,7 @@ class PrefillWorkload:
 
 def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=None,
                           chunk_lens=None, num_seqs=None, cached_range=None, chunk=None,
-                          pool_factor=1.25, scale=None) -> PrefillWorkload:
+                          pool_factor=1.25, scale=None, block_size=BLOCK_SIZE) -> PrefillWorkload:
     """Chunks of ``chunk_lens`` query tokens ending contexts of ``context_lens``
     (or: ``num_seqs`` sequences with ``rng.integers`` cached lengths in
     ``cached_range`` plus a fixed ``chunk``).  Draws, in order: cached lengths
@@ -473,6 +475,7 @@ def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, conte
     are NaN; slots past the context in its last block hold canaries."""
     rng = np.random.default_rng(seed)
     Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    BS = int(block_size)
     if context_lens is None:
         lo, hi = cached_range
         cached = rng.integers(lo, hi + 1, size=num_seqs).astype(np.int64)
@@ -483,11 +486,11 @@ def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, conte
         nqs = np.asarray(chunk_lens, dtype=np.int64)
     assert (nqs >= 0).all() and (nqs <= lens).all()
     S = lens.size
-    MB = max(1, -(-int(lens.max()) // BLOCK_SIZE))
-    needed = int(sum(-(-int(n) // BLOCK_SIZE) for n in lens))
+    MB = max(1, -(-int(lens.max()) // BS))
+    needed = int(sum(-(-int(n) // BS) for n in lens))
     NB = max(1, math.ceil(pool_factor * needed))
     perm = rng.permutation(NB)
-    bm = BlockManager(NB, free_order=perm)
+    bm = BlockManager(NB, free_order=perm, block_size=BS)
     slots = []
     for s in range(S):
         bm.allocate(s, int(lens[s] - nqs[s]))
@@ -497,8 +500,8 @@ def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, conte
             slots.append(slot)
     tables = bm.table_array(range(S), MB)
     T = int(nqs.sum())
-    k_cache = np.empty((NB, Hkv, D // CHUNK, BLOCK_SIZE, CHUNK), dtype=np.float16)
-    v_cache = np.empty((NB, Hkv, BLOCK_SIZE // CHUNK, D, CHUNK), dtype=np.float16)
+    k_cache = np.empty((NB, Hkv, D // CHUNK, BS, CHUNK), dtype=np.float16)
+    v_cache = np.empty((NB, Hkv, BS // CHUNK, D, CHUNK), dtype=np.float16)
     _fill_normal_fp16(rng, k_cache)
     _fill_normal_fp16(rng, v_cache)
     q = np.empty((T, Hq, D), dtype=np.float16)
@@ -514,12 +517,12 @@ def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, conte
     ku[~referenced] = FP16_NAN
     vu[~referenced] = FP16_NAN
     for slot in slots:
-        _set_slot_bits(ku, vu, slot // BLOCK_SIZE, slot % BLOCK_SIZE, FP16_NAN)
+        _set_slot_bits(ku, vu, slot // BS, slot % BS, FP16_NAN)
     for s in range(S):
         n = int(lens[s])
-        if n % BLOCK_SIZE:
-            blk = bm.tables[s][n // BLOCK_SIZE]
-            for o in range(n % BLOCK_SIZE, BLOCK_SIZE):
+        if n % BS:
+            blk = bm.tables[s][n // BS]
+            for o in range(n % BS, BS):
                 _set_slot_bits(ku, vu, blk, o, _CANARIES[o % 3])
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -530,7 +533,7 @@ def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, conte
         context_lens=lens.astype(np.int32),
         query_start=np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32),
         k_new=k_new, v_new=v_new, slot_mapping=np.asarray(slots, dtype=np.int64),
-        meta={"pool_factor": pool_factor})
+        meta={"pool_factor": pool_factor}, block_size=BS)
 
 
 PREFILL_WORKLOADS = {

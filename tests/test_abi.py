@@ -115,7 +115,7 @@ def test_cache_op_argument_errors(L):
     E = binding
     r = L.pa_reshape_and_cache
     assert r(1, 1, 1, 1, 1, 4, 8, 96, 16, 10, NULL) == E.PA_ERR_UNSUPPORTED
-    assert r(1, 1, 1, 1, 1, 4, 8, 128, 8, 10, NULL) == E.PA_ERR_UNSUPPORTED
+    assert r(1, 1, 1, 1, 1, 4, 8, 128, 24, 10, NULL) == E.PA_ERR_UNSUPPORTED   # block size
     assert r(1, 1, 1, 1, 1, -1, 8, 128, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
     assert r(NULL, 1, 1, 1, 1, 4, 8, 128, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
     assert r(NULL, NULL, NULL, NULL, NULL, 0, 8, 128, 16, 10, NULL) == E.PA_OK
@@ -124,6 +124,13 @@ def test_cache_op_argument_errors(L):
     assert c(1, 1, 1, 2, 8, 80, 16, 10, NULL) == E.PA_ERR_UNSUPPORTED
     assert c(1, NULL, 1, 2, 8, 64, 16, 10, NULL) == E.PA_ERR_INVALID_ARG
     assert c(NULL, NULL, NULL, 0, 8, 64, 16, 10, NULL) == E.PA_OK
+    assert c(1, 1, 1, 2, 8, 64, 4, 10, NULL) == E.PA_ERR_UNSUPPORTED
+    w = L.pa_swap_blocks
+    assert w(1, 2, 3, 4, 5, 2, 8, 64, 12, 10, 10, NULL) == E.PA_ERR_UNSUPPORTED   # block size
+    assert w(1, 2, 3, 4, 5, 2, 8, 64, 16, 0, 10, NULL) == E.PA_ERR_INVALID_ARG
+    assert w(1, 2, 1, 4, 5, 2, 8, 64, 16, 10, 10, NULL) == E.PA_ERR_INVALID_ARG   # one pool
+    assert w(1, 2, 3, 4, NULL, 2, 8, 64, 16, 10, 10, NULL) == E.PA_ERR_INVALID_ARG
+    assert w(NULL, NULL, NULL, NULL, NULL, 0, 8, 64, 32, 10, 10, NULL) == E.PA_OK
 
 
 def test_binding_refuses_cpu_tensors():
