@@ -72,7 +72,7 @@ enum {
   PA_ERR_HIP = -4,         /* a HIP call or kernel launch failed              */
 };
 
-#define PA_BLOCK_SIZE 16
+#define PA_BLOCK_SIZE 16 /* the default block size; 8 and 32 are also accepted */
 
 /*
  * Append: write each new token's K and V rows into its slot ([AQ] "TL;DR",
@@ -156,18 +156,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *   out[s][h] = softmax_i( scale * q[s][h] . K_s[kh][i] ) V_s[kh][i],
  *               i = 0 .. context_lens[s]-1,
  *
- * where position i of sequence s is slot offset i%16 of physical block
- * block_tables[s][i/16].  The unused tail of the last block never enters the
+ * where position i of sequence s is slot offset i%BS of physical block
+ * block_tables[s][i/BS] (BS = block_size: 8, 16 or 32).  The unused tail of the last block never enters the
  * result, whatever it holds (NaN included).  A length of 0 gives a zero row.
  *
  *   out               fp16 [num_seqs][num_q_heads][head_dim]
  *   q                 fp16 [num_seqs][num_q_heads][head_dim]
  *   block_tables      int32 [num_seqs][max_blocks_per_seq] (row stride
- *                     max_blocks_per_seq); entries past ceil(len/16) unread
+ *                     max_blocks_per_seq); entries past ceil(len/BS) unread
  *   context_lens      int32 [num_seqs]; values are clamped to [0, max_context_len]
  *   scale             softmax scale (e.g. 1/sqrt(head_dim)), finite
  *   max_context_len   host-known upper bound of context_lens, at most
- *                     max_blocks_per_seq*16
+ *                     max_blocks_per_seq*BS
  *   num_workers       0 = automatic (pa_decode_num_workers()); else the number
  *                     of persistent wavefronts that share the work.  Every
  *                     (sequence, KV head) is cut into 64-token units that
@@ -238,7 +238,7 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  *                     clamped to [0, max_context_len])
  *   max_query_len     host-known upper bound of every chunk length, at most
  *                     max_context_len; 0 = nothing to do
- * Any G = num_q_heads / num_kv_heads is accepted.  A chunk longer than its
+ * block_size 8, 16 or 32.  Any G = num_q_heads / num_kv_heads is accepted.  A chunk longer than its
  * context or than max_query_len, or reaching past num_tokens, is a broken
  * precondition: its rows are left unwritten (nothing outside q and out is
  * touched).  Accumulation is fp32; softmax weights enter the value product

@@ -151,9 +151,10 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || !std::isfinite(scale))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (block_size != PA_BLOCK_SIZE || !head_dim_supported(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
+    return PA_ERR_UNSUPPORTED;
   if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_INVALID_ARG;
   if (num_workers < 0 || num_workers > pa::kMaxWorkers) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
@@ -179,6 +180,7 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
@@ -224,8 +226,9 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
       !std::isfinite(scale))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (block_size != PA_BLOCK_SIZE || !head_dim_supported(head_dim)) return PA_ERR_UNSUPPORTED;
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE ||
+  if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
       max_query_len > max_context_len)
     return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || max_query_len == 0 || num_tokens == 0) return PA_OK;
@@ -253,6 +256,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;

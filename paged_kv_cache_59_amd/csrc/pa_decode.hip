@@ -167,12 +167,15 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 
 }  // namespace
 
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
   constexpr int kF = D / 16;           // floats per lane of one partial in a merge
-  constexpr int64_t kTile = (int64_t)kBlockSize * D;
+  constexpr int64_t kTile = (int64_t)BS * D;
+  constexpr int NBU = kGroupTokens / BS;  // blocks per 64-token unit (8, 4 or 2)
+  constexpr int kGroups = BS / kChunk;    // 8-token V groups per block
+  static_assert(NBU * BS == kGroupTokens && kGroups * kChunk == BS, "block size 8, 16 or 32");
   static_assert(kChunks * kChunk == D && kSets * 64 == D, "head_dim must be 64 or 128");
 
   // [S] head units (per KV head) before sequence s, [S] its length, then the
@@ -495,48 +498,52 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     return c;
   };
 
-  const int my_blk = lane >> 4;  // which of a unit's 4 blocks holds this lane's token
+  const int my_blk = lane / BS;  // which of a unit's blocks holds this lane's token
   const int g_lane = lane & 3;   // q head of the group this lane's MFMA row carries
   const int64_t block_stride = (int64_t)Hkv * kTile;
 
-  // Table entries of unit c's 4 blocks: one vector load, lane i & 3 reads
-  // entry 4g + (i & 3).  Blocks past the sequence's last re-read its last
+  // Table entries of unit c's NBU blocks: one vector load, lane i reads
+  // entry NBU g + i % NBU.  Blocks past the sequence's last re-read its last
   // block, so every unit issues the same loads; positions past the end are
   // removed later by position.
   auto load_table = [&](const Cursor& c) {
     const int32_t* row = a.block_tables + (int64_t)c.s * a.max_blocks_per_seq;
-    const int last = (c.len + kBlockSize - 1) / kBlockSize - 1;
-    return row[min(4 * c.g + (lane & 3), last)];
+    const int last = (c.len + BS - 1) / BS - 1;
+    return row[min(NBU * c.g + (lane % NBU), last)];
   };
-  // The 4 physical ids (uniform) from such a load; an id outside the pool (a
-  // broken table) reads pool block 0 instead.
-  auto blocks_of = [&](int tbl, int (&pb)[4]) {
+  // The NBU physical ids (uniform) from such a load; an id outside the pool
+  // (a broken table) reads pool block 0 instead.
+  auto blocks_of = [&](int tbl, int (&pb)[NBU]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NBU; ++i) {
       const int e = __builtin_amdgcn_readlane(tbl, i);
       pb[i] = (e >= 0 && e < a.num_blocks) ? e : 0;
     }
   };
 
   half8_t kreg[kChunks];
-  half8_t vreg[4][kSets][2];
+  half8_t vreg[8][kSets];  // 8-token group g of the unit, 64-dim range st
   half8_t qreg;  // lane g*kChunks + c: 16-byte chunk c of q row g of a run
-  auto load_k = [&](const Cursor& c, const int (&pb)[4]) {
-    const int phys = my_blk == 0 ? pb[0] : my_blk == 1 ? pb[1] : my_blk == 2 ? pb[2] : pb[3];
+  // K of unit c: lane l's token lies in the unit's block l / BS, whose table
+  // entry lane l / BS of the table load tbl holds (a cross-lane read, not a
+  // register-indexed select, which the compiler would turn into scratch)
+  auto load_k = [&](const Cursor& c, int tbl) {
+    const int e = __shfl(tbl, my_blk);
+    const int phys = (e >= 0 && e < a.num_blocks) ? e : 0;
     const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
-                       (lane & 15) * kChunk;
+                       (lane % BS) * kChunk;
 #pragma unroll
-    for (int cc = 0; cc < kChunks; ++cc) kreg[cc] = load_nt(kp + cc * (kBlockSize * kChunk));
+    for (int cc = 0; cc < kChunks; ++cc) kreg[cc] = load_nt(kp + cc * (BS * kChunk));
   };
-  auto load_v = [&](const Cursor& c, const int (&pb)[4]) {
+  // V group g (tokens 8g..8g+7 of the unit) is group g % kGroups of the
+  // unit's block g / kGroups: for a fixed 64-dim range one 1 KiB load
+  auto load_v = [&](const Cursor& c, const int (&pb)[NBU]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const half_t* vp = a.v_cache + (int64_t)pb[i] * block_stride + (int64_t)c.h * kTile;
+    for (int g = 0; g < 8; ++g) {
+      const half_t* vp = a.v_cache + (int64_t)pb[g / kGroups] * block_stride +
+                         (int64_t)c.h * kTile + (int64_t)(g % kGroups) * D * kChunk;
 #pragma unroll
-      for (int st = 0; st < kSets; ++st)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          vreg[i][st][hh] = load_nt(vp + ((int64_t)hh * D + st * 64 + lane) * kChunk);
+      for (int st = 0; st < kSets; ++st) vreg[g][st] = load_nt(vp + (st * 64 + lane) * kChunk);
     }
   };
   // q rows of c's run; every lane loads (rows past G and lanes past the rows
@@ -808,7 +815,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   }
   Cursor nxt = next(cur);
   Cursor nxt2 = next(nxt);
-  int pb_cur[4], pb_nxt[4];
+  int pb_cur[NBU], pb_nxt[NBU];
   const int tbl_cur = load_table(cur);
   int tbl_nxt = load_table(nxt);
   load_q(cur);
@@ -816,7 +823,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   // keep the prologue in loop order (all K loads, then all V loads): the
   // wait counts at the loop head are merged over both ways in
   __builtin_amdgcn_sched_barrier(0);
-  load_k(cur, pb_cur);
+  load_k(cur, tbl_cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, pb_cur);
   __builtin_amdgcn_sched_barrier(0);
@@ -848,7 +855,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     // table entries two units ahead, then the next unit's K and q
     const int tbl_nxt2 = load_table(nxt2);
     blocks_of(tbl_nxt, pb_nxt);
-    load_k(nxt, pb_nxt);
+    load_k(nxt, tbl_nxt);
     load_q(nxt);
     // the unit after nxt2, computed while this unit's V is in flight (finding
     // a newly claimed chunk takes a few LDS round trips)
@@ -880,16 +887,13 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     // it) in the sequence's last unit: V element := 0
     if (t0 + kGroupTokens > cur.len) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int g = 0; g < 8; ++g)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int e = 0; e < kChunk; ++e) {
+          const bool dead = t0 + g * kChunk + e >= cur.len;
 #pragma unroll
-          for (int e = 0; e < kChunk; ++e) {
-            const bool dead = t0 + i * kBlockSize + hh * kChunk + e >= cur.len;
-#pragma unroll
-            for (int st = 0; st < kSets; ++st)
-              vreg[i][st][hh][e] = dead ? (half_t)0.0f : vreg[i][st][hh][e];
-          }
+          for (int st = 0; st < kSets; ++st) vreg[g][st][e] = dead ? (half_t)0.0f : vreg[g][st][e];
+        }
     }
 
     __builtin_amdgcn_wave_barrier();
@@ -900,10 +904,10 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     // out[g][d] += sum_t P[g][t] V[t][d]; chunk c = tokens 4c..4c+3 of the unit
     static_for<0, 16>([&](auto ic) {
       constexpr int c = decltype(ic)::value;
-      constexpr int i = c / 4, hh = (c % 4) / 2, sub = c % 2;
+      constexpr int g = c / 2, sub = c % 2;  // 8-token group, its half
 #pragma unroll
       for (int st = 0; st < kSets; ++st) {
-        const half4_t vf = sub ? hi4(vreg[i][st][hh]) : lo4(vreg[i][st][hh]);
+        const half4_t vf = sub ? hi4(vreg[g][st]) : lo4(vreg[g][st]);
         acc_o[st] = __builtin_amdgcn_mfma_f32_4x4x4f16(pfrag, vf, acc_o[st], 4, c, 0);
       }
     });
@@ -1001,22 +1005,23 @@ DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64
   return w;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
-                         hipEvent_t stop) {
+template <int D, int BS>
+void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
   const uint32_t lds = (uint32_t)(((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int));
-  if (!start && !stop) {
-    if (a.head_dim == 128)
-      hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, a);
-    else
-      hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, a);
-  } else {
-    // the events take the kernel's own start and end times
-    if (a.head_dim == 128)
-      hipExtLaunchKernelGGL(decode_kernel<128>, grid, dim3(192), lds, stream, start, stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(decode_kernel<64>, grid, dim3(192), lds, stream, start, stop, 0, a);
-  }
+  if (!start && !stop)
+    hipLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(192), lds, stream, a);
+  else  // the events take the kernel's own start and end times
+    hipExtLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(192), lds, stream, start, stop, 0, a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop) {
+#define PA_DECODE(D, BS) \
+  if (a.head_dim == D && a.block_size == BS) launch_decode_t<D, BS>(a, stream, start, stop);
+  PA_DECODE(128, 16) PA_DECODE(64, 16) PA_DECODE(128, 8) PA_DECODE(64, 8) PA_DECODE(128, 32)
+  PA_DECODE(64, 32)
+#undef PA_DECODE
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBlockSize = 16;    // token slots per block
+constexpr int kBlockSize = 16;    // token slots per block (the default; 8 and 32 also built)
 constexpr int kChunk = 8;         // fp16 elements per 16-byte chunk
 constexpr int kGroupTokens = 64;  // tokens one wave handles per step of its loop (a "unit")
 constexpr int kWorkersPerCU = 2;  // decode waves per compute unit
@@ -97,6 +97,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
   int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int block_size;  // 8, 16 or 32
   int max_blocks_per_seq;
   int64_t num_blocks;
   int max_context_len;
@@ -125,6 +126,7 @@ struct PrefillArgs {
   float scale_log2;  // |softmax scale| times log2(e), at least 1e-30
   int negate_q;      // the scale is negative: q enters with its sign flipped
   int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int block_size;    // 8, 16 or 32
   int max_blocks_per_seq;
   int64_t num_blocks;
   int max_context_len, max_query_len;

@@ -63,11 +63,13 @@ __device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c)
 
 }  // namespace
 
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 32;             // 32-dim steps of the contraction over D
   constexpr int DT = D / 16;             // 16-dim tiles of the output
-  constexpr int64_t kTile = (int64_t)kBlockSize * D;
+  constexpr int64_t kTile = (int64_t)BS * D;
+  constexpr int NBS = 32 / BS;           // blocks per 32-key step (4, 2 or 1)
+  static_assert(NBS * BS == 32, "block size 8, 16 or 32");
   constexpr float kStale = 8.0f;         // see the rescale below
   constexpr float kFloor = -1.0e30f;     // initial reference max (log2 units)
 
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   }
 
   const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int last_blk = (len + kBlockSize - 1) / kBlockSize - 1;
+  const int last_blk = (len + BS - 1) / BS - 1;
   const int64_t hoff = (int64_t)h * kTile;
   const int64_t bstride = (int64_t)a.num_kv_heads * kTile;
   // physical block of logical block lb (clamped to the sequence's last): a
@@ -142,19 +144,39 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // key of this lane's K rows in S^T sub-tile kt: 8 (c16 / 4) + 4 kt + c16 % 4
   const int kq = 8 * (c16 >> 2) + (c16 & 3);
   half8_t kf[2][KS], vf[DT];
-  // K and V of a step held in blocks p0 (keys 0..15) and p1 (keys 16..31)
-  auto load_k = [&](int64_t p0, int64_t p1) {
+  // The NBS blocks of a step (keys i BS .. i BS + BS - 1 in block i), as
+  // separate values: a lane picks its own with selects (an indexed array
+  // would be placed in scratch memory).
+  struct StepBlocks {
+    int64_t p0, p1, p2, p3;
+  };
+  auto step_blocks = [&](int st) {
+    StepBlocks b{phys_of(NBS * st), 0, 0, 0};
+    if (NBS > 1) b.p1 = phys_of(NBS * st + 1);
+    if (NBS > 2) {
+      b.p2 = phys_of(NBS * st + 2);
+      b.p3 = phys_of(NBS * st + 3);
+    }
+    return b;
+  };
+  auto pick = [&](const StepBlocks& b, int i) -> int64_t {
+    if constexpr (NBS == 1) return b.p0;
+    else if constexpr (NBS == 2) return i == 0 ? b.p0 : b.p1;
+    else return i < 2 ? (i == 0 ? b.p0 : b.p1) : (i == 2 ? b.p2 : b.p3);
+  };
+  auto load_k = [&](const StepBlocks& b) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kq + 4 * kt;  // < 32
-      const half_t* kp = a.k_cache + (key < 16 ? p0 : p1) * bstride + hoff + (key & 15) * 8;
+      const half_t* kp = a.k_cache + pick(b, key / BS) * bstride + hoff + (key % BS) * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * 16 * 8);
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * BS * 8);
     }
   };
-  auto load_v = [&](int64_t p0, int64_t p1) {
-    // V^T operand: keys 8j..8j+7 = block j / 2, 8-token group j % 2
-    const half_t* vp = a.v_cache + (j < 2 ? p0 : p1) * bstride + hoff + (int64_t)(j & 1) * D * 8;
+  auto load_v = [&](const StepBlocks& b) {
+    // V^T operand: keys 8j..8j+7 = block 8j / BS, 8-token group (8j % BS) / 8
+    const half_t* vp = a.v_cache + pick(b, (8 * j) / BS) * bstride + hoff +
+                       (int64_t)((8 * j % BS) / 8) * D * 8;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
   };
@@ -174,16 +196,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // kf, its V once step st's value product is done with vf; the loads then
   // fly under the softmax and the other product.
   {
-    const int64_t p0 = phys_of(0), p1 = phys_of(1);
-    load_k(p0, p1);
-    load_v(p0, p1);
+    const StepBlocks b0 = step_blocks(0);
+    load_k(b0);
+    load_v(b0);
   }
   for (int st = 0; st < nsteps; ++st) {
     // every step issues the same loads (the last one re-reads its own blocks,
     // which hit L2), so the hardware wait counts stay exact across the loop;
     // the next step's table entries load under this step's logits
     const int nxt = min(st + 1, nsteps - 1);
-    const int64_t pn0 = phys_of(2 * nxt), pn1 = phys_of(2 * nxt + 1);
+    const StepBlocks bn = step_blocks(nxt);
     // logits of both row sub-tiles, then the next step's K
     float4v sacc[2][2];
 #pragma unroll
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           sacc[rt][kt] = mfma16x16x32(kf[kt][ks], qf[rt][ks], sacc[rt][kt]);
       }
-    load_k(pn0, pn1);
+    load_k(bn);
 
     // positions past the context (the last block's tail: any bits, NaN
     // included, and re-read blocks past it) get V := 0 by selection; their
@@ -262,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vf[dt], pf[rt], o[rt][dt]);
-    load_v(pn0, pn1);
+    load_v(bn);
   }
 
   // out[row][dims 16 dt + 4 j .. +3] = O^T / l
@@ -287,10 +309,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t padded = (pairs + 7) / 8 * 8 * a.tile_groups;  // 8 XCDs x pairs/8 x tile groups
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)padded), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)padded), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)padded);
+#define PA_PREFILL(D, BS)                     \
+  if (a.head_dim == D && a.block_size == BS) \
+    hipLaunchKernelGGL((prefill_kernel<D, BS>), grid, dim3(256), 0, stream, a);
+  PA_PREFILL(128, 16) PA_PREFILL(64, 16) PA_PREFILL(128, 8) PA_PREFILL(64, 8) PA_PREFILL(128, 32)
+  PA_PREFILL(64, 32)
+#undef PA_PREFILL
   return hipGetLastError();
 }
 

@@ -52,15 +52,17 @@ def gpu_step(w, d, num_workers=0):
 
 
 def oracle_pools(w):
-    kc, vc = oracle.copy_blocks(w.k_cache, w.v_cache, w.block_mapping, w.num_kv_heads, w.head_dim)
-    return oracle.reshape_and_cache(w.k_new, w.v_new, kc, vc, w.slot_mapping)
+    kc, vc = oracle.copy_blocks(w.k_cache, w.v_cache, w.block_mapping, w.num_kv_heads, w.head_dim,
+                                block_size=w.block_size)
+    return oracle.reshape_and_cache(w.k_new, w.v_new, kc, vc, w.slot_mapping,
+                                    block_size=w.block_size)
 
 
 def oracle_decode(w, kc, vc, seqs=None, scale=None):
     idx = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs)
     sc = w.scale if scale is None else scale
     return oracle.decode(w.q[idx], kc, vc, w.block_tables[idx], w.context_lens[idx], sc,
-                         w.num_kv_heads)
+                         w.num_kv_heads, block_size=w.block_size)
 
 
 def compare(gpu, ref, label=""):

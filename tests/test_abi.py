@@ -76,7 +76,7 @@ def test_decode_argument_errors(L):
     E = binding
     assert dec(L, hq=30) == E.PA_ERR_INVALID_ARG            # Hq % Hkv != 0
     assert dec(L, D=96) == E.PA_ERR_UNSUPPORTED
-    assert dec(L, bs=32) == E.PA_ERR_UNSUPPORTED
+    assert dec(L, bs=24) == E.PA_ERR_UNSUPPORTED             # block size not 8, 16 or 32
     assert dec(L, hq=64) == E.PA_ERR_UNSUPPORTED             # G = 8
     assert dec(L, maxctx=129) == E.PA_ERR_INVALID_ARG        # > 8 blocks * 16
     assert dec(L, S=-1) == E.PA_ERR_INVALID_ARG

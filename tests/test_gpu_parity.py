@@ -313,3 +313,22 @@ def test_timed_decode_matches_and_times_the_kernel(num_seqs):
     kc, vc = oracle_pools(w)
     seqs = np.r_[0:9] if num_seqs < 100 else np.r_[0:20, num_seqs - 20:num_seqs]
     compare(timed[seqs], oracle_decode(w, kc, vc, seqs), "timed decode")
+
+
+@pytest.mark.parametrize("BS", [8, 32])
+@pytest.mark.parametrize("Hq,Hkv,D,workers", [(32, 8, 128, 0), (8, 8, 64, 37), (4, 4, 128, 1),
+                                              (16, 4, 64, 5000)])
+def test_decode_block_sizes(BS, Hq, Hkv, D, workers):
+    """Block sizes 8 and 32: a 64-token unit spans 8 blocks, or 2; lengths
+    ending inside and at block and unit edges; shared prefixes with copies."""
+    w = wl.make_workload("bs", 900 + BS + Hq + D, Hq, Hkv, D, context_lens=EDGE_LENS + [33, 40],
+                         block_size=BS)
+    run_case(w, workers, f"decode BS{BS} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
+
+
+@pytest.mark.parametrize("BS", [8, 32])
+def test_decode_block_sizes_dynamic_tails_and_prefix(monkeypatch, BS):
+    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", "8")
+    w = wl.make_workload("bsp", 950 + BS, 32, 8, 128, num_seqs=12, prefix_groups=3,
+                         prefix_len=128, suffix_range=(1, 300), block_size=BS)
+    run_case(w, 0, f"decode BS{BS} prefix + dynamic tails")

@@ -41,7 +41,8 @@ def gpu_prefill_step(w, d, max_query_len=None):
 
 
 def oracle_pools_prefill(w):
-    return oracle.reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_mapping)
+    return oracle.reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_mapping,
+                                    block_size=w.block_size)
 
 
 def oracle_rows(w, kc, vc, rows):
@@ -54,7 +55,7 @@ def oracle_rows(w, kc, vc, rows):
         p = n - (t1 - t0) + (t - t0)
         out[k] = oracle.prefill(w.q[t:t + 1], kc, vc, w.block_tables[s:s + 1],
                                 np.array([p + 1], np.int32), np.array([0, 1], np.int32),
-                                w.scale, w.num_kv_heads)[0]
+                                w.scale, w.num_kv_heads, block_size=w.block_size)[0]
     return out
 
 
@@ -67,7 +68,7 @@ def run_full_parity(w, label):
     assert np.array_equal(d["k_cache"].cpu().numpy().view(np.uint16), kc.view(np.uint16))
     assert np.array_equal(d["v_cache"].cpu().numpy().view(np.uint16), vc.view(np.uint16))
     ref = oracle.prefill(w.q, kc, vc, w.block_tables, w.context_lens, w.query_start, w.scale,
-                         w.num_kv_heads)
+                         w.num_kv_heads, block_size=w.block_size)
     compare(out, ref, label)
     return out
 
@@ -168,7 +169,7 @@ def test_prefill_rows_past_max_query_len_untouched_and_errors():
             int(w.num_blocks), w.max_context_len, w.max_query_len, None]
     assert L.pa_prefill(*args) == 0
     bad = list(args)
-    bad[13] = 32                                        # block size
+    bad[13] = 24                                        # block size not 8, 16 or 32
     assert L.pa_prefill(*bad) == -2
     bad = list(args)
     bad[17] = w.max_context_len + 1                     # chunk bound above the context bound
@@ -220,3 +221,15 @@ def test_prefill_negative_and_zero_scale(scale):
         for i in (0, 1, 69):
             mean = v[:, :i + 1].mean(axis=1)              # [Hkv, D]
             assert np.abs(out[i].astype(np.float64) - np.repeat(mean, 4, axis=0)).max() < 2e-3
+
+
+@pytest.mark.parametrize("BS", [8, 32])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 64), (16, 2, 64)])
+def test_prefill_block_sizes(BS, Hq, Hkv, D):
+    """Block sizes 8 and 32: a 32-key step spans 4 blocks, or one; contexts
+    and chunks ending inside and at block edges."""
+    lens = [1, 8, 9, 31, 32, 33, 100, 257, 64]
+    nqs = [1, 8, 3, 31, 1, 17, 64, 100, 0]
+    w = wl.make_prefill_workload("pbs", 800 + BS + Hq + D, Hq, Hkv, D, context_lens=lens,
+                                 chunk_lens=nqs, block_size=BS)
+    run_full_parity(w, f"prefill BS{BS} Hq{Hq} Hkv{Hkv} D{D}")
