@@ -157,8 +157,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *               i = 0 .. context_lens[s]-1,
  *
  * where position i of sequence s is slot offset i%BS of physical block
- * block_tables[s][i/BS] (BS = block_size: 8, 16 or 32).  The unused tail of the last block never enters the
- * result, whatever it holds (NaN included).  A length of 0 gives a zero row.
+ * block_tables[s][i/BS] (BS = block_size: 8, 16 or 32).  The unused tail of
+ * the last block never enters the result, whatever it holds (NaN included).
+ * A length of 0 gives a zero row.
  *
  *   out               fp16 [num_seqs][num_q_heads][head_dim]
  *   q                 fp16 [num_seqs][num_q_heads][head_dim]
