@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32])
+    ap.add_argument("--swap-blocks", type=int, default=0,
+                    help="only measure swapping this many blocks (Llama-3.1-8B layer shape) "
+                         "out to pinned host memory and back in")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run `steps` plain device copies of this many MiB (an elementwise "
                          "kernel reading and writing known bytes, to calibrate HBM counters)")
@@ -147,7 +151,7 @@ def bench_prefill(args):
 
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
-    w = wl.make_named_prefill(args.workload)
+    w = wl.make_named_prefill(args.workload, block_size=args.block_size)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, tab, lens, qs = t(w.q), t(w.block_tables), t(w.context_lens), t(w.query_start)
     k_new, v_new, slots = t(w.k_new), t(w.v_new), t(w.slot_mapping)
@@ -192,7 +196,7 @@ def bench_prefill(args):
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_tokens": w.num_tokens,
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "block_size": 16, "max_context_len": w.max_context_len,
+            "head_dim": w.head_dim, "block_size": w.block_size, "max_context_len": w.max_context_len,
             "max_query_len": w.max_query_len, "seed": w.seed, "accumulate": "f32",
             "flops": flops,
         },
@@ -213,6 +217,68 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args):
+    """Preemption by swap: copy N blocks of the Llama-3.1-8B layer shape (8 KV
+    heads, head dim 128) from the device pool to pinned host memory and back,
+    one pa_swap_blocks call per direction, timed with HIP events.  Bound by
+    the host link."""
+    import torch
+    from paged_kv_cache_59_amd import binding as pk
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    bs, hkv, d, n = args.block_size, 8, 128, args.swap_blocks
+    nb = 2 * n
+    rng = np.random.default_rng(7)
+    kd = torch.from_numpy(rng.standard_normal((nb, hkv, d // 8, bs, 8), dtype=np.float32)
+                          .astype(np.float16)).cuda()
+    vd = torch.from_numpy(rng.standard_normal((nb, hkv, bs // 8, d, 8), dtype=np.float32)
+                          .astype(np.float16)).cuda()
+    hk = torch.empty((n, hkv, d // 8, bs, 8), dtype=torch.float16).pin_memory()
+    hv = torch.empty((n, hkv, bs // 8, d, 8), dtype=torch.float16).pin_memory()
+    src = torch.from_numpy(rng.permutation(nb)[:n].astype(np.int64))
+    out_map = torch.stack([src, torch.arange(n)], 1).contiguous().cuda()
+    in_map = torch.stack([torch.arange(n), torch.from_numpy(rng.permutation(nb)[:n].astype(np.int64))],
+                         1).contiguous().cuda()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pk.pa_swap_blocks(kd, vd, hk, hv, out_map)
+        pk.pa_swap_blocks(hk, hv, kd, vd, in_map)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_out, t_in = [], []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        pk.pa_swap_blocks(kd, vd, hk, hv, out_map)
+        ev[1].record(stream)
+        pk.pa_swap_blocks(hk, hv, kd, vd, in_map)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_out.append(ev[0].elapsed_time(ev[1]))
+        t_in.append(ev[1].elapsed_time(ev[2]))
+    wall = time.perf_counter() - t0
+    nbytes = n * 2 * hkv * d * bs * 2
+    out_gbs = nbytes / (np.mean(t_out) * 1e-3) / 1e9
+    in_gbs = nbytes / (np.mean(t_in) * 1e-3) / 1e9
+    res = {"metric": "block swap over the host link: GB/s per direction", "unit": "GB/s",
+           "value": round(2 * nbytes * args.steps / wall / 1e9, 2), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": f"swap_llama_{n}", "blocks": n, "block_size": bs,
+                      "num_kv_heads": hkv, "head_dim": d, "bytes_per_direction": nbytes},
+           "roofline": {"bound": "host link", "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                        "swap_out": round(out_gbs, 2), "swap_in": round(in_gbs, 2),
+                        "frac_out": round(out_gbs / HOST_LINK_PEAK_GBS, 4),
+                        "frac_in": round(in_gbs / HOST_LINK_PEAK_GBS, 4),
+                        "out_ms": round(float(np.mean(t_out)), 4),
+                        "in_ms": round(float(np.mean(t_in)), 4)},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -221,6 +287,9 @@ def main():
         sys.exit(2)
     if args.copy_probe_mb:
         copy_probe(args)
+        return
+    if args.swap_blocks:
+        bench_swap(args)
         return
     from paged_kv_cache_59_amd import workloads as wl_names
     if args.workload in wl_names.PREFILL_WORKLOADS:
@@ -232,7 +301,7 @@ def main():
 
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
-    w = wl.make_named(args.workload, placement=args.placement)
+    w = wl.make_named(args.workload, placement=args.placement, block_size=args.block_size)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, tab, lens = t(w.q), t(w.block_tables), t(w.context_lens)
     k_new, v_new, slots = t(w.k_new), t(w.v_new), t(w.slot_mapping)
@@ -315,7 +384,7 @@ def main():
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
-            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
             "max_context_len": w.max_context_len, "mean_context_len": float(w.context_lens.mean()),
             "seed": w.seed, "num_workers": workers, "replicas": R, "accumulate": "f32",
             "copies_per_step": int(w.block_mapping.shape[0]), "placement": args.placement,
@@ -323,7 +392,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name) if w.block_size == 16 else None,
             "kernel": "decode_kernel",
             "mean_us": round(dec_mean_s * 1e6, 3),
             "median_us": round(float(np.median(dec_ms)) * 1e3, 3),
