@@ -130,8 +130,8 @@ int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_
 /*
  * Number of decode workers pa_decode uses when it is passed num_workers == 0:
  * 2 per compute unit of the current HIP device.  A worker is one workgroup of
- * three 64-lane wavefronts: one streams K and V, one writes and merges the
- * partial results of cut sequences, one claims dynamic work.
+ * two 64-lane wavefronts: one streams K and V, one writes and merges the
+ * partial results of cut sequences.
  * Returns a negative PA_ERR_* code if the device cannot be queried.
  */
 int32_t pa_decode_num_workers(void);
@@ -139,10 +139,11 @@ int32_t pa_decode_num_workers(void);
 /*
  * Workspace bytes pa_decode needs for these sizes; max_context_len and
  * num_workers as for pa_decode (0 workers = automatic, on the current
- * device).  Returns 0 for invalid sizes.  The workspace holds one arrival
- * counter per (sequence, KV head), the claim counters of the dynamic work
- * and the partial results of sequences cut between workers.  Batches above
- * 4096 sequences need no more than 4096 do (they run as several launches).
+ * device).  Returns 0 for invalid sizes.  The workspace holds, from its
+ * start, the partial results of sequences cut between workers and, against
+ * its end, one arrival counter per (sequence, KV head).
+ * Batches above 4096 sequences need no more than 4096 do (they run as
+ * several launches).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t num_workers);
@@ -170,22 +171,19 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *   max_context_len   host-known upper bound of context_lens, at most
  *                     max_blocks_per_seq*BS
  *   num_workers       0 = automatic (pa_decode_num_workers()); else the number
- *                     of persistent wavefronts that share the work.  Every
- *                     (sequence, KV head) is cut into 64-token units that
- *                     go into equal contiguous shares, one per worker.  With
- *                     the environment variable PA_DECODE_STATIC_SIXTEENTHS
- *                     = F (0..15), only the first F/16 of each run is
- *                     shared out; the rest is cut into small chunks (1, 1,
- *                     2, 4, 8.. units from the run's end) that workers claim
- *                     as they finish, largest first.  A sequence cut into
- *                     several pieces is merged by the last piece to finish
- *                     (log-sum-exp rescaling).
+ *                     of persistent workgroups that share the work.  Every
+ *                     (sequence, KV head) is cut into 64-token units; all
+ *                     units, end to end, go into equal contiguous shares,
+ *                     one per worker.  A sequence cut into several pieces
+ *                     is merged by the last piece to finish (log-sum-exp
+ *                     rescaling).
  *   workspace         device buffer of at least pa_decode_workspace_size(
  *                     num_seqs, num_kv_heads, head_dim, max_context_len,
  *                     num_workers) bytes, 256-byte aligned, ZERO-FILLED before
  *                     its first use; each call leaves its counters at zero
- *                     again, so a workspace is reusable without clearing.  Two
- *                     calls that overlap in time must not share one workspace.
+ *                     again, so a workspace is reusable without clearing,
+ *                     also by calls of smaller shapes.  Two calls
+ *                     that overlap in time must not share one workspace.
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.

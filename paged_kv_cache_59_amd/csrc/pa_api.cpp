@@ -4,7 +4,6 @@
 #include "pa.h"
 
 #include <cmath>
-#include <cstdlib>
 
 #include "pa_internal.h"
 
@@ -34,15 +33,6 @@ int32_t auto_workers() {
   const int32_t w = ((cus * pa::kWorkersPerCU + 7) / 8) * 8;
   if (dev >= 0 && dev < 64) cache[dev] = w;
   return w;
-}
-
-// Static share of each run, in sixteenths: the default, or the value of
-// PA_DECODE_STATIC_SIXTEENTHS (clamped to 0..16) when it is set.
-int static_sixteenths() {
-  const char* e = std::getenv("PA_DECODE_STATIC_SIXTEENTHS");
-  if (!e || !*e) return pa::kStaticSixteenths;
-  const int v = std::atoi(e);
-  return v < 0 ? 0 : v > 16 ? 16 : v;
 }
 
 // Workers to use, or a negative PA code.
@@ -137,7 +127,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   const int32_t w = resolve_workers(num_workers);
   if (w <= 0) return 0;
   const int64_t s = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
-  return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, max_context_len, w);
+  return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, w);
 }
 
 int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -168,12 +158,13 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
   const size_t need =
-      pa::decode_workspace_bytes(per_launch, num_kv_heads, head_dim, max_context_len, w);
+      pa::decode_workspace_bytes(per_launch, num_kv_heads, head_dim, w);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
-  a.ws = pa::decode_workspace_carve(workspace, per_launch, num_kv_heads, max_context_len, w);
+  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, per_launch, num_kv_heads, head_dim,
+                                    w);
   a.k_cache = static_cast<const pa::half_t*>(k_cache);
   a.v_cache = static_cast<const pa::half_t*>(v_cache);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
@@ -185,7 +176,6 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_workers = w;
-  a.static_sixteenths = static_sixteenths();
   (void)hipGetLastError();
   // launches on one stream run in order, so they share the workspace
   for (int64_t s0 = 0; s0 < num_seqs; s0 += per_launch) {

@@ -11,27 +11,25 @@
 //
 // Design (the pages give none; decode reads every K/V byte once, so HBM
 // bandwidth bounds it):
-//  * Units and segments.  Each (sequence, KV head) pair is a run of 64-token
+//  * Units and shares.  Each (sequence, KV head) pair is a run of 64-token
 //    units (4 blocks each); all runs are laid end to end in (sequence, head)
-//    order.  A fixed grid of persistent workers (one wave each) shares them:
-//    the first part of the units is cut into one static segment per worker,
-//    the rest into small dynamic segments that workers claim from counters
-//    (one pool per XCD group) when they near the end of their current segment.  Workers that stream
-//    faster (HBM channels, XCD placement) thus take more of the tail, and all
-//    finish within about one segment of each other.  Each worker finds units
-//    through a prefix sum of the lengths it keeps in LDS; the host never
-//    reads the lengths.
-//  * A run cut between segments is merged by the last of its pieces to
+//    order and cut into one equal contiguous share per worker of a fixed grid
+//    of persistent workers.  Each worker finds its units through a prefix
+//    sum of the lengths it keeps in LDS; the host never reads the lengths.
+//    (Shares balanced at run time, by claimed chunks or by taking units from
+//    slower workers' shares, were measured slower on MI355X: the claims'
+//    lookahead, the extra cut pieces and their merges at the kernel's end
+//    cost more than the per-XCD speed spread they remove.)
+//  * A run cut between shares is merged by the last of its pieces to
 //    arrive: each piece writes (max, sum, unnormalised output) through to
-//    memory, bumps the run's counter two loop iterations later (by then the
-//    stores have completed: vector memory operations of a wave complete in
-//    issue order and the wave has waited on younger loads), and the piece
-//    that completes the count merges with the log-sum-exp rescale and resets
-//    the counter.  Merges therefore happen inside the stream, not after it.
-//    One launch per decode.
-//  * Consecutive static segments run on one XCD (workgroups are handed to
-//    the 8 XCDs in turn), so neighbouring runs, e.g. sequences sharing prefix
-//    blocks, meet in the same L2.
+//    memory and adds its units to the run's counter; the piece that
+//    completes the count merges with the log-sum-exp rescale and resets the
+//    counter.  A piece that finds every other unit of its run already
+//    counted merges at once, without counting.  Merges therefore happen
+//    inside the stream, not after it.  One launch per decode.
+//  * Consecutive shares run on one XCD (workgroups are handed to the 8 XCDs
+//    in turn), so neighbouring runs, e.g. sequences sharing prefix blocks,
+//    meet in the same L2.
 //  * The grouped query heads of one KV head (G <= 4) are the 4 rows of the
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
@@ -144,18 +142,15 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // outstanding memory operation, draining the streamer's K/V pipeline.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-__device__ __forceinline__ int wave_max_int(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
-}
-
 // Loads and stores of the partial results, coherent across XCDs: stores write
 // through to memory, loads bypass the caches (system scope, sc0 sc1).
 __device__ __forceinline__ void store_through(float* p, float x) {
   __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ float load_through(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ int load_through_i(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 // 16 bytes at byte offset `off` of the buffer starting at `base` (uniform).
@@ -168,7 +163,7 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 }  // namespace
 
 template <int D, int BS>
-__global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
   constexpr int kF = D / 16;           // floats per lane of one partial in a merge
@@ -178,8 +173,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   static_assert(NBU * BS == kGroupTokens && kGroups * kChunk == BS, "block size 8, 16 or 32");
   static_assert(kChunks * kChunk == D && kSets * 64 == D, "head_dim must be 64 or 128");
 
-  // [S] head units (per KV head) before sequence s, [S] its length, then the
-  // dynamic classes' first chunks
+  // [S] units (per KV head) of the sequences before s, [S] its length
   extern __shared__ int seq_lds[];
   // Rows padded so that the 4 rows of one access fall in different LDS banks
   // (unpadded, rows 128 and 256 bytes apart share banks: 4-way conflicts).
@@ -190,16 +184,12 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   // streamer -> merger: cut pieces, a ring of kRing entries
   __shared__ float ring_o[kRing][4 * D];
   __shared__ float ring_ml[kRing][8];
-  __shared__ int ring_meta[kRing][4];  // sequence, KV head, partial slot
-  // claimer -> streamer: claimed chunks (nd = none left) with their first unit
-  // already located: chunk, sequence, KV head, unit, end unit
-  __shared__ int claim_q[kClaimDepth][8];
-  __shared__ int ctl[8];  // ring produced/consumed, claims produced/consumed, streamer done
+  __shared__ int ring_meta[kRing][4];  // sequence, KV head, partial slot, units
+  __shared__ int ctl[4];  // ring produced/consumed, streamer done
 
-  // Wave 0 streams the units.  Every operation whose latency would stall a
-  // wave's in-order memory queue is taken by a helper wave: wave 1 writes cut
-  // pieces through, counts their arrivals and merges; wave 2 claims dynamic
-  // chunks when the streamer asks and locates them.
+  // Wave 0 streams the units.  Wave 1 takes every operation whose latency
+  // would stall the streamer's in-order memory queue: it writes cut pieces
+  // through, counts their arrivals and merges.
   const int role = threadIdx.x >> 6;
   const bool streamer = role == 0;
   const int lane = threadIdx.x & 63;
@@ -213,29 +203,21 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   const int G = Hq / Hkv;
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
-  int* const cls_lds = seq_lds + 2 * S;
 
   auto units_for = [](int c) { return (c + kGroupTokens - 1) / kGroupTokens; };
-  const int F = a.static_sixteenths;
-  auto tail_of = [&](int n) { return n - ((n * F) >> 4); };  // dynamic units of a run of n
 
   // ---- lengths into LDS; zero the rows of empty sequences ----------------
-  // off_lds[s]: head units (per KV head) of the sequences before s
-  int carry = 0, total_n = 0, b_max = 0;  // uniform
+  int carry = 0;  // uniform
   for (int c0 = 0; c0 < S; c0 += 64) {
     const int s = c0 + lane;
     const int c = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
     const int n = units_for(c);
-    const int b = tail_of(n);
-    const int hd = n - b;
-    const int incl = wave_inclusive_scan(hd, lane);
+    const int incl = wave_inclusive_scan(n, lane);
     if (streamer && s < S) {
-      off_lds[s] = carry + incl - hd;
+      off_lds[s] = carry + incl - n;
       len_lds[s] = c;
     }
     carry += __builtin_amdgcn_readlane(incl, 63);
-    total_n += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
-    b_max = max(b_max, uniform(wave_max_int(b)));
     uint64_t empty = streamer ? __ballot(s < S && n == 0 && (s % nw) == w) : 0;
     while (empty) {
       const int se = c0 + __builtin_ctzll(empty);
@@ -244,72 +226,28 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
       for (int e = lane; e < Hq * D; e += 64) o[e] = (half_t)0.0f;
     }
   }
-  const int U = total_n * Hkv;  // all units (the host bounds this below 2^31)
+  const int U = carry * Hkv;  // all units (the host bounds this below 2^31)
   if (U == 0) return;
-  const int P = min(nw, U);  // active workers: one static share each
+  const int P = min(nw, U);  // active workers: one share each
   if (w >= P) return;
-  const int U1 = carry * Hkv;  // static units (the runs' heads)
-
-  // ---- dynamic chunks of the tails -------------------------------------------
-  // Class c of a tail of b units is the chunk [b - E(c+1), b - E(c)) counted
-  // from the tail's start, E(c) = 0, 1, 2, 4, 8, 8+M, 8+2M, ... (sizes 1, 1,
-  // 2, 4, M, M, ...; the first chunk of the tail may be shorter).  Claim order
-  // is class-major, largest class first, (sequence, head) within a class.
-  const int M = b_max > 8 ? max(8, (b_max - 8 + kMaxClasses - 5) / (kMaxClasses - 4)) : 8;
-  const int ncls = tail_chunks(b_max, M);  // classes present
-  auto E = [&](int c) { return c <= 2 ? c : c == 3 ? 4 : 8 + M * (c - 4); };
-  // cls_lds[c]: first dynamic chunk of class c (classes start in decreasing
-  // c, so class ncls-1 starts at 0); cls_lds[ncls]: all dynamic chunks.
-  // Built from a histogram of the sequences' last classes.
-  if (streamer) {
-    for (int c = lane; c <= ncls; c += 64) cls_lds[c] = 0;
-    if (lane < 8) ctl[lane] = 0;
-  }
-  __syncthreads();
-  for (int c0 = 0; c0 < S; c0 += 64) {
-    const int s = c0 + lane;
-    if (streamer && s < S) {
-      const int nc = tail_chunks(tail_of(units_for(len_lds[s])), M);
-      if (nc > 0) atomicAdd(&cls_lds[nc - 1], 1);
-    }
-  }
-  __syncthreads();
-  // in order k = ncls-1-c: sequences having class c = an inclusive scan of
-  // the histogram; class starts = an exclusive scan of those counts times Hkv
-  if (streamer) {
-    int have_carry = 0, start_carry = 0;
-    for (int k0 = 0; k0 < ncls; k0 += 64) {
-      const int k = k0 + lane, c = ncls - 1 - k;
-      const int hist = k < ncls ? cls_lds[c] : 0;
-      const int have = have_carry + wave_inclusive_scan(hist, lane);
-      const int size = k < ncls ? have * Hkv : 0;
-      const int incl = wave_inclusive_scan(size, lane);
-      if (k < ncls) cls_lds[c] = start_carry + incl - size;
-      have_carry = __builtin_amdgcn_readlane(have, 63);
-      start_carry += __builtin_amdgcn_readlane(incl, 63);
-    }
-    if (lane == 0) cls_lds[ncls] = start_carry;
-  }
+  if (streamer && lane < 4) ctl[lane] = 0;
   __syncthreads();  // the LDS tables are complete
-  const int nd = uniform(cls_lds[ncls]);
-  const bool dyn = nd > 0;
-  auto cls_start = [&](int c) { return uniform(cls_lds[c]); };
 
-  // ---- static shares -----------------------------------------------------------
-  // share j < Q: head units [j*U1/Q, (j+1)*U1/Q) in (sequence, head, unit)
-  // order; Q <= P so that no share is empty (workers Q.. start by claiming)
-  const int Q = min(P, U1);
-  const bool narrow = (int64_t)U1 * Q < ((int64_t)1 << 31);  // 32-bit share arithmetic suffices
-  auto share_begin = [&](int j) -> int {
-    return narrow ? (int)((unsigned)(j * U1) / (unsigned)Q) : (int)((int64_t)j * U1 / Q);
+  // ---- shares ------------------------------------------------------------------
+  // share j: units [sb(j), sb(j+1)), sb(j) = floor(j U / P), in (sequence,
+  // head, unit) order
+  const bool narrow = (int64_t)U * P < ((int64_t)1 << 31);  // 32-bit share arithmetic suffices
+  auto sb = [&](int j) -> int {
+    return narrow ? (int)((unsigned)(j * U) / (unsigned)P) : (int)((int64_t)j * U / P);
   };
-  auto share_of = [&](int u) -> int {  // the share holding head unit u
-    return narrow ? (int)((unsigned)((u + 1) * Q - 1) / (unsigned)U1)
-                  : (int)(((int64_t)(u + 1) * Q - 1) / U1);
+  auto share_of = [&](int u) -> int {  // the share holding unit u
+    return narrow ? (int)((unsigned)((u + 1) * P - 1) / (unsigned)U)
+                  : (int)(((int64_t)(u + 1) * P - 1) / U);
   };
-  const int R = S * Hkv;  // runs; slots [0, R) hold the first piece of each run's head
+  // Partial slots: [0, R) the piece that starts run r, R + j the piece that
+  // starts share j inside a run.
+  const int R = S * Hkv;
 
-  // ---- sequences by prefix sums and by class membership ------------------------
   // the sequence holding head index `key`: the last s with off[s] <= key (a
   // 64-ary search over the LDS prefix sums)
   auto find_head = [&](int key) {
@@ -325,40 +263,12 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     }
     return uniform(lo);
   };
-  auto tail_of_seq = [&](int s) { return tail_of(units_for(len_lds[s])); };  // per lane
-  // sequences before s whose tail exceeds e units (they have class c with E(c) = e)
-  auto rank_tail = [&](int s, int e) {
-    int r = 0;
-    for (int c0 = 0; c0 < s; c0 += 64) {
-      const int t = c0 + lane;
-      r += __popcll(__ballot(t < s && tail_of_seq(min(t, S - 1)) > e));
-    }
-    return uniform(r);
-  };
-  // the i-th sequence (from 0) whose tail exceeds e units
-  auto select_tail = [&](int i, int e) {
-    for (int c0 = 0; c0 < S; c0 += 64) {
-      const int t = c0 + lane;
-      const bool q = t < S && tail_of_seq(min(t, S - 1)) > e;
-      const uint64_t m = __ballot(q);
-      const int cnt = __popcll(m);
-      if (i < cnt) {
-        const uint64_t hit = __ballot(q && __popcll(m & ((1ull << lane) - 1)) == i);
-        return uniform(c0 + __builtin_ctzll(hit));
-      }
-      i -= cnt;
-    }
-    return S - 1;  // unreachable for i < class size
-  };
 
   // ---- cursors over units --------------------------------------------------
   struct Cursor {
     int s, h, g;   // sequence, KV head, unit of the run
-    int glim;      // end (exclusive) of the current stretch of this run in the segment
     int n_s, len;  // units and length of s
-    int seg;       // segment: static share (< Q) or P + dynamic chunk
-    int left;      // units of the segment from this one on
-    int seglen;    // units of the segment
+    int left;      // units of the worker's share from this one on
     bool valid;    // false past the worker's last unit (then a copy of it)
   };
   auto set_seq = [&](Cursor& c, int s) {
@@ -366,48 +276,20 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     c.len = uniform(len_lds[s]);
     c.n_s = units_for(c.len);
   };
-  // head unit u of share j
-  auto locate_share = [&](int u, int j) {
+  auto locate = [&](int u) {
     Cursor c;
     set_seq(c, find_head(u / Hkv));
-    const int hd = c.n_s - tail_of(c.n_s);
     const int r = u - Hkv * uniform(off_lds[c.s]);
-    c.h = r / hd;
-    c.g = r - c.h * hd;
-    c.glim = hd;
-    c.seg = j;
-    c.left = share_begin(j + 1) - u;
-    c.seglen = c.left;
+    c.h = r / c.n_s;
+    c.g = r - c.h * c.n_s;
+    c.left = 1;
     c.valid = true;
     return c;
   };
-  // the first unit of dynamic chunk d
-  auto locate_chunk = [&](int d) {
-    // its class: the smallest c whose start is <= d (starts fall with c)
-    int cl = 0;
-    for (int c0 = 0; c0 < ncls; c0 += 64) {
-      const int c = c0 + lane;
-      cl += __popcll(__ballot(c < ncls && cls_lds[c] > d));
-    }
-    cl = uniform(cl);
-    const int j = d - cls_start(cl);
-    Cursor c;
-    set_seq(c, select_tail(j / Hkv, E(cl)));
-    c.h = j - (j / Hkv) * Hkv;
-    const int b = tail_of(c.n_s), hd = c.n_s - b;
-    c.g = hd + max(0, b - E(cl + 1));
-    c.glim = hd + b - E(cl);
-    c.seg = P + d;
-    c.left = c.glim - c.g;
-    c.seglen = c.left;
-    c.valid = true;
-    return c;
-  };
-  // the unit after c inside its segment: the next unit of the run, else the
-  // head of the next run (shares only: a chunk lies inside one run)
+  // the next unit in (sequence, head, unit) order
   auto step = [&](Cursor c) {
     --c.left;
-    if (c.g + 1 < c.glim) {
+    if (c.g + 1 < c.n_s) {
       ++c.g;
       return c;
     }
@@ -420,26 +302,11 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
       do {
         s = min(s + 1, S - 1);
         set_seq(c, s);
-      } while (c.n_s - tail_of(c.n_s) == 0 && s + 1 < S);
+      } while (c.n_s == 0 && s + 1 < S);
     }
-    c.glim = c.n_s - tail_of(c.n_s);
     return c;
   };
 
-  // Dynamic claims.  Same-address atomics serialise in the memory system, so
-  // the dynamic chunks form NPOOL pools with counters of their own: pool x
-  // holds the chunks d with d % NPOOL == x.  Worker w's home pool is
-  // w * NPOOL / P (for a full grid, its XCD); it claims there until a claim
-  // fails, then from the next pool until a claim fails.  Every pool is thus
-  // visited by its home workers and its left neighbour's, each failing on it
-  // exactly once, so a pool sees n_x + F_x claims in all; the one that draws
-  // value n_x + F_x - 1 is the last and resets the counter for the next call.
-  const int npool = min(kClaimPools, P);
-  auto pool_first = [&](int x) { return (x * P + npool - 1) / npool; };  // first worker of pool x
-  auto pool_homes = [&](int x) { return pool_first(x + 1) - pool_first(x); };
-  const int home = (int)(((int64_t)w * npool) / P);
-  const int stages = npool > 1 ? 2 : 1;
-  auto pool_of = [&](int st) { return st == 0 ? home : (home + 1) % npool; };
   auto lds_ld = [](const int* p) {
     lds_order();
     const int v = *p;
@@ -451,49 +318,9 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     if (lane == 0) *p = v;
     lds_order();
   };
-  // (streamer) claims are made by the claimer wave on request, as late as the
-  // lookahead allows, so that they follow the streamer's actual progress
-  int cq_cons = 0, requested = 0;
-  auto request_claims = [&](int outstanding) {
-    if (requested - cq_cons < outstanding) {
-      requested = cq_cons + outstanding;
-      lds_st(&ctl[kCtlClaimsWanted], requested);
-    }
-  };
-  // (streamer) the next claimed chunk from the claimer's queue, already
-  // located; an invalid cursor when none is left
-  auto take_claim = [&]() -> Cursor {
-    request_claims(1);
-    Cursor c{};
-    c.valid = false;
-    for (int spin = 0; lds_ld(&ctl[kCtlClaimsMade]) == cq_cons; ++spin) {
-      if (spin == kSpinLimit) return c;  // never reached: the claimer answers every request
-      __builtin_amdgcn_s_sleep(1);
-    }
-    const int* e = claim_q[cq_cons % kClaimDepth];
-    lds_order();
-    const int d = uniform(e[0]);
-    c.s = uniform(e[1]);
-    c.h = uniform(e[2]);
-    c.g = uniform(e[3]);
-    c.glim = uniform(e[4]);
-    c.len = uniform(e[5]);
-    lds_order();
-    lds_st(&ctl[kCtlClaimsTaken], ++cq_cons);
-    c.n_s = units_for(c.len);
-    c.seg = P + d;
-    c.left = c.glim - c.g;
-    c.seglen = c.left;
-    c.valid = d < nd;
-    return c;
-  };
   auto next = [&](Cursor c) -> Cursor {
     if (!c.valid) return c;
     if (c.left > 1) return step(c);
-    if (dyn) {
-      const Cursor n = take_claim();
-      if (n.valid) return n;
-    }
     c.valid = false;
     return c;
   };
@@ -562,63 +389,34 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
   };
 
   // ---- merge of a cut run ----------------------------------------------------
-  // The run r = (s, kvh) has np parts: first its head's pieces in shares
-  // wa..wb (piece 0 starts the head: slot r; piece p > 0 starts share wa+p:
-  // slot R + wa + p), then its tail's chunks of classes 0 .. nc-1 (chunk d in
-  // slot R + P + d).
-  struct Parts {
-    int s, kvh, n_sh, wa, nc, b;
-  };
-  auto run_parts = [&](int s, int kvh) {
-    Parts r;
-    r.s = s;
-    r.kvh = kvh;
+  // Run r = (s, kvh) holds units [u0, u0 + n); its pieces are its overlaps
+  // with the shares v it meets: slot r for the one that starts the run, slot
+  // R + v for a piece that starts share v.  Lane 16*gq + pq handles head gq:
+  // for a batch of up to 16 pieces it loads (max, sum) of piece pq and output
+  // dims pq*kF .. +kF of head gq of every piece (one round trip); batches
+  // combine with the running-max rescale.  Writes the output rows, then
+  // clears the run's counter for the next call.
+  auto merge = [&](int s, int kvh) {
     const int n = units_for(uniform(len_lds[s]));
-    r.b = tail_of(n);
-    const int hd = n - r.b;
-    r.nc = tail_chunks(r.b, M);
-    r.n_sh = 0;
-    r.wa = 0;
-    if (hd > 0) {
-      const int ua = Hkv * uniform(off_lds[s]) + kvh * hd;  // the head's first unit
-      r.wa = share_of(ua);
-      r.n_sh = share_of(ua + hd - 1) - r.wa + 1;
-    }
-    return r;
-  };
-  auto slot_of = [&](const Parts& r, int p) -> int64_t {
-    if (p < r.n_sh) return p == 0 ? (int64_t)r.s * Hkv + r.kvh : (int64_t)R + r.wa + p;
-    const int c = p - r.n_sh;
-    return (int64_t)R + P + cls_start(c) + Hkv * rank_tail(r.s, E(c)) + r.kvh;
-  };
-  // Lane 16*gq + pq handles head gq: it loads (max, sum) of part p0 + pq and,
-  // for every part of the batch, output dims pq*kF .. +kF of head gq.  The
-  // parts of a batch load together (one round trip); batches combine with the
-  // running-max rescale.  Writes the output rows and resets the counter.
-  auto merge = [&](auto batch, int s, int kvh) {
-    constexpr int B = decltype(batch)::value;
-    const Parts r = run_parts(s, kvh);
-    const int np = r.n_sh + r.nc;
+    const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
+    const int r = s * Hkv + kvh;
     const int gq = lane >> 4, pq = lane & 15;
     float acc[kF];
 #pragma unroll
     for (int j = 0; j < kF; ++j) acc[j] = 0.0f;
     float mx = -INFINITY, lsum = 0.0f;
-    for (int p0 = 0; p0 < np; p0 += B) {
-      const int nb = min(B, np - p0);
-      const bool valid = pq < nb && gq < G;
-      // slot of part p0 + pq in lane pq of every row (parts past the batch
-      // repeat its last); the slot arithmetic runs on uniform values
-      int sl = 0;
-      for (int qi = 0; qi < nb; ++qi) {
-        const int sq = (int)slot_of(r, p0 + qi);
-        if (pq == qi || (qi == nb - 1 && pq > qi)) sl = sq;
-      }
+    const int va = share_of(u0), np_all = share_of(u0 + n - 1) - va + 1;
+    for (int p0 = 0; p0 < np_all; p0 += 16) {
+      const int np = min(16, np_all - p0);
+      const bool valid = pq < np && gq < G;
+      // piece p0 + pq (pieces past the batch repeat its last)
+      const int v = va + p0 + min(pq, np - 1);
+      const int sl = v == va ? r : R + v;
       const float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
       const float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
-      float ov[B][kF];
+      float ov[16][kF];
 #pragma unroll
-      for (int qi = 0; qi < B; ++qi) {
+      for (int qi = 0; qi < 16; ++qi) {
         const float* base = a.ws.o + (int64_t)__builtin_amdgcn_readlane(sl, qi) * 4 * D;
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
@@ -635,8 +433,8 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < kF; ++j) acc[j] *= alpha;
 #pragma unroll
-      for (int qi = 0; qi < B; ++qi) {
-        const float wq = __shfl(wt, (lane & 48) | qi);  // 0 for qi >= nb
+      for (int qi = 0; qi < 16; ++qi) {
+        const float wq = __shfl(wt, (lane & 48) | qi);  // 0 for pieces past the batch
 #pragma unroll
         for (int j = 0; j < kF; ++j) acc[j] += wq * ov[qi][j];
       }
@@ -648,8 +446,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
       for (int j = 0; j < kF; ++j) o[j] = (half_t)(acc[j] * inv);
     }
     if (lane == 0)  // ready for the next call
-      __hip_atomic_store(a.ws.counters + (int64_t)s * Hkv + kvh, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ws.counters + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // per-piece softmax state
@@ -665,71 +462,14 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
 
-  // ---- the claimer wave -------------------------------------------------------
-  if (role == 2) {
-    // Claims.  Same-address atomics serialise in the memory system, so the
-    // dynamic chunks form NPOOL pools with counters of their own (pool x:
-    // chunks d with d % NPOOL == x).  This worker's home pool is w*NPOOL/P
-    // (for a full grid, its XCD); it claims there until a claim fails, then
-    // from the next pool until a claim fails.  Every pool is thus visited by
-    // its home workers and its left neighbour's, each failing on it exactly
-    // once, so pool x sees n_x + F_x claims in all; the one that draws value
-    // n_x + F_x - 1 is the last and resets the counter for the next call.
-    int stage = 0, made = 0;
-    bool claiming = dyn;
-    for (int idle = 0; claiming && idle < kSpinLimit;) {
-      if (made >= lds_ld(&ctl[kCtlClaimsWanted])) {
-        if (lds_ld(&ctl[kCtlDone])) break;
-        __builtin_amdgcn_s_sleep(1);
-        ++idle;
-        continue;
-      }
-      idle = 0;
-      int d = nd;
-      while (stage < stages) {
-        const int x = pool_of(stage);
-        int t = 0;
-        if (lane == 0)
-          t = __hip_atomic_fetch_add(a.ws.claims + x * kClaimStride, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        const int v = __builtin_amdgcn_readlane(t, 0);
-        const int n_x = x < nd ? (nd - x + npool - 1) / npool : 0;
-        const int f_x = pool_homes(x) + (npool > 1 ? pool_homes((x + npool - 1) % npool) : 0);
-        if (v == n_x + f_x - 1 && lane == 0)
-          __hip_atomic_store(a.ws.claims + x * kClaimStride, 0, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        if (v >= 0 && v < n_x) {
-          d = v * npool + x;
-          break;
-        }
-        ++stage;
-      }
-      claiming = d < nd;
-      int* e = claim_q[made % kClaimDepth];
-      if (d < nd) {
-        const Cursor c = locate_chunk(d);
-        lds_order();
-        if (lane == 0) {
-          e[1] = c.s;
-          e[2] = c.h;
-          e[3] = c.g;
-          e[4] = c.glim;
-          e[5] = c.len;
-        }
-      }
-      lds_st(&e[0], d);
-      lds_st(&ctl[kCtlClaimsMade], ++made);
-    }
-    return;
-  }
-
   // ---- the merger wave --------------------------------------------------------
   if (!streamer) {
     // The merger works in rounds: take every finished piece from the ring (up
-    // to kRing); write them through to their slots; wait once; count all
-    // their arrivals at once (one lane each); wait once; merge the runs whose
-    // last piece it holds.  Two memory round trips per round, however many
-    // pieces.
+    // to kRing); read their runs' counters and write the pieces through to
+    // their slots; wait once.  A piece whose run already has every other
+    // unit in is the last: it merges at once, without being counted.  The
+    // others count their arrivals (one lane each, by units); wait once; the
+    // piece that completes its run's count merges.
     int cons = 0;
     for (int idle = 0; idle < kSpinLimit;) {
       const int avail = min(lds_ld(&ctl[kCtlRingMade]) - cons, kRing);
@@ -742,8 +482,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
         continue;
       }
       idle = 0;
-      // the pieces: into registers, release their entries, write them through
-      int ps[kRing], ph[kRing];
+      int ps[kRing], ph[kRing], pu[kRing];
       int64_t pslot[kRing];
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
@@ -752,6 +491,25 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
           ps[i] = lds_ld(&ring_meta[k][0]);
           ph[i] = lds_ld(&ring_meta[k][1]);
           pslot[i] = lds_ld(&ring_meta[k][2]);
+          pu[i] = lds_ld(&ring_meta[k][3]);
+        }
+      }
+      // lane i < avail: piece i's run counter and units
+      int ci = 0, ui = 0, seen = 0;
+      if (lane < avail) {
+        int si = ps[0], hi = ph[0];
+        ui = pu[0];
+#pragma unroll
+        for (int i = 1; i < kRing; ++i)
+          if (lane == i) si = ps[i], hi = ph[i], ui = pu[i];
+        ci = si * Hkv + hi;
+        seen = load_through_i(a.ws.counters + ci);
+      }
+      // the pieces: into registers, release their entries, write them through
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        if (i < avail) {
+          const int k = (cons + i) % kRing;
           float pv[4][kSets];
 #pragma unroll
           for (int g = 0; g < 4; ++g)
@@ -771,22 +529,19 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
       cons += avail;
       lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
       __builtin_amdgcn_s_waitcnt(0);      // the slots are written through before they are counted
-      // arrivals: lane i counts piece i
       int arr = 0;
       if (lane < avail) {
-        int si = ps[0], hi = ph[0];
-#pragma unroll
-        for (int i = 1; i < kRing; ++i)
-          if (lane == i) si = ps[i], hi = ph[i];
-        arr = __hip_atomic_fetch_add(a.ws.counters + (int64_t)si * Hkv + hi, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        const int s_i = ci / Hkv;
+        const int n_i = units_for(len_lds[s_i]);
+        arr = seen + ui == n_i ? seen
+                               : __hip_atomic_fetch_add(a.ws.counters + ci, ui, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
-          const Parts r = run_parts(ps[i], ph[i]);
-          if (__builtin_amdgcn_readlane(arr, i) == r.n_sh + r.nc - 1)
-            merge(std::integral_constant<int, 16>{}, ps[i], ph[i]);
+          const int n = units_for(uniform(len_lds[ps[i]]));
+          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n) merge(ps[i], ph[i]);
         }
       }
     }
@@ -795,24 +550,15 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
 
   // ---- the streamer wave -----------------------------------------------------
   int ring_made = 0;
-  // the streamer is done: merger and claimer finish what is queued and stop
+  // the streamer is done: the merger finishes what is queued and stops
   auto finish = [&]() { lds_st(&ctl[kCtlDone], 1); };
 
   // ---- prologue: first unit's loads, next unit's table entries ------------
   // Lookahead: cur is computed, nxt has its K/V loads in flight and its ids in
   // pb_nxt, nxt2 has its table entries loading into tbl_nxt2.
-  // the first unit: the start of this worker's share, else its first claim
-  Cursor cur{};
-  cur.valid = false;
-  if (w < Q) {
-    cur = locate_share(share_begin(w), w);
-  } else if (dyn) {
-    cur = take_claim();
-  }
-  if (!cur.valid) {  // no work for this worker (its claims have all failed)
-    finish();
-    return;
-  }
+  // the first unit: the start of this worker's share
+  Cursor cur = locate(sb(w));
+  cur.left = sb(w + 1) - sb(w);
   Cursor nxt = next(cur);
   Cursor nxt2 = next(nxt);
   int pb_cur[NBU], pb_nxt[NBU];
@@ -857,13 +603,8 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     blocks_of(tbl_nxt, pb_nxt);
     load_k(nxt, tbl_nxt);
     load_q(nxt);
-    // the unit after nxt2, computed while this unit's V is in flight (finding
-    // a newly claimed chunk takes a few LDS round trips)
+    // the unit after nxt2, computed while this unit's V is in flight
     const Cursor nxt3 = next(nxt2);
-    // ask for the chunk after nxt3's segment two units ahead (two ahead for
-    // dynamic chunks of one or two units, which pass in an iteration or two)
-    if (dyn && nxt3.valid && nxt3.left <= 2)
-      request_claims((nxt3.seg >= P && nxt3.seglen <= 2) ? 2 : 1);
 
     // online softmax over these 64 positions
     const bool live = (t0 + lane) < cur.len;
@@ -914,12 +655,13 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
     load_v(nxt, pb_nxt);
     __builtin_amdgcn_wave_barrier();
 
-    // ---- end of a piece: a run ends or the segment ends ------------------
-    if (cur.g + 1 == cur.glim || cur.left == 1) {
+    // ---- end of a piece: the run or the share ends ------------------------
+    const bool run_end = cur.g + 1 == cur.n_s;
+    if (run_end || !nxt.valid) {
       float l_tot[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) l_tot[g] = (g < G) ? wave_sum(l_lane[g]) : 1.0f;
-      if (piece_g0 == 0 && cur.g + 1 == cur.n_s) {
+      if (piece_g0 == 0 && run_end) {
         // the whole run is in this piece
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -931,11 +673,11 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
           }
         }
       } else {
-        // a cut piece: the start of a run's head goes to slot r, a piece that
-        // starts share j mid-head to slot R + j, dynamic chunk d to slot
-        // R + P + d.  It is handed to the merger through the LDS ring (wait
-        // while the ring is full, which the merger rarely lets happen).
-        const int slot = (cur.seg < P && piece_g0 == 0) ? cur.s * Hkv + cur.h : R + cur.seg;
+        // a cut piece: a piece that starts a run goes to slot r, the piece
+        // that starts this worker's share inside a run to slot R + w.  It is
+        // handed to the merger through the LDS ring (wait while the ring is
+        // full, which the merger rarely lets happen).
+        const int slot = piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
         for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
              ++spin)
           __builtin_amdgcn_s_sleep(1);
@@ -955,6 +697,7 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
           ring_meta[k][0] = cur.s;
           ring_meta[k][1] = cur.h;
           ring_meta[k][2] = slot;
+          ring_meta[k][3] = cur.g - piece_g0 + 1;
         }
         lds_st(&ctl[kCtlRingMade], ++ring_made);
       }
@@ -976,43 +719,52 @@ __global__ __launch_bounds__(192) void decode_kernel(const DecodeArgs a) {
 
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partial slots at the front, the arrival counters at the back of the
+// workspace.  A call places its counters against the workspace's end: calls
+// of any shape sharing one workspace then find only counters there, which
+// every call leaves at zero, and never another call's partial results.
+struct WorkspaceLayout {
+  int64_t slots;
+  size_t ml, o, partial;  // partial slots: offsets, size
+  size_t control;         // arrival counters: size
+};
+
+WorkspaceLayout workspace_layout(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
+  WorkspaceLayout l;
+  l.slots = S * Hkv + workers;
+  l.ml = 0;
+  l.o = align256((size_t)(l.slots * 8) * sizeof(float));
+  l.partial = l.o + align256((size_t)(l.slots * 4 * D) * sizeof(float));
+  l.control = align256((size_t)(S * Hkv) * sizeof(int));
+  return l;
+}
 }  // namespace
 
-int64_t decode_max_slots(int64_t S, int64_t Hkv, int64_t max_len, int64_t workers) {
-  // a run's tail has at most all its units; M >= 8 and the class cap bound its chunks
-  const int64_t n = (max_len + kGroupTokens - 1) / kGroupTokens;
-  const int64_t chunks = n > 8 + 8 * (int64_t)(kMaxClasses - 4) ? kMaxClasses : tail_chunks((int)n, 8);
-  return S * Hkv + workers + S * Hkv * chunks;
+size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
+  const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
+  return l.partial + l.control;
 }
 
-size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t max_len, int64_t workers) {
-  const int64_t slots = decode_max_slots(S, Hkv, max_len, workers);
-  return align256((size_t)(S * Hkv) * sizeof(int)) + kClaimBytes +
-         align256((size_t)(slots * 8) * sizeof(float)) + (size_t)(slots * 4 * D) * sizeof(float);
-}
-
-DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t max_len,
+DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int64_t Hkv, int64_t D,
                                        int64_t workers) {
-  const int64_t slots = decode_max_slots(S, Hkv, max_len, workers);
-  const size_t cnt = align256((size_t)(S * Hkv) * sizeof(int));
-  const size_t ml = align256((size_t)(slots * 8) * sizeof(float));
+  const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
   char* p = reinterpret_cast<char*>(base);
   DecodeWorkspace w;
-  w.counters = reinterpret_cast<int*>(p);
-  w.claims = reinterpret_cast<int*>(p + cnt);
-  w.ml = reinterpret_cast<float*>(p + cnt + kClaimBytes);
-  w.o = reinterpret_cast<float*>(p + cnt + kClaimBytes + ml);
+  w.ml = reinterpret_cast<float*>(p + l.ml);
+  w.o = reinterpret_cast<float*>(p + l.o);
+  w.counters = reinterpret_cast<int*>(p + ((bytes - l.control) & ~(size_t)255));
   return w;
 }
 
 template <int D, int BS>
 void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
-  const uint32_t lds = (uint32_t)(((size_t)a.num_seqs * 2 + kMaxClasses + 1) * sizeof(int));
+  const uint32_t lds = (uint32_t)((size_t)a.num_seqs * 2 * sizeof(int));
   if (!start && !stop)
-    hipLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(192), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(128), lds, stream, a);
   else  // the events take the kernel's own start and end times
-    hipExtLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(192), lds, stream, start, stop, 0, a);
+    hipExtLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(128), lds, stream, start, stop, 0, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,

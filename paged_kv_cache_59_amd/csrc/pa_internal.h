@@ -21,58 +21,29 @@ constexpr int kMaxWorkers = 1 << 16;
 // LDS, 8 bytes each); the host splits larger batches into several launches.
 constexpr int kMaxSeqsPerLaunch = 4096;
 
-// Work split of one decode launch (see decode_kernel).  Every (sequence, KV
-// head) run of n 64-token units keeps its first floor(n * F / 16) units (its
-// head) in the static part, cut into one equal share per worker; the rest of
-// the run (its tail) is cut, from its end, into dynamic chunks of 1, 1, 2, 4
-// and then M units ("classes" 0, 1, 2, 3, 4, ...), that workers claim largest
-// class first.  M >= 8 keeps the classes below kMaxClasses.  F defaults to
-// kStaticSixteenths (all static: measured fastest while the claims' atomics
-// share the streaming wave's in-order memory queue); the environment variable
-// PA_DECODE_STATIC_SIXTEENTHS (0..16) overrides it per call.
-constexpr int kStaticSixteenths = 16;
-constexpr int kMaxClasses = 256;
-
-// Claim counters of the dynamic chunks: kClaimPools of them, kClaimStride
-// ints (4 KiB) apart so that they sit in different memory channels.
-constexpr int kClaimPools = 8;
-constexpr int kClaimStride = 1024;
-constexpr size_t kClaimBytes = (size_t)kClaimPools * kClaimStride * sizeof(int);
-
-// LDS exchange between a decode workgroup's three waves: cut pieces the
-// streamer hands to the merger (a ring of kRing), chunks the claimer has
-// claimed for the streamer (at most kClaimDepth queued, claimed on the
-// streamer's request), and the control words.
+// LDS exchange between a decode workgroup's two waves: cut pieces the
+// streamer hands to the merger (a ring of kRing) and the control words.
 constexpr int kRing = 4;
-constexpr int kClaimDepth = 2;
-enum { kCtlRingMade = 0, kCtlRingTaken, kCtlClaimsMade, kCtlClaimsTaken, kCtlClaimsWanted, kCtlDone };
+enum { kCtlRingMade = 0, kCtlRingTaken, kCtlDone };
 // Bound on every wait between the waves (about 0.5 s of s_sleep): a wait
 // that long means a broken invariant, and the kernel then ends with wrong
 // results rather than never.
 constexpr int kSpinLimit = 1 << 23;
 
-// Dynamic chunks of one run with a tail of b units when the top chunks are M
-// units long.
-__host__ __device__ inline int tail_chunks(int b, int M) {
-  return b <= 2 ? b : b <= 4 ? 3 : b <= 8 ? 4 : 4 + (b - 8 + M - 1) / M;
-}
-
-// Decode workspace: one arrival counter per (sequence, KV head) run, the
-// claim counters of the dynamic chunks, then the partial slots: one per run
-// (the first piece of its head), one per worker (a piece that starts its
-// share) and one per dynamic chunk, each holding for 4 query-head rows a
-// (max, sum) pair and a D-vector of unnormalised fp32 output.
+// Decode workspace.  Partial slots first: one per (sequence, KV head) run
+// (the piece that starts it) and one per share (the piece that starts the
+// share inside a run), each holding for 4 query-head rows a (max, sum) pair
+// and a D-vector of unnormalised fp32 output.  Then, against the workspace's
+// end, one arrival counter per run, zero between calls.
 struct DecodeWorkspace {
-  int* counters;  // [S][Hkv], zero between calls
-  int* claims;    // [kClaimPools * kClaimStride], zero between calls
   float* ml;      // [slots][4][2]
   float* o;       // [slots][4][D]
+  int* counters;  // [S][Hkv] units arrived
 };
 
-// Partial slots a launch over S sequences of at most max_len tokens can use.
-int64_t decode_max_slots(int64_t S, int64_t Hkv, int64_t max_len, int64_t workers);
-size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t max_len, int64_t workers);
-DecodeWorkspace decode_workspace_carve(void* base, int64_t S, int64_t Hkv, int64_t max_len,
+size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
+// The layout of one launch in a workspace of `bytes` >= decode_workspace_bytes.
+DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int64_t Hkv, int64_t D,
                                        int64_t workers);
 
 hipError_t launch_reshape_and_cache(const half_t* k, const half_t* v, half_t* k_cache,
@@ -101,8 +72,7 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int64_t num_blocks;
   int max_context_len;
-  int num_workers;        // grid size: persistent waves sharing the work
-  int static_sixteenths;  // static share of each run, in sixteenths (0..16)
+  int num_workers;        // grid size: persistent workgroups sharing the work
   DecodeWorkspace ws;
 };
 

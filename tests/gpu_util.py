@@ -43,6 +43,13 @@ def gpu_decode(w, d, num_workers=0, max_context_len=None, workspace=None):
     return d["out"].cpu().numpy()
 
 
+def decode_control_bytes(num_seqs, num_kv_heads):
+    """Bytes of arrival counters at the end of a decode workspace sized for
+    num_seqs (one int32 per (sequence, KV head) run, 256-byte aligned), which
+    every call, of whatever shape, leaves at zero."""
+    return -(-num_seqs * num_kv_heads * 4 // 256) * 256
+
+
 def gpu_step(w, d, num_workers=0):
     """copy-on-write, append, decode on one stream; returns out as numpy fp16."""
     if w.block_mapping.shape[0]:

@@ -92,20 +92,17 @@ def test_decode_argument_errors(L):
 
 
 def test_workspace_sizes(L):
-    # counters for 64 x 8 runs, 8 claim counters 4 KiB apart, then the partial
-    # slots: one per run (its head's first piece), one per worker (a piece that
-    # starts its share) and, per run, one per chunk of its tail (a 2048-token
-    # bound gives 32 units, at most 7 chunks: 1, 1, 2, 4, 8, 8, 8), each of
-    # 4 rows x (2 + 128) floats
+    # partial slots: one per run (64 x 8) and one per worker, each of 4 rows x
+    # (2 + 128) floats, (max, sum) pairs and vectors 256-byte aligned; then
+    # one arrival counter per run
     need = L.pa_decode_workspace_size(64, 8, 128, 2048, 2048)
-    slots = 64 * 8 + 2048 + 64 * 8 * 7
-    base = 64 * 8 * 4 + 8 * 4096 + slots * 4 * 130 * 4
-    assert base <= need < base + 1024
+    slots = 64 * 8 + 2048
+    assert need == slots * 8 * 4 + slots * 4 * 128 * 4 + 64 * 8 * 4
     # batches above one launch (4096 sequences) reuse the counters
     assert (L.pa_decode_workspace_size(10000, 8, 128, 100, 64)
             == L.pa_decode_workspace_size(4096, 8, 128, 100, 64))
     assert L.pa_decode_workspace_size(64, 8, 64, 2048, 2048) < need
-    assert L.pa_decode_workspace_size(64, 8, 128, 4096, 2048) > need
+    assert L.pa_decode_workspace_size(64, 8, 128, 2048, 4096) > need
     assert L.pa_decode_workspace_size(-1, 8, 128, 100, 16) == 0
     assert L.pa_decode_workspace_size(4, 8, 128, -1, 16) == 0
     assert L.pa_decode_workspace_size(4, 8, 128, 100, -2) == 0

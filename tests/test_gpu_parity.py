@@ -12,8 +12,8 @@ import torch
 import oracle
 from paged_kv_cache_59_amd import binding as pk
 from paged_kv_cache_59_amd import workloads as wl
-from tests.gpu_util import (assert_pools_equal, compare, dev, gpu_decode, gpu_step, log,
-                            oracle_decode, oracle_pools, to_device)
+from tests.gpu_util import (assert_pools_equal, compare, decode_control_bytes, dev, gpu_decode,
+                            gpu_step, log, oracle_decode, oracle_pools, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,36 +45,6 @@ def test_decode_shapes_and_work_splits(Hq, Hkv, D, workers):
     every 64-token unit is its own share and every sequence is merged."""
     w = wl.make_workload("edge", 100 + Hq + D, Hq, Hkv, D, context_lens=EDGE_LENS)
     run_case(w, workers, f"edge Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
-
-
-@pytest.mark.parametrize("sixteenths", [0, 8, 12])
-@pytest.mark.parametrize("Hq,Hkv,D,workers", [(32, 8, 128, 0), (8, 8, 128, 37), (4, 4, 64, 512),
-                                              (8, 2, 64, 3)])
-def test_dynamic_tail_chunks(monkeypatch, sixteenths, Hq, Hkv, D, workers):
-    """Runs split into a static head and dynamic tail chunks claimed at run
-    time (PA_DECODE_STATIC_SIXTEENTHS < 16): every run is then cut, and its
-    pieces merged, whatever the number of workers."""
-    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", str(sixteenths))
-    w = wl.make_workload("tails", 300 + sixteenths + Hq + D, Hq, Hkv, D,
-                         context_lens=EDGE_LENS + [2048, 3000, 4100])
-    run_case(w, workers, f"tails F{sixteenths} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
-
-
-def test_dynamic_tail_chunks_workspace_reuse(monkeypatch):
-    """Claim counters and arrival counters are left at zero by every call."""
-    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", "10")
-    w = wl.make_workload("tails-reuse", 330, 32, 8, 128, len_range=(1, 3000), num_seqs=20)
-    ws = pk.new_workspace(20, 8, 128, w.max_context_len, 64)
-    d = to_device(w)
-    pk.pa_reshape_and_cache(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
-    kc, vc = oracle_pools(w)
-    ref = oracle_decode(w, kc, vc)
-    for rep in range(3):
-        out = gpu_decode(w, d, 64, workspace=ws)
-        compare(out, ref, f"tails reuse rep{rep}")
-        counters = ws[: 20 * 8 * 4].view(torch.int32).cpu().numpy()
-        claims = ws[768:768 + 8 * 4096].view(torch.int32)[::1024].cpu().numpy()
-        assert (counters == 0).all() and (claims == 0).all()
 
 
 def test_ragged_random_lengths_many_seqs():
@@ -248,12 +218,14 @@ def test_side_stream():
 
 
 def test_workspace_reuse_leaves_counters_zero():
-    """Every call leaves the arrival counters at zero: the same workspace serves
-    consecutive calls, also with a different batch shape."""
+    """Every call leaves the workspace's control words at zero: the same
+    workspace serves consecutive calls, also with a different batch shape
+    (whose partial results and control words sit elsewhere)."""
     w1 = wl.make_workload("reuse1", 216, 32, 8, 128, len_range=(300, 900), num_seqs=7)
     w2 = wl.make_workload("reuse2", 217, 32, 8, 128, len_range=(1, 500), num_seqs=5)
     workers = 50
-    ws = pk.new_workspace(7, 8, 128, max(w1.max_context_len, w2.max_context_len), workers)
+    ws_len = max(w1.max_context_len, w2.max_context_len)
+    ws = pk.new_workspace(7, 8, 128, ws_len, workers)
     for rep in range(3):
         for w in (w1, w2):
             d = to_device(w)
@@ -264,12 +236,7 @@ def test_workspace_reuse_leaves_counters_zero():
             out = gpu_decode(w, d, workers, workspace=ws)
             kc, vc = oracle_pools(w)
             compare(out, oracle_decode(w, kc, vc), f"reuse {w.name} rep{rep}")
-            counters = ws[: 7 * 8 * 4].view(torch.int32).cpu().numpy()
-            assert (counters == 0).all()
-            # the 8 claim counters of the dynamic segments follow the arrival
-            # counters (256-byte aligned), 4 KiB apart
-            claims = ws[256:256 + 8 * 4096].view(torch.int32)[::1024].cpu().numpy()
-            assert (claims == 0).all()
+            assert not ws[len(ws) - decode_control_bytes(7, 8):].any()
 
 
 def test_batch_above_one_launch():
@@ -327,8 +294,8 @@ def test_decode_block_sizes(BS, Hq, Hkv, D, workers):
 
 
 @pytest.mark.parametrize("BS", [8, 32])
-def test_decode_block_sizes_dynamic_tails_and_prefix(monkeypatch, BS):
-    monkeypatch.setenv("PA_DECODE_STATIC_SIXTEENTHS", "8")
+@pytest.mark.parametrize("workers", [0, 41])
+def test_decode_block_sizes_prefix(BS, workers):
     w = wl.make_workload("bsp", 950 + BS, 32, 8, 128, num_seqs=12, prefix_groups=3,
                          prefix_len=128, suffix_range=(1, 300), block_size=BS)
-    run_case(w, 0, f"decode BS{BS} prefix + dynamic tails")
+    run_case(w, workers, f"decode BS{BS} prefix workers{workers}")
