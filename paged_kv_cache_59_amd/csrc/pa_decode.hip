@@ -394,59 +394,86 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // R + v for a piece that starts share v.  Lane 16*gq + pq handles head gq:
   // for a batch of up to 16 pieces it loads (max, sum) of piece pq and output
   // dims pq*kF .. +kF of head gq of every piece (one round trip); batches
-  // combine with the running-max rescale.  Writes the output rows, then
-  // clears the run's counter for the next call.
-  auto merge = [&](int s, int kvh) {
+  // combine with the running-max rescale into (mx, lsum, acc): mx the running
+  // max of head gq, lsum this lane's part of the weighted sum, acc the
+  // weighted output dims.
+  struct Merged {
+    float mx, lsum;
+    float acc[kF];
+  };
+  const int gq = lane >> 4, pq = lane & 15;
+  // one batch of nb <= B pieces whose slot lane pq holds in sl (lanes past
+  // the batch repeat its last), B = 2, 4 or 16 so that small batches load
+  // only what they use
+  auto absorb = [&](auto batch, Merged& m, int sl, int nb) {
+    constexpr int B = decltype(batch)::value;
+    const bool valid = pq < nb && gq < G;
+    const float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
+    const float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
+    float ov[B][kF];
+#pragma unroll
+    for (int qi = 0; qi < B; ++qi) {
+      const float* base = a.ws.o + (int64_t)__builtin_amdgcn_readlane(sl, qi) * 4 * D;
+#pragma unroll
+      for (int st = 0; st < kSets; ++st) {
+        const float4_t x = load_through16(base, ((gq & 3) * D + pq * kF + st * 4) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[qi][st * 4 + e] = x[e];
+      }
+    }
+    const float m_new = fmaxf(m.mx, row_max16(m_p));
+    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m.mx - m_new);
+    const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
+    m.lsum = m.lsum * alpha + wt * l_p;
+    m.mx = m_new;
+#pragma unroll
+    for (int j = 0; j < kF; ++j) m.acc[j] *= alpha;
+#pragma unroll
+    for (int qi = 0; qi < B; ++qi) {
+      const float wq = __shfl(wt, (lane & 48) | qi);  // 0 for pieces past the batch
+#pragma unroll
+      for (int j = 0; j < kF; ++j) m.acc[j] += wq * ov[qi][j];
+    }
+  };
+  // all pieces of run (s, kvh)
+  auto merge_pieces = [&](int s, int kvh) {
+    Merged m;
+    m.mx = -INFINITY;
+    m.lsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kF; ++j) m.acc[j] = 0.0f;
     const int n = units_for(uniform(len_lds[s]));
     const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
     const int r = s * Hkv + kvh;
-    const int gq = lane >> 4, pq = lane & 15;
-    float acc[kF];
-#pragma unroll
-    for (int j = 0; j < kF; ++j) acc[j] = 0.0f;
-    float mx = -INFINITY, lsum = 0.0f;
-    const int va = share_of(u0), np_all = share_of(u0 + n - 1) - va + 1;
+    const int va = share_of(u0), vb = share_of(u0 + n - 1);
+    const int np_all = vb - va + 1;
     for (int p0 = 0; p0 < np_all; p0 += 16) {
-      const int np = min(16, np_all - p0);
-      const bool valid = pq < np && gq < G;
+      const int nb = min(16, np_all - p0);
       // piece p0 + pq (pieces past the batch repeat its last)
-      const int v = va + p0 + min(pq, np - 1);
+      const int p = p0 + min(pq, nb - 1);
+      const int v = va + p;
       const int sl = v == va ? r : R + v;
-      const float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
-      const float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
-      float ov[16][kF];
-#pragma unroll
-      for (int qi = 0; qi < 16; ++qi) {
-        const float* base = a.ws.o + (int64_t)__builtin_amdgcn_readlane(sl, qi) * 4 * D;
-#pragma unroll
-        for (int st = 0; st < kSets; ++st) {
-          const float4_t x = load_through16(base, ((gq & 3) * D + pq * kF + st * 4) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[qi][st * 4 + e] = x[e];
-        }
-      }
-      const float m_new = fmaxf(mx, row_max16(m_p));
-      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(mx - m_new);
-      const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
-      lsum = lsum * alpha + wt * l_p;
-      mx = m_new;
-#pragma unroll
-      for (int j = 0; j < kF; ++j) acc[j] *= alpha;
-#pragma unroll
-      for (int qi = 0; qi < 16; ++qi) {
-        const float wq = __shfl(wt, (lane & 48) | qi);  // 0 for pieces past the batch
-#pragma unroll
-        for (int j = 0; j < kF; ++j) acc[j] += wq * ov[qi][j];
-      }
+      if (nb <= 2)
+        absorb(std::integral_constant<int, 2>{}, m, sl, nb);
+      else if (nb <= 4)
+        absorb(std::integral_constant<int, 4>{}, m, sl, nb);
+      else
+        absorb(std::integral_constant<int, 16>{}, m, sl, nb);
     }
-    const float inv = 1.0f / row_sum16(lsum);
+    return m;
+  };
+  // the output rows of run (s, kvh) from its merged pieces; clears the run's
+  // counter for the next call
+  auto merge_out = [&](int s, int kvh, const Merged& m) {
+    const float inv = 1.0f / row_sum16(m.lsum);
     if (gq < G) {
       half_t* o = a.out + ((int64_t)s * Hq + kvh * G + gq) * D + pq * kF;
 #pragma unroll
-      for (int j = 0; j < kF; ++j) o[j] = (half_t)(acc[j] * inv);
+      for (int j = 0; j < kF; ++j) o[j] = (half_t)(m.acc[j] * inv);
     }
-    if (lane == 0)  // ready for the next call
-      __hip_atomic_store(a.ws.counters + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+      __hip_atomic_store(a.ws.counters + s * Hkv + kvh, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // per-piece softmax state
@@ -531,8 +558,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       __builtin_amdgcn_s_waitcnt(0);      // the slots are written through before they are counted
       int arr = 0;
       if (lane < avail) {
-        const int s_i = ci / Hkv;
-        const int n_i = units_for(len_lds[s_i]);
+        const int n_i = units_for(len_lds[ci / Hkv]);
         arr = seen + ui == n_i ? seen
                                : __hip_atomic_fetch_add(a.ws.counters + ci, ui, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
@@ -541,7 +567,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
           const int n = units_for(uniform(len_lds[ps[i]]));
-          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n) merge(ps[i], ph[i]);
+          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n)
+            merge_out(ps[i], ph[i], merge_pieces(ps[i], ph[i]));
         }
       }
     }
