@@ -103,6 +103,9 @@ struct PrefillArgs {
   int tile_groups;
 };
 
+// 32-key K/V steps a prefill workgroup keeps in its LDS ring (64 KiB at D = 128)
+constexpr int kPrefillStages = 4;
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

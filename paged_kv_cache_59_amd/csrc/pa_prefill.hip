@@ -27,6 +27,16 @@
 // 8 consecutive tokens of one 8-token V group, so its V^T operand is one
 // 16-byte load, and the O^T result of lane l is its own row c, the row whose
 // softmax state it holds.
+//
+// K and V reach the waves through LDS: a workgroup's 4 waves (128 rows of
+// one (sequence, KV head)) share every 32-key step, which the waves copy
+// from memory into a ring of kStages steps with LDS-DMA loads
+// (global_load_lds_dwordx4, 1 KiB per wave instruction), kStages - 1 steps
+// ahead.  Read straight from L2 into each wave's registers, every step's
+// K/V would cross the L2-to-CU path 4 times, which bounds the MFMA rate at
+// about half of peak (a 32-row wave needs 1/32 byte of K/V per flop).  In LDS
+// the K tile is stored in the MFMA's key order and the V tile by 8-key group,
+// so that each 16-lane group of a wave reads 256 contiguous bytes.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -57,6 +67,17 @@ __device__ __forceinline__ float sum8(half8_t v) {
   return acc;
 }
 
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 k-slot groups of one row),
+// with the gfx950 cross-row swaps: each swap of x with itself leaves lane
+// l's value and its partner's across the 16- (32-) lane boundary in its two
+// results.
+__device__ __forceinline__ float max_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(x, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
+}
+
 __device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -72,9 +93,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   static_assert(NBS * BS == 32, "block size 8, 16 or 32");
   constexpr float kStale = 8.0f;         // see the rescale below
   constexpr float kFloor = -1.0e30f;     // initial reference max (log2 units)
+  constexpr int kTileBytes = 32 * D * 2;        // K (or V) of one 32-key step
+  constexpr int kStepBytes = 2 * kTileBytes;    // K then V
+  constexpr int kDmaPerTile = kTileBytes / 4096;  // wave instructions per tile and wave
+  constexpr int kDmaPerStep = 2 * kDmaPerTile;
+  static_assert(kDmaPerTile * 4096 == kTileBytes, "head_dim must be 64 or 128");
+  extern __shared__ __attribute__((aligned(16))) char kv_lds[];  // [kPrefillStages][kStepBytes]
+  constexpr int kStages = kPrefillStages;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;  // column of the MFMA operands / results: this lane's row
   const int j = lane >> 4;    // k-slot group
 
@@ -89,7 +117,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   if (sh >= a.num_seqs * a.num_kv_heads) return;
   const int s = sh / a.num_kv_heads;
   const int h = sh - s * a.num_kv_heads;
-  const int tile = (a.tile_groups - 1 - m % a.tile_groups) * 4 + wave;
+  const int group = a.tile_groups - 1 - m % a.tile_groups;
+  const int tile = group * 4 + wave;
 
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
@@ -97,10 +126,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int nq = a.query_start[s + 1] - t0;
   const int len = min(max(a.context_lens[s], 0), a.max_context_len);
   // an empty chunk, or one that breaks a precondition (longer than its
-  // context or than the bound, or rows outside q): nothing to do
+  // context or than the bound, or rows outside q): nothing to do (the whole
+  // workgroup leaves together)
   if (nq <= 0 || nq > len || nq > a.max_query_len || t0 < 0 || t0 + nq > a.num_tokens) return;
   const int rows = nq * G;
-  if (tile * 32 >= rows) return;
+  if (group * 128 >= rows) return;
+  // steps of the workgroup: keys 0 .. the position of its last row; every
+  // wave takes part in all of them (the ring's barriers), and computes those
+  // up to its own last row
+  const int wg_last_row = min(group * 128 + 127, rows - 1);
+  const int nsteps = (len - nq + wg_last_row / G) / 32 + 1;
+  const bool active = tile * 32 < rows;  // (uniform per wave)
 
   // this lane's two rows (sub-tiles rt = 0, 1)
   int tok[2], grp[2], pos[2];
@@ -114,10 +150,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     grp[rt] = rr - tok[rt] * G;
     pos[rt] = valid[rt] ? len - nq + tok[rt] : -1;
   }
-  const int last_row = min(tile * 32 + 31, rows - 1);
-  const int pos_first = len - nq + (tile * 32) / G;  // the tile's first (smallest) position
-  const int pos_max = len - nq + last_row / G;
-  const int nsteps = pos_max / 32 + 1;  // 32-key steps covering keys 0 .. pos_max
+  const int last_row = active ? min(tile * 32 + 31, rows - 1) : rows - 1;
+  const int pos_first = len - nq + (min(tile * 32, rows - 1)) / G;  // the tile's first position
+  const int my_steps = active ? (len - nq + last_row / G) / 32 + 1 : 0;
 
   // Q^T operands, held for the whole loop
   half8_t qf[2][KS];
@@ -136,49 +171,86 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int64_t hoff = (int64_t)h * kTile;
   const int64_t bstride = (int64_t)a.num_kv_heads * kTile;
   // physical block of logical block lb (clamped to the sequence's last): a
-  // scalar load, whose wait (lgkmcnt) does not drain the K/V loads in flight
-  auto phys_of = [&](int lb) -> int64_t {
-    const int e = row[__builtin_amdgcn_readfirstlane(min(lb, last_blk))];
+  // scalar load, whose wait (lgkmcnt) does not drain the loads in flight
+  // (read through the constant address space: a scalar load, which the LDS
+  // copies in flight cannot be taken to alias)
+  const __attribute__((address_space(4))) int32_t* crow =
+      (const __attribute__((address_space(4))) int32_t*)row;
+  auto phys_of = [&](int lb) -> int {
+    const int e = crow[__builtin_amdgcn_readfirstlane(min(lb, last_blk))];
     return (e >= 0 && e < a.num_blocks) ? e : 0;  // a broken table entry reads block 0
   };
-  // key of this lane's K rows in S^T sub-tile kt: 8 (c16 / 4) + 4 kt + c16 % 4
-  const int kq = 8 * (c16 >> 2) + (c16 & 3);
-  half8_t kf[2][KS], vf[DT];
   // The NBS blocks of a step (keys i BS .. i BS + BS - 1 in block i), as
-  // separate values: a lane picks its own with selects (an indexed array
-  // would be placed in scratch memory).
-  struct StepBlocks {
-    int64_t p0, p1, p2, p3;
-  };
-  auto step_blocks = [&](int st) {
-    StepBlocks b{phys_of(NBS * st), 0, 0, 0};
-    if (NBS > 1) b.p1 = phys_of(NBS * st + 1);
+  // separate scalars (uniform): a lane picks its own with selects.  (Held
+  // in a struct or an array across the loop, the compiler indexes them in
+  // scratch memory.)
+  int nb0 = 0, nb1 = 0, nb2 = 0, nb3 = 0;  // the next step to issue
+  auto fetch_blocks = [&](int st) {
+    st = min(st, nsteps - 1);  // steps past the end re-read the last one
+    nb0 = phys_of(NBS * st);
+    if (NBS > 1) nb1 = phys_of(NBS * st + 1);
     if (NBS > 2) {
-      b.p2 = phys_of(NBS * st + 2);
-      b.p3 = phys_of(NBS * st + 3);
-    }
-    return b;
-  };
-  auto pick = [&](const StepBlocks& b, int i) -> int64_t {
-    if constexpr (NBS == 1) return b.p0;
-    else if constexpr (NBS == 2) return i == 0 ? b.p0 : b.p1;
-    else return i < 2 ? (i == 0 ? b.p0 : b.p1) : (i == 2 ? b.p2 : b.p3);
-  };
-  auto load_k = [&](const StepBlocks& b) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = kq + 4 * kt;  // < 32
-      const half_t* kp = a.k_cache + pick(b, key / BS) * bstride + hoff + (key % BS) * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = ld16(kp + (int64_t)(ks * 4 + j) * BS * 8);
+      nb2 = phys_of(NBS * st + 2);
+      nb3 = phys_of(NBS * st + 3);
     }
   };
-  auto load_v = [&](const StepBlocks& b) {
-    // V^T operand: keys 8j..8j+7 = block 8j / BS, 8-token group (8j % BS) / 8
-    const half_t* vp = a.v_cache + pick(b, (8 * j) / BS) * bstride + hoff +
-                       (int64_t)((8 * j % BS) / 8) * D * 8;
+  // element offset of block i of the step
+  auto pick = [&](int b0, int b1, int b2, int b3, int i) -> int64_t {
+    const int64_t o0 = (int64_t)b0 * bstride, o1 = (int64_t)b1 * bstride;
+    const int64_t o2 = (int64_t)b2 * bstride, o3 = (int64_t)b3 * bstride;
+    if constexpr (NBS == 1) return o0;
+    else if constexpr (NBS == 2) return i == 0 ? o0 : o1;
+    else return i < 2 ? (i == 0 ? o0 : o1) : (i == 2 ? o2 : o3);
+  };
+
+  // One step's K and V into ring stage `stage`: each wave writes its
+  // kDmaPerTile KiB of each tile; lane L of wave instruction ci writes 16
+  // bytes at ci KiB + 16 L.
+  //   K tile: [chunk c of 8 dims][slot 16 kt + c][8 dims]; slot (kt, c)
+  //           holds key 8 (c / 4) + 4 kt + c % 4 (the MFMA's key order).
+  //   V tile: [8-key group jj][dim][8 keys].
+  auto issue = [&](int b0, int b1, int b2, int b3, int stage) {
+    char* base = kv_lds + stage * kStepBytes;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vf[dt] = ld16(vp + (int64_t)(dt * 16 + c16) * 8);
+    for (int i = 0; i < kDmaPerTile; ++i) {
+      const int ci = wave * kDmaPerTile + i;
+      const int c = 2 * ci + (lane >> 5), slot = lane & 31;
+      const int cs = slot & 15, key = 8 * (cs >> 2) + (cs & 3) + 4 * (slot >> 4);
+      const half_t* src = a.k_cache + pick(b0, b1, b2, b3, key / BS) + hoff + (c * BS + key % BS) * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + ci * 1024),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kDmaPerTile; ++i) {
+      const int ci = wave * kDmaPerTile + i;
+      const int e = ci * 64 + lane, jj = e / D, d = e % D;
+      const half_t* src = a.v_cache + pick(b0, b1, b2, b3, (8 * jj) / BS) + hoff +
+                          (int64_t)((8 * jj % BS) / 8 * D + d) * 8;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(base + kTileBytes + ci * 1024), 16, 0, 0);
+    }
+  };
+  half8_t kf[2][KS], vf[DT];
+  auto read_k = [&](int stage) {
+    const char* base = kv_lds + stage * kStepBytes;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kt][ks] = *reinterpret_cast<const half8_t*>(base + ((4 * ks + j) * 32 + kt * 16 + c16) * 16);
+  };
+  auto read_v = [&](int stage) {
+    const char* base = kv_lds + stage * kStepBytes + kTileBytes;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vf[dt] = *reinterpret_cast<const half8_t*>(base + (j * D + dt * 16 + c16) * 16);
+  };
+  // s_waitcnt for "at most n vector memory operations of this wave in
+  // flight" (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+  // left at their maxima, i.e. not waited for)
+  auto wait_vm = [](auto n) {
+    constexpr int N = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
   };
 
   float4v o[2][DT];
@@ -192,21 +264,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   float m_run[2] = {kFloor, kFloor};
   float l_lane[2] = {0.0f, 0.0f};
 
-  // Pipeline: step st+1's K is issued once step st's logits are done with
-  // kf, its V once step st's value product is done with vf; the loads then
-  // fly under the softmax and the other product.
-  {
-    const StepBlocks b0 = step_blocks(0);
-    load_k(b0);
-    load_v(b0);
+  // Ring: steps 0 .. kStages - 2 are issued first; at step st the waves
+  // wait for their own copies of step st, meet at a barrier (then every
+  // wave's copy has landed, and every wave is done with stage (st - 1) %
+  // kStages), and issue step st + kStages - 1 into that stage.  Every step
+  // issues the same loads (past the end they re-read the last step), so the
+  // wait counts are exact.  Table entries are read one issue ahead.
+  fetch_blocks(0);
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p) {
+    const int b0 = nb0, b1 = nb1, b2 = nb2, b3 = nb3;
+    fetch_blocks(p + 1);
+    issue(b0, b1, b2, b3, p);
   }
   for (int st = 0; st < nsteps; ++st) {
-    // every step issues the same loads (the last one re-reads its own blocks,
-    // which hit L2), so the hardware wait counts stay exact across the loop;
-    // the next step's table entries load under this step's logits
-    const int nxt = min(st + 1, nsteps - 1);
-    const StepBlocks bn = step_blocks(nxt);
-    // logits of both row sub-tiles, then the next step's K
+    const int stage = st % kStages;
+    wait_vm(std::integral_constant<int, kDmaPerStep * (kStages - 2)>{});
+    __builtin_amdgcn_s_barrier();
+    {
+      const int b0 = nb0, b1 = nb1, b2 = nb2, b3 = nb3;
+      fetch_blocks(st + kStages);
+      issue(b0, b1, b2, b3, (st + kStages - 1) % kStages);
+    }
+    if (st >= my_steps) continue;  // past this wave's last row (uniform)
+
+    read_k(stage);
+    // logits of both row sub-tiles
     float4v sacc[2][2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -217,11 +300,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           sacc[rt][kt] = mfma16x16x32(kf[kt][ks], qf[rt][ks], sacc[rt][kt]);
       }
-    load_k(bn);
+    read_v(stage);
 
-    // positions past the context (the last block's tail: any bits, NaN
-    // included, and re-read blocks past it) get V := 0 by selection; their
-    // logits are removed below, and 0 * NaN would not be 0
     // raw logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row.
     // The scale c > 0 (the host folds a negative scale into q's sign) enters
     // through the row max, max(c z) = c max(z), and the exponent's fma.
@@ -249,8 +329,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       mt[rt] = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mt[rt] = fmaxf(mt[rt], z[rt][e]);
-      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16));
-      mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32)) * a.scale_log2;
+      mt[rt] = max_rows(mt[rt]) * a.scale_log2;
     }
     // The reference max m_run is raised only when a row's max passes it by
     // more than kStale (log2 units); otherwise the weights exp2(z - m_run)
@@ -284,8 +363,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vf[dt], pf[rt], o[rt][dt]);
-    load_v(bn);
   }
+  wait_vm(std::integral_constant<int, 0>{});  // the ring's last copies land before the wave ends
+  if (!active) return;
 
   // out[row][dims 16 dt + 4 j .. +3] = O^T / l
 #pragma unroll
@@ -310,9 +390,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t padded = (pairs + 7) / 8 * 8 * a.tile_groups;  // 8 XCDs x pairs/8 x tile groups
   const dim3 grid((unsigned)padded);
-#define PA_PREFILL(D, BS)                     \
-  if (a.head_dim == D && a.block_size == BS) \
-    hipLaunchKernelGGL((prefill_kernel<D, BS>), grid, dim3(256), 0, stream, a);
+#define PA_PREFILL(D, BS)                                                             \
+  if (a.head_dim == D && a.block_size == BS)                                         \
+    hipLaunchKernelGGL((prefill_kernel<D, BS>), grid, dim3(256),                     \
+                       (size_t)kPrefillStages * 2 * 32 * D * sizeof(half_t), stream, a);
   PA_PREFILL(128, 16) PA_PREFILL(64, 16) PA_PREFILL(128, 8) PA_PREFILL(64, 8) PA_PREFILL(128, 32)
   PA_PREFILL(64, 32)
 #undef PA_PREFILL
