@@ -21,7 +21,14 @@ namespace pa {
 // One lane per (token, KV head, 16-byte chunk of the head dimension), for a
 // block size BS of 8, 16 or 32 token slots.
 // K: the chunk lands whole at k[b][h][chunk][o][0..7] (16 contiguous bytes).
-// V: its 8 elements land at v[b][h][o/8][d][o%8], one element per 16 bytes.
+// V: its 8 elements land at v[b][h][o/8][d][o%8], 8 consecutive slots of one
+// dimension per 16 bytes.  When the 8 tokens t..t+7 fill one aligned 8-slot
+// group (slot of t a multiple of 8, slots consecutive: the usual case for a
+// prefill chunk), the lane of token t gathers their 8 rows and writes 8 whole
+// 16-byte groups; the lanes of t+1..t+7 leave V to it.  Any other token (a
+// decode step's single tokens, a group only partly in the batch) writes its
+// 8 elements one by one.  Lead and members test the same 8 slot entries, so
+// every element is written exactly once.
 template <int D, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const half_t* __restrict__ k, const half_t* __restrict__ v, half_t* __restrict__ k_cache,
@@ -39,16 +46,41 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   if (slot < 0 || slot >= num_blocks * BS) return;
   const int64_t b = slot / BS;
   const int o = (int)(slot - b * BS);
-  const int64_t src = (t * num_kv_heads + h) * D + c * kChunk;
+  const int64_t row = (int64_t)num_kv_heads * D;  // elements per token of k and v
+  const int64_t src = t * row + h * D + c * kChunk;
   const int64_t tile = (b * num_kv_heads + h) * (int64_t)(BS * D);
 
   const half8_t kv = *reinterpret_cast<const half8_t*>(k + src);
   *reinterpret_cast<half8_t*>(k_cache + tile + ((int64_t)c * BS + o) * kChunk) = kv;
 
-  const half8_t vv = *reinterpret_cast<const half8_t*>(v + src);
-  half_t* vdst = v_cache + tile + ((int64_t)(o / kChunk) * D + c * kChunk) * kChunk + (o % kChunk);
+  // the aligned 8-slot group of this token, and whether tokens lead..lead+7
+  // fill it in order
+  const int o8 = (int)(slot % kChunk);
+  const int64_t lead = t - o8;
+  bool whole = lead >= 0 && lead + kChunk <= num_tokens;
+  if (whole) {
 #pragma unroll
-  for (int e = 0; e < kChunk; ++e) vdst[e * kChunk] = vv[e];
+    for (int i = 0; i < kChunk; ++i) whole = whole && slot_mapping[lead + i] == slot - o8 + i;
+  }
+  // dims c*8 .. c*8+7 of the 8-slot group start here
+  half_t* vgrp = v_cache + tile + ((int64_t)(o / kChunk) * D + c * kChunk) * kChunk;
+  if (whole) {
+    if (o8 != 0) return;  // the group's first token writes it
+    half8_t rows[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) rows[i] = *reinterpret_cast<const half8_t*>(v + src + i * row);
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+      half8_t col;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) col[i] = rows[i][e];
+      *reinterpret_cast<half8_t*>(vgrp + e * kChunk) = col;
+    }
+    return;
+  }
+  const half8_t vv = *reinterpret_cast<const half8_t*>(v + src);
+#pragma unroll
+  for (int e = 0; e < kChunk; ++e) vgrp[e * kChunk + o8] = vv[e];
 }
 
 // One workgroup per (pair, KV head, K|V): the (block, head) tile is BS*D

@@ -35,6 +35,40 @@ def test_append_and_copy_bit_exact(BS, D):
 
 
 @pytest.mark.parametrize("BS", [8, 16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_append_runs_of_slots_bit_exact(BS, D):
+    """Prefill-style appends: runs of consecutive slots starting at several
+    offsets of a block and crossing into the next block, aligned 8-slot groups
+    only partly in the batch, single scattered tokens and skipped (-1) slots
+    in between, bit-exact against the oracle (whole 8-slot groups take the
+    append's gathered path, the rest its element path)."""
+    rng = np.random.default_rng(3000 + BS + D)
+    Hkv, NB = 4, 64
+    kc = rng.standard_normal((NB, Hkv, D // 8, BS, 8), dtype=np.float32).astype(np.float16)
+    vc = rng.standard_normal((NB, Hkv, BS // 8, D, 8), dtype=np.float32).astype(np.float16)
+    free = list(rng.permutation(NB))
+    slots = []
+    # (first logical position, tokens): runs of a sequence's positions
+    for start, n in [(0, 3 * BS), (3, 2 * BS + 5), (8 % BS, 13), (BS - 2, 9), (5, 3), (0, 5), (8, 7)]:
+        nblk = (start + n - 1) // BS + 1
+        blocks = [free.pop() for _ in range(nblk)]
+        slots += [blocks[(start + i) // BS] * BS + (start + i) % BS for i in range(n)]
+        slots.append(-1)                                   # a skipped token between runs
+        slots.append(free.pop() * BS + int(rng.integers(BS)))  # a single scattered token
+    slots = np.asarray(slots, dtype=np.int64)
+    T = slots.shape[0]
+    kn = rng.standard_normal((T, Hkv, D), dtype=np.float32).astype(np.float16)
+    vn = rng.standard_normal((T, Hkv, D), dtype=np.float32).astype(np.float16)
+    log(f"append runs BS={BS} D={D}: {T} tokens")
+    kd, vd = dev(kc), dev(vc)
+    pk.pa_reshape_and_cache(dev(kn), dev(vn), kd, vd, dev(slots))
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache(kn, vn, kc, vc, slots, block_size=BS)
+    assert np.array_equal(u16(kd), ek.view(np.uint16))
+    assert np.array_equal(u16(vd), ev.view(np.uint16))
+
+
+@pytest.mark.parametrize("BS", [8, 16, 32])
 def test_swap_out_to_pinned_host_and_back(BS):
     rng = np.random.default_rng(BS)
     Hkv, D, NB, NH = 8, 128, 40, 24
