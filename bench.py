@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="decode: a third pass of kernel timings, each step preceded by a write "
+                         "of this many MB of scratch (flushes L2 and the Infinity Cache); 0 = skip")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32])
     ap.add_argument("--swap-blocks", type=int, default=0,
                     help="only measure swapping this many blocks (Llama-3.1-8B layer shape) "
@@ -83,14 +86,25 @@ def measured_traffic(workload):
     return int(round(rec["traffic_bytes_per_dispatch"]))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def cpu_baseline(w, budget_s):
-    """The oracle (as it is) on whole steps of the same batch, on this host."""
+    """The oracle (as it is) on whole steps of the same batch, on this host;
+    then one step with BLAS on a single thread."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas = 1
+        blas, threadpool_limits = 1, None
     step_bytes = w.decode_bytes() + w.append_bytes() + w.copy_bytes()
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -102,9 +116,19 @@ def cpu_baseline(w, budget_s):
         if el >= budget_s * 0.5 or reps >= 20:
             break
     sec = el / reps
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            oracle.decode_step(w.q, w.k_new, w.v_new, w.k_cache, w.v_cache, w.block_tables,
+                               w.context_lens, w.slot_mapping, w.block_mapping, w.scale,
+                               w.num_kv_heads)
+            one = time.perf_counter() - t1
     return {"value": step_bytes / sec / 1e9, "unit": "GB/s", "cores": int(blas),
             "kind": "oracle", "seconds_per_step": sec, "seqs_per_s": w.num_seqs / sec,
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "one_thread_seconds_per_step": one,
+            "host_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
             "sample": f"{reps} whole step(s) of {w.name} (copy, append, fp64 decode of all "
                       f"{w.num_seqs} sequences), NumPy"}
 
@@ -362,6 +386,26 @@ def main():
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in kev])
 
+    # cross-check of the cache hygiene: the same steps once more, each
+    # preceded (outside the kernel-bound events) by a write of flush_mb MB of
+    # scratch, which evicts L2 and the Infinity Cache; with the replicas
+    # rotating, the kernel should take as long as above
+    flushed_ms = None
+    if args.flush_mb > 0:
+        scratch = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device="cuda")
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in fev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scratch.fill_(i & 255)
+            step(2 * args.steps + i, kernel_ev=fev[i])
+        torch.cuda.synchronize()
+        flushed_ms = np.array([a.elapsed_time(b) for a, b in fev])
+        del scratch
+
     ms_per_step = wall * 1e3 / args.steps
     step_bytes = w.decode_bytes() + w.append_bytes() + w.copy_bytes()
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -402,6 +446,9 @@ def main():
             "timing": "HIP events bound to the decode kernel (hipExtLaunchKernel), over "
                       "the timed steps run again right after the wall-clock region",
             "call_mean_us": round(float(call_ms.mean()) * 1e3, 3),
+            "flushed_mean_us": (None if flushed_ms is None
+                                else round(float(flushed_ms.mean()) * 1e3, 3)),
+            "flush_mb": args.flush_mb,
             "call_frac": round(w.decode_bytes() / (float(call_ms.mean()) * 1e-3) / 1e9
                                / HBM_PEAK_GBS, 4),
         },
