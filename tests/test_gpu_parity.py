@@ -47,6 +47,24 @@ def test_decode_shapes_and_work_splits(Hq, Hkv, D, workers):
     run_case(w, workers, f"edge Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
 
 
+@pytest.mark.parametrize("n_len,workers", [(4096, 64), (4100, 70), (64 * 37, 37), (32768, 512)])
+def test_one_run_over_many_shares(n_len, workers):
+    """One (sequence, KV head) run cut into one piece per worker: its merge
+    combines the pieces in several batches (16 slots per round trip, then a
+    last batch of 2, 4 or 16), each rescaled to the running maximum."""
+    w = wl.make_workload("long-run", 700 + workers, 4, 1, 128, context_lens=[n_len])
+    run_case(w, workers, f"one run of {n_len} tokens over {workers} workers")
+
+
+@pytest.mark.parametrize("workers", [3, 16, 17])
+def test_runs_across_share_edges(workers):
+    """Runs whose lengths put share edges at every offset inside a run, with
+    runs both shorter and longer than a share."""
+    w = wl.make_workload("edges", 720 + workers, 8, 2, 64,
+                         context_lens=[64 * k + (k % 3) for k in range(1, 12)])
+    run_case(w, workers, f"share edges, {workers} workers")
+
+
 def test_ragged_random_lengths_many_seqs():
     w = wl.make_workload("ragged", 201, 32, 8, 128, len_range=(1, 700), num_seqs=40)
     run_case(w, 96, "ragged 40 seqs 96 workers")
