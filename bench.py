@@ -14,8 +14,10 @@ Prints one JSON line:
                the merge of cut sequences fused) timed with HIP events bound to
                the kernel on its stream: algorithmic decode bytes / mean kernel
                duration vs 8 TB/s, over a second pass of the same steps
-               (`call_mean_us`: events recorded around the call in the timed
-               region, which add queueing and dispatch latency);
+               (`call_mean_us`: events recorded around the call, in a pass of
+               their own, which add queueing and dispatch latency; the
+               wall-clock region records no events, since on this stack each
+               record costs the step several microseconds);
                `traffic` is the HBM bytes per launch from the committed
                rocprofv3 counter summary (profiles/), null if the kernel changed
   cpu_baseline the CPU oracle on this host on one whole step of the same batch
@@ -196,14 +198,18 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # wall clock over exactly `steps` steps, no events in between; then the
+    # same steps with events around each prefill call
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = wall * 1e3 / args.steps
     mean_s = float(ms.mean()) * 1e-3
@@ -357,17 +363,22 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronised on both sides, with
-    # events recorded around each decode call (they include queueing and
-    # dispatch latency)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, synchronised on both sides and
+    # nothing else enqueued between them
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # the same steps again with events recorded around each decode call (they
+    # include queueing and dispatch latency)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.steps + i, evs[i])
+    torch.cuda.synchronize()
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
     # kernel durations: the same `steps` steps again, right after, with events
@@ -382,7 +393,7 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(args.steps + i, kernel_ev=kev[i])
+        step(2 * args.steps + i, kernel_ev=kev[i])
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in kev])
 
@@ -401,7 +412,7 @@ def main():
         torch.cuda.synchronize()
         for i in range(args.steps):
             scratch.fill_(i & 255)
-            step(2 * args.steps + i, kernel_ev=fev[i])
+            step(3 * args.steps + i, kernel_ev=fev[i])
         torch.cuda.synchronize()
         flushed_ms = np.array([a.elapsed_time(b) for a, b in fev])
         del scratch

@@ -20,15 +20,19 @@ namespace pa {
 
 // One lane per (token, KV head, 16-byte chunk of the head dimension), for a
 // block size BS of 8, 16 or 32 token slots.
-// K: the chunk lands whole at k[b][h][chunk][o][0..7] (16 contiguous bytes).
+// K: a token's chunk lands at k[b][h][chunk][o][0..7] (16 contiguous bytes;
+// the 8 slots of an aligned group make 128 contiguous bytes).
 // V: its 8 elements land at v[b][h][o/8][d][o%8], 8 consecutive slots of one
-// dimension per 16 bytes.  When the 8 tokens t..t+7 fill one aligned 8-slot
-// group (slot of t a multiple of 8, slots consecutive: the usual case for a
-// prefill chunk), the lane of token t gathers their 8 rows and writes 8 whole
-// 16-byte groups; the lanes of t+1..t+7 leave V to it.  Any other token (a
-// decode step's single tokens, a group only partly in the batch) writes its
-// 8 elements one by one.  Lead and members test the same 8 slot entries, so
-// every element is written exactly once.
+// dimension per 16 bytes.
+// When the 8 tokens t..t+7 fill one aligned 8-slot group (slot of t a
+// multiple of 8, slots consecutive: the usual case for a prefill chunk), the
+// lane of token t gathers their 8 K and 8 V rows and writes 128 contiguous
+// bytes of each pool; the lanes of t+1..t+7 leave the group to it.  Any other
+// token (a decode step's single tokens, a group only partly in the batch)
+// writes its own K chunk and its 8 V elements one by one.  Lead and members
+// test the same 8 slot entries, so every element is written exactly once.
+// Round trips: the slot with the lane's own rows, then the group's 8 slots
+// (all in flight together), then, for a group's lead, the other 7 rows.
 template <int D, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const half_t* __restrict__ k, const half_t* __restrict__ v, half_t* __restrict__ k_cache,
@@ -42,43 +46,66 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int rem = (int)(idx - t * per_token);
   const int h = rem / kChunks;
   const int c = rem - h * kChunks;
+  const int64_t row = (int64_t)num_kv_heads * D;  // elements per token of k and v
+  const int64_t src = t * row + h * D + c * kChunk;
+
   const int64_t slot = slot_mapping[t];
+  const half8_t kv = *reinterpret_cast<const half8_t*>(k + src);
+  const half8_t vv = *reinterpret_cast<const half8_t*>(v + src);
+  // Empty asm uses keep each load at the top, all in flight together; the
+  // compiler would otherwise sink a load into the branch that first needs it.
+  asm volatile("" ::"v"(slot), "v"(kv), "v"(vv));
   if (slot < 0 || slot >= num_blocks * BS) return;
   const int64_t b = slot / BS;
   const int o = (int)(slot - b * BS);
-  const int64_t row = (int64_t)num_kv_heads * D;  // elements per token of k and v
-  const int64_t src = t * row + h * D + c * kChunk;
   const int64_t tile = (b * num_kv_heads + h) * (int64_t)(BS * D);
 
-  const half8_t kv = *reinterpret_cast<const half8_t*>(k + src);
-  *reinterpret_cast<half8_t*>(k_cache + tile + ((int64_t)c * BS + o) * kChunk) = kv;
-
-  // the aligned 8-slot group of this token, and whether tokens lead..lead+7
-  // fill it in order
+  // the aligned 8-slot group of this token is tokens lead .. lead+7; it is
+  // whole when they hold slots slot-o8 .. slot-o8+7 in order (a token outside
+  // the batch reads -1, which never matches since slot - o8 >= 0)
   const int o8 = (int)(slot % kChunk);
   const int64_t lead = t - o8;
-  bool whole = lead >= 0 && lead + kChunk <= num_tokens;
-  if (whole) {
+  int64_t grp[kChunk];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) whole = whole && slot_mapping[lead + i] == slot - o8 + i;
+  for (int i = 0; i < kChunk; ++i) {
+    const int64_t u = lead + i;
+    const int64_t uc = u < 0 ? 0 : (u >= num_tokens ? num_tokens - 1 : u);
+    grp[i] = slot_mapping[uc];
+    if (u != uc) grp[i] = -1;
   }
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) asm volatile("" ::"v"(grp[i]));
+  int mismatch = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) mismatch |= (int)(grp[i] != slot - o8 + i);
+
+  half_t* kdst = k_cache + tile + ((int64_t)c * BS + o) * kChunk;
   // dims c*8 .. c*8+7 of the 8-slot group start here
   half_t* vgrp = v_cache + tile + ((int64_t)(o / kChunk) * D + c * kChunk) * kChunk;
-  if (whole) {
+  if (mismatch == 0) {
     if (o8 != 0) return;  // the group's first token writes it
-    half8_t rows[kChunk];
+    half8_t krows[kChunk], vrows[kChunk];
+    krows[0] = kv;
+    vrows[0] = vv;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) rows[i] = *reinterpret_cast<const half8_t*>(v + src + i * row);
+    for (int i = 1; i < kChunk; ++i) {
+      krows[i] = *reinterpret_cast<const half8_t*>(k + src + i * row);
+      vrows[i] = *reinterpret_cast<const half8_t*>(v + src + i * row);
+    }
+#pragma unroll
+    for (int i = 1; i < kChunk; ++i) asm volatile("" ::"v"(krows[i]), "v"(vrows[i]));
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) reinterpret_cast<half8_t*>(kdst)[i] = krows[i];
 #pragma unroll
     for (int e = 0; e < kChunk; ++e) {
       half8_t col;
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) col[i] = rows[i][e];
+      for (int i = 0; i < kChunk; ++i) col[i] = vrows[i][e];
       *reinterpret_cast<half8_t*>(vgrp + e * kChunk) = col;
     }
     return;
   }
-  const half8_t vv = *reinterpret_cast<const half8_t*>(v + src);
+  *reinterpret_cast<half8_t*>(kdst) = kv;
 #pragma unroll
   for (int e = 0; e < kChunk; ++e) vgrp[e * kChunk + o8] = vv[e];
 }
