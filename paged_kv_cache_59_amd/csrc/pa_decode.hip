@@ -577,6 +577,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
   // ---- the streamer wave -----------------------------------------------------
   int ring_made = 0;
+  __builtin_amdgcn_s_setprio(1);
   // the streamer is done: the merger finishes what is queued and stops
   auto finish = [&]() { lds_st(&ctl[kCtlDone], 1); };
 

@@ -300,6 +300,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           sacc[rt][kt] = mfma16x16x32(kf[kt][ks], qf[rt][ks], sacc[rt][kt]);
       }
+    __builtin_amdgcn_s_setprio(1);
     read_v(stage);
 
     // raw logits of keys 32 st + 8 j + e, e = 4 kt + i, of this lane's row.
@@ -363,6 +364,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rt][dt] = mfma16x16x32(vf[dt], pf[rt], o[rt][dt]);
+    __builtin_amdgcn_s_setprio(0);
   }
   wait_vm(std::integral_constant<int, 0>{});  // the ring's last copies land before the wave ends
   if (!active) return;
