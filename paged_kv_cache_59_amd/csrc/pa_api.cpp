@@ -3,6 +3,7 @@
 // memory.  The operations and their sources are described in include/pa.h.
 #include "pa.h"
 
+#include <atomic>
 #include <cmath>
 
 #include "pa_internal.h"
@@ -20,18 +21,22 @@ bool block_size_supported(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Decode workers for the current device: kWorkersPerCU per compute unit,
-// rounded up to a multiple of 8 (the XCD count).  Cached per device.
+// rounded up to a multiple of 8 (the XCD count).  Cached per device; calls
+// from several threads may each fill an entry, with the same value.
 int32_t auto_workers() {
-  static int32_t cache[64] = {0};
+  static std::atomic<int32_t> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev >= 0 && dev < 64) {
+    const int32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return PA_ERR_HIP;
   const int32_t w = ((cus * pa::kWorkersPerCU + 7) / 8) * 8;
-  if (dev >= 0 && dev < 64) cache[dev] = w;
+  if (dev >= 0 && dev < 64) cache[dev].store(w, std::memory_order_relaxed);
   return w;
 }
 

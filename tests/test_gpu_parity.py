@@ -75,6 +75,15 @@ def test_stale_tails():
     run_case(w, 0, "stale tails")
 
 
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128), 0.0, -8.0 / np.sqrt(128)])
+def test_negative_and_zero_scale(scale):
+    """The scale multiplies the logits before the running max, so a negative
+    one needs no special case; a zero one makes every weight equal (the
+    output is the plain mean of the V rows)."""
+    w = wl.make_workload("scale", 207, 32, 8, 128, len_range=(1, 700), num_seqs=8, scale=scale)
+    run_case(w, 24, f"scale {scale}")
+
+
 def test_peaky_softmax():
     """scale x 8: weights close to one-hot, the running max moves a lot."""
     w = wl.make_workload("peaky", 203, 32, 8, 128, len_range=(100, 900), num_seqs=8,
