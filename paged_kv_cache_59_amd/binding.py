@@ -25,7 +25,7 @@ PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
-            "pa_decode_timed",
+            "pa_decode_timed", "pa_decode_append", "pa_decode_append_timed",
             "pa_prefill", "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_decode_timed.argtypes = L.pa_decode.argtypes + [vp, vp]
     L.pa_decode_timed.restype = ctypes.c_int
+    L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
+                                   i32, i32, i32, i32, i64, i32, i32, vp, sz, vp]
+    L.pa_decode_append.restype = ctypes.c_int
+    L.pa_decode_append_timed.argtypes = L.pa_decode_append.argtypes + [vp, vp]
+    L.pa_decode_append_timed.restype = ctypes.c_int
     L.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32, i32, i32,
                              i32, i32, i64, i32, i32, vp]
     L.pa_prefill.restype = ctypes.c_int
@@ -208,6 +213,60 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
         if not start.cuda_event or not stop.cuda_event:
             raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
         _check(lib().pa_decode_timed(*args, start.cuda_event, stop.cuda_event), "pa_decode_timed")
+    return out
+
+
+def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                     context_lens, scale, num_kv_heads, max_context_len=None, num_workers=0,
+                     workspace=None, stream=None, kernel_events=None):
+    """Append each sequence's new token and decode, in one launch: the same
+    results as pa_reshape_and_cache(k_new, v_new, k_cache, v_cache,
+    slot_mapping) followed by pa_decode(...), when token s is sequence s's
+    token at position context_lens[s] - 1 and slot_mapping[s] is that
+    position's slot (negative: attended, not stored).  k_new and v_new are
+    [num_seqs, Hkv, D] fp16; the other arguments as pa_decode."""
+    _dev(out, "out", torch.float16)
+    _dev(q, "q", torch.float16)
+    _dev(k_new, "k_new", torch.float16)
+    _dev(v_new, "v_new", torch.float16)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_cache, "k_cache", torch.float16)
+    _dev(v_cache, "v_cache", torch.float16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if hkv != int(num_kv_heads):
+        raise ValueError("num_kv_heads does not match k_cache")
+    S, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if slot_mapping.numel() != S:
+        raise ValueError("slot_mapping must be [num_seqs]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], context_lens [num_seqs]")
+    mb = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = mb * bs
+    if workspace is None:
+        workspace = new_workspace(S, hkv, d, int(max_context_len), num_workers, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    args = (out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+            slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv, S, hq, d, bs, mb,
+            nb, int(max_context_len), int(num_workers), workspace.data_ptr(), workspace.numel(),
+            _stream(q, stream))
+    if kernel_events is None:
+        _check(lib().pa_decode_append(*args), "pa_decode_append")
+    else:
+        start, stop = kernel_events
+        if not start.cuda_event or not stop.cuda_event:
+            raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
+        _check(lib().pa_decode_append_timed(*args, start.cuda_event, stop.cuda_event),
+               "pa_decode_append_timed")
     return out
 
 

@@ -135,13 +135,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, w);
 }
 
-int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, float scale,
-                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                    int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream,
-                    hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+}  // extern "C"
+
+namespace {
+
+// Decode, and with k_new non-null the fused append (see pa_decode_append).
+int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                const int64_t* slot_mapping, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                int32_t max_context_len, int32_t num_workers, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, hipEvent_t kernel_start,
+                hipEvent_t kernel_stop) {
+  const bool fused = k_new || v_new || slot_mapping;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || !std::isfinite(scale))
     return PA_ERR_INVALID_ARG;
@@ -154,6 +161,9 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
   if (num_workers < 0 || num_workers > pa::kMaxWorkers) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  // the fused append reads the new K rows as 4-byte pieces
+  if (fused && (!k_new || !v_new || !slot_mapping || (reinterpret_cast<uintptr_t>(k_new) & 3)))
     return PA_ERR_INVALID_ARG;
   // one launch takes at most kMaxSeqsPerLaunch sequences; its 64-token units
   // (all heads) must fit a 32-bit index
@@ -191,11 +201,79 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
     a.block_tables = block_tables + s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
     a.num_seqs = (int)n;
+    if (fused) {
+      const int64_t rows = s0 * num_kv_heads * head_dim;
+      a.k_new = static_cast<const pa::half_t*>(k_new) + rows;
+      a.v_new = static_cast<const pa::half_t*>(v_new) + rows;
+      a.slot_mapping = slot_mapping + s0;
+      a.k_cache_w = const_cast<pa::half_t*>(a.k_cache);
+      a.v_cache_w = const_cast<pa::half_t*>(a.v_cache);
+    }
     hipEvent_t start = s0 == 0 ? kernel_start : nullptr;
     hipEvent_t stop = s0 + n >= num_seqs ? kernel_stop : nullptr;
     if (pa::launch_decode(a, stream, start, stop) != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+  return decode_impl(out, q, nullptr, nullptr, nullptr, k_cache, v_cache, block_tables,
+                     context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
+                     workspace, workspace_bytes, stream, kernel_start, kernel_stop);
+}
+
+int pa_decode_append_timed(void* out, const void* q, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  // One launch only while there is at most one row to append per worker:
+  // every stored row stalls its worker's stream for a few microseconds,
+  // which more rows per worker cost more than the second launch saves.
+  const int32_t w = resolve_workers(num_workers);
+  if (w < 0) return w;
+  if ((int64_t)num_seqs * num_kv_heads > w) {
+    const int e = pa_reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs,
+                                       num_kv_heads, head_dim, block_size, num_blocks, stream);
+    if (e != PA_OK) return e;
+    return decode_impl(out, q, nullptr, nullptr, nullptr, k_cache, v_cache, block_tables,
+                       context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
+                       workspace, workspace_bytes, stream, kernel_start, kernel_stop);
+  }
+  return decode_impl(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                     context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
+                     workspace, workspace_bytes, stream, kernel_start, kernel_stop);
+}
+
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return pa_decode_append_timed(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                                num_q_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                max_context_len, num_workers, workspace, workspace_bytes, stream,
+                                nullptr, nullptr);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -162,7 +162,7 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 
 }  // namespace
 
-template <int D, int BS>
+template <int D, int BS, bool Fused>
 __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
@@ -387,6 +387,27 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       *reinterpret_cast<half8_t*>(q_lds + q_row * kQRow + q_chunk * kChunk) = v;
     }
   };
+  // Fused append: the new token of sequence s sits at position len - 1.  The
+  // units attend to positions < len - 1 from the pools; the piece that ends
+  // the run folds the new row in from k_new / v_new and stores it into its
+  // slot.  The rows of a unit's run (and the slot) are loaded with the
+  // unit's K in every iteration, whether or not the unit ends its run, so
+  // that every iteration issues the same loads.  The stores are scattered
+  // partial-line writes, slow to complete; a wave's memory operations
+  // complete in order, so each holds back the loads issued after it (the
+  // host fuses only batches with at most one appended row per worker).  Lane l holds dims 2l, 2l+1
+  // of the K row (lanes past D/2 take no part) and dims 64 st + l of the V row.
+  const int kn_dim = (2 * lane) % D;
+  const bool kn_lane = 2 * lane < D;
+  auto load_new = [&](const Cursor& c, uint32_t& kn, half_t (&vn)[kSets], int64_t& slot) {
+    if constexpr (Fused) {
+      const int64_t row = ((int64_t)c.s * Hkv + c.h) * D;
+      kn = *reinterpret_cast<const uint32_t*>(a.k_new + row + kn_dim);
+#pragma unroll
+      for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
+      slot = a.slot_mapping[c.s];
+    }
+  };
 
   // ---- merge of a cut run ----------------------------------------------------
   // Run r = (s, kvh) holds units [u0, u0 + n); its pieces are its overlaps
@@ -597,7 +618,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // keep the prologue in loop order (all K loads, then all V loads): the
   // wait counts at the loop head are merged over both ways in
   __builtin_amdgcn_sched_barrier(0);
+  uint32_t kn_cur = 0, kn_nxt = 0;
+  half_t vn_cur[kSets] = {}, vn_nxt[kSets] = {};
+  int64_t slot_cur = -1, slot_nxt = -1;
   load_k(cur, tbl_cur);
+  load_new(cur, kn_cur, vn_cur, slot_cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, pb_cur);
   __builtin_amdgcn_sched_barrier(0);
@@ -609,6 +634,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
   while (cur.valid) {
     const int t0 = cur.g * kGroupTokens;
+    // positions the pools supply (a fused append supplies the last one)
+    const int vis = Fused ? cur.len - 1 : cur.len;
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.
@@ -631,19 +658,23 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     blocks_of(tbl_nxt, pb_nxt);
     load_k(nxt, tbl_nxt);
     load_q(nxt);
+    load_new(nxt, kn_nxt, vn_nxt, slot_nxt);
     // the unit after nxt2, computed while this unit's V is in flight
     const Cursor nxt3 = next(nxt2);
 
     // online softmax over these 64 positions
-    const bool live = (t0 + lane) < cur.len;
+    const bool live = (t0 + lane) < vis;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       half_t ph = (half_t)0.0f;
       if (g < G) {
         const float z = live ? sacc[g] * a.scale_log2 : -INFINITY;
         const float m_new = fmaxf(m_run[g], wave_max(z));
-        const float alpha = fast_exp2(m_run[g] - m_new);
-        ph = (half_t)fast_exp2(z - m_new);
+        // a fused append's run can end in a unit with no pool position: a
+        // piece of that unit alone has no max yet (exponentials then 0)
+        const float m_ref = (Fused && m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run[g] - m_ref);
+        ph = (half_t)fast_exp2(z - m_ref);
         l_lane[g] = l_lane[g] * alpha + (float)ph;
 #pragma unroll
         for (int st = 0; st < kSets; ++st) acc_o[st][g] *= alpha;
@@ -654,12 +685,12 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
     // positions past the end (tail of the last block, and re-read blocks past
     // it) in the sequence's last unit: V element := 0
-    if (t0 + kGroupTokens > cur.len) {
+    if (t0 + kGroupTokens > vis) {
 #pragma unroll
       for (int g = 0; g < 8; ++g)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
-          const bool dead = t0 + g * kChunk + e >= cur.len;
+          const bool dead = t0 + g * kChunk + e >= vis;
 #pragma unroll
           for (int st = 0; st < kSets; ++st) vreg[g][st][e] = dead ? (half_t)0.0f : vreg[g][st][e];
         }
@@ -685,6 +716,52 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
     // ---- end of a piece: the run or the share ends ------------------------
     const bool run_end = cur.g + 1 == cur.n_s;
+    if constexpr (Fused) {
+      if (run_end) {
+        // the new token: logits q_g . k_new (q rows of this run are in LDS),
+        // folded in with the running-max rescale
+        float zn[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          zn[g] = -INFINITY;
+          if (g < G) {
+            const half_t* qr = q_lds + g * kQRow + kn_dim;
+            const half_t k0 = __builtin_bit_cast(half_t, (uint16_t)(kn_cur & 0xffffu));
+            const half_t k1 = __builtin_bit_cast(half_t, (uint16_t)(kn_cur >> 16));
+            const float part = kn_lane ? (float)qr[0] * (float)k0 + (float)qr[1] * (float)k1 : 0.0f;
+            zn[g] = wave_sum(part) * a.scale_log2;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (g < G) {
+            const float m_new = fmaxf(m_run[g], zn[g]);
+            const float alpha = fast_exp2(m_run[g] - m_new);  // 0 when no position came before
+            const float pn = fast_exp2(zn[g] - m_new);
+            l_lane[g] = l_lane[g] * alpha + (lane == 0 ? pn : 0.0f);
+#pragma unroll
+            for (int st = 0; st < kSets; ++st)
+              acc_o[st][g] = acc_o[st][g] * alpha + pn * (float)vn_cur[st];
+            m_run[g] = m_new;
+          }
+        }
+        // the append: K row as 4-byte pieces at [chunk][slot][8], V elements
+        // at [slot / 8][dim][slot % 8]
+        const int64_t slot = (int64_t)__builtin_amdgcn_readfirstlane((int)(slot_cur & 0xffffffff)) |
+                             ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot_cur >> 32)) << 32);
+        if (slot >= 0 && slot < a.num_blocks * BS) {
+          const int64_t b = slot / BS;
+          const int o = (int)(slot - b * BS);
+          const int64_t tile = (b * Hkv + cur.h) * kTile;
+          if (kn_lane)
+            *reinterpret_cast<uint32_t*>(a.k_cache_w + tile + ((kn_dim / kChunk) * BS + o) * kChunk +
+                                         kn_dim % kChunk) = kn_cur;
+#pragma unroll
+          for (int st = 0; st < kSets; ++st)
+            a.v_cache_w[tile + ((o / kChunk) * D + st * 64 + lane) * kChunk + o % kChunk] = vn_cur[st];
+        }
+      }
+    }
     if (run_end || !nxt.valid) {
       float l_tot[4];
 #pragma unroll
@@ -738,6 +815,12 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     cur = nxt;
     nxt = nxt2;
     tbl_nxt = tbl_nxt2;
+    if constexpr (Fused) {
+      kn_cur = kn_nxt;
+#pragma unroll
+      for (int st = 0; st < kSets; ++st) vn_cur[st] = vn_nxt[st];
+      slot_cur = slot_nxt;
+    }
     nxt2 = nxt3;
     __builtin_amdgcn_wave_barrier();
   }
@@ -785,14 +868,23 @@ DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int6
   return w;
 }
 
-template <int D, int BS>
-void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+template <int D, int BS, bool Fused>
+void launch_decode_f(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
   const uint32_t lds = (uint32_t)((size_t)a.num_seqs * 2 * sizeof(int));
   if (!start && !stop)
-    hipLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(128), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, Fused>), grid, dim3(128), lds, stream, a);
   else  // the events take the kernel's own start and end times
-    hipExtLaunchKernelGGL((decode_kernel<D, BS>), grid, dim3(128), lds, stream, start, stop, 0, a);
+    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused>), grid, dim3(128), lds, stream, start, stop,
+                          0, a);
+}
+
+template <int D, int BS>
+void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (a.k_new)
+    launch_decode_f<D, BS, true>(a, stream, start, stop);
+  else
+    launch_decode_f<D, BS, false>(a, stream, start, stop);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,

@@ -74,6 +74,15 @@ struct DecodeArgs {
   int max_context_len;
   int num_workers;        // grid size: persistent workgroups sharing the work
   DecodeWorkspace ws;
+  // Fused append (null when plain decode): token s's new K and V rows
+  // ([S][Hkv][D]), its slot, and writable views of the pools.  Position
+  // context_lens[s] - 1 is then taken from these rows, not from the pools,
+  // and the rows are stored into the slot.
+  const half_t* k_new;
+  const half_t* v_new;
+  const int64_t* slot_mapping;
+  half_t* k_cache_w;
+  half_t* v_cache_w;
 };
 
 // One launch over a.num_seqs <= kMaxSeqsPerLaunch sequences.  Non-null
