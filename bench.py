@@ -439,11 +439,9 @@ def main():
         del scratch
 
     ms_per_step = wall * 1e3 / args.steps
-    # pa_decode_append runs as one launch when the batch has at most one row
-    # to append per worker, else as the append kernel and the decode kernel.
     # One launch reads each new row once (for the attention and the store)
     # and writes it once; two launches read it twice.
-    fused = not args.separate and w.num_seqs * w.num_kv_heads <= workers
+    fused = not args.separate
     kernel_bytes = w.decode_bytes() + (w.append_bytes() // 2 if fused else 0)
     step_bytes = w.decode_bytes() + w.copy_bytes() + (
         w.append_bytes() // 2 if fused else w.append_bytes())

@@ -222,8 +222,7 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  * "TL;DR": one new K and V entry per sequence, then attention over the whole
  * cache) and slot_mapping[s] is the slot the block table gives that position.
  *
- *   k_new, v_new   fp16 [num_seqs][num_kv_heads][head_dim]; k_new 4-byte
- *                  aligned
+ *   k_new, v_new   fp16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
  *   slot_mapping   int64 [num_seqs]: the slot of token s; negative (or past
  *                  the pool) = the row is attended but not stored
  *   the rest       as pa_decode; k_cache and v_cache are written (the new
@@ -234,13 +233,12 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  * with context length 0 appends nothing and gets a zero row.  Errors as
  * pa_decode, and PA_ERR_INVALID_ARG for a null or misaligned new row.
  *
- * Each stored row stalls the worker that stores it for a few microseconds
- * (scattered partial-line writes, in the worker's in-order memory queue).
- * The call therefore runs as one launch only when num_seqs * num_kv_heads
- * is at most the worker count; larger batches run as the append kernel
- * followed by the decode kernel, with the same results.  Measured on MI355X
- * (Llama-3.1-8B layer, 64 sequences): 60.1 us per step in one launch against
- * 62.7 us in two.
+ * One launch: each worker stores the new rows of the runs that end in its
+ * share after its last unit (scattered partial-line writes, slow to
+ * complete; a worker's memory operations complete in order, so inside its
+ * stream they would hold back its K/V loads).  Measured on MI355X
+ * (Llama-3.1-8B layer, 64 sequences): 59.1 us per step, against 62.7 us for
+ * pa_reshape_and_cache then pa_decode.
  */
 int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
                      const int64_t* slot_mapping, void* k_cache, void* v_cache,
@@ -250,8 +248,7 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* pa_decode_append with the kernel-bound timing events of pa_decode_timed
- * (bound to the decode kernel when the call runs as two launches). */
+/* pa_decode_append with the kernel-bound timing events of pa_decode_timed. */
 int pa_decode_append_timed(void* out, const void* q, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, void* k_cache, void* v_cache,
                            const int32_t* block_tables, const int32_t* context_lens, float scale,

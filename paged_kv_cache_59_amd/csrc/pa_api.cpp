@@ -162,8 +162,9 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
-  // the fused append reads the new K rows as 4-byte pieces
-  if (fused && (!k_new || !v_new || !slot_mapping || (reinterpret_cast<uintptr_t>(k_new) & 3)))
+  // the fused append moves the new rows in 16-byte pieces
+  if (fused && (!k_new || !v_new || !slot_mapping || (reinterpret_cast<uintptr_t>(k_new) & 15) ||
+                (reinterpret_cast<uintptr_t>(v_new) & 15)))
     return PA_ERR_INVALID_ARG;
   // one launch takes at most kMaxSeqsPerLaunch sequences; its 64-token units
   // (all heads) must fit a 32-bit index
@@ -242,20 +243,6 @@ int pa_decode_append_timed(void* out, const void* q, const void* k_new, const vo
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
-  // One launch only while there is at most one row to append per worker:
-  // every stored row stalls its worker's stream for a few microseconds,
-  // which more rows per worker cost more than the second launch saves.
-  const int32_t w = resolve_workers(num_workers);
-  if (w < 0) return w;
-  if ((int64_t)num_seqs * num_kv_heads > w) {
-    const int e = pa_reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs,
-                                       num_kv_heads, head_dim, block_size, num_blocks, stream);
-    if (e != PA_OK) return e;
-    return decode_impl(out, q, nullptr, nullptr, nullptr, k_cache, v_cache, block_tables,
-                       context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
-                       block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
-                       workspace, workspace_bytes, stream, kernel_start, kernel_stop);
-  }
   return decode_impl(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                      context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
                      block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,

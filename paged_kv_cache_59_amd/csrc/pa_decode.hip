@@ -389,23 +389,70 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   };
   // Fused append: the new token of sequence s sits at position len - 1.  The
   // units attend to positions < len - 1 from the pools; the piece that ends
-  // the run folds the new row in from k_new / v_new and stores it into its
-  // slot.  The rows of a unit's run (and the slot) are loaded with the
-  // unit's K in every iteration, whether or not the unit ends its run, so
-  // that every iteration issues the same loads.  The stores are scattered
-  // partial-line writes, slow to complete; a wave's memory operations
-  // complete in order, so each holds back the loads issued after it (the
-  // host fuses only batches with at most one appended row per worker).  Lane l holds dims 2l, 2l+1
+  // the run folds the new row in from k_new / v_new.  The rows of a unit's
+  // run are loaded with the unit's K in every iteration, whether or not the
+  // unit ends its run, so that every iteration issues the same loads.  Lane l holds dims 2l, 2l+1
   // of the K row (lanes past D/2 take no part) and dims 64 st + l of the V row.
   const int kn_dim = (2 * lane) % D;
   const bool kn_lane = 2 * lane < D;
-  auto load_new = [&](const Cursor& c, uint32_t& kn, half_t (&vn)[kSets], int64_t& slot) {
+  auto load_new = [&](const Cursor& c, uint32_t& kn, half_t (&vn)[kSets]) {
     if constexpr (Fused) {
       const int64_t row = ((int64_t)c.s * Hkv + c.h) * D;
       kn = *reinterpret_cast<const uint32_t*>(a.k_new + row + kn_dim);
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
-      slot = a.slot_mapping[c.s];
+    }
+  };
+  // The stores of the new rows, after the worker's last unit: scattered
+  // partial-line writes are slow to complete, and a wave's memory operations
+  // complete in order, so inside the loop each would hold back the K/V loads
+  // issued after it.  The runs whose last unit lies in this worker's share
+  // [first, end) are walked in order and stored 4 at a time: lane 16 i + c
+  // moves 16-byte chunk c (8 dims) of the i-th run's K and V rows, K to
+  // [chunk][slot][8], V as 8 elements at [slot / 8][dim][slot % 8].
+  auto store_new_rows = [&]() {
+    if constexpr (Fused) {
+      const int first = sb(w), end = sb(w + 1);
+      const int ch = lane & 15;
+      int my_s = -1, my_h = 0, grp = 0;
+      auto flush = [&]() {
+        if (my_s >= 0 && ch < kChunks) {
+          const int64_t slot = a.slot_mapping[my_s];
+          const int64_t row = ((int64_t)my_s * Hkv + my_h) * D + ch * kChunk;
+          const half8_t kr = *reinterpret_cast<const half8_t*>(a.k_new + row);
+          const half8_t vr = *reinterpret_cast<const half8_t*>(a.v_new + row);
+          if (slot >= 0 && slot < a.num_blocks * BS) {
+            const int64_t b = slot / BS;
+            const int o = (int)(slot - b * BS);
+            const int64_t tile = (b * Hkv + my_h) * kTile;
+            *reinterpret_cast<half8_t*>(a.k_cache_w + tile + ((int64_t)ch * BS + o) * kChunk) = kr;
+            half_t* vp = a.v_cache_w + tile + ((int64_t)(o / kChunk) * D + ch * kChunk) * kChunk +
+                         o % kChunk;
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) vp[e * kChunk] = vr[e];
+          }
+        }
+        my_s = -1;
+        grp = 0;
+      };
+      Cursor c = locate(first);
+      while (true) {
+        const int run0 = Hkv * uniform(off_lds[c.s]) + c.h * c.n_s;  // the run's first unit
+        if (run0 >= end) break;
+        const int last = run0 + c.n_s - 1;
+        if (last >= first && last < end) {
+          if ((lane >> 4) == grp) {
+            my_s = c.s;
+            my_h = c.h;
+          }
+          if (++grp == 4) flush();
+        }
+        if (run0 + c.n_s >= end) break;  // no further run starts in the share
+        c.g = c.n_s - 1;  // step to the next run
+        c.left = 2;
+        c = step(c);
+      }
+      if (grp > 0) flush();
     }
   };
 
@@ -620,9 +667,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   uint32_t kn_cur = 0, kn_nxt = 0;
   half_t vn_cur[kSets] = {}, vn_nxt[kSets] = {};
-  int64_t slot_cur = -1, slot_nxt = -1;
   load_k(cur, tbl_cur);
-  load_new(cur, kn_cur, vn_cur, slot_cur);
+  load_new(cur, kn_cur, vn_cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, pb_cur);
   __builtin_amdgcn_sched_barrier(0);
@@ -658,7 +704,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     blocks_of(tbl_nxt, pb_nxt);
     load_k(nxt, tbl_nxt);
     load_q(nxt);
-    load_new(nxt, kn_nxt, vn_nxt, slot_nxt);
+    load_new(nxt, kn_nxt, vn_nxt);
     // the unit after nxt2, computed while this unit's V is in flight
     const Cursor nxt3 = next(nxt2);
 
@@ -745,21 +791,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
             m_run[g] = m_new;
           }
         }
-        // the append: K row as 4-byte pieces at [chunk][slot][8], V elements
-        // at [slot / 8][dim][slot % 8]
-        const int64_t slot = (int64_t)__builtin_amdgcn_readfirstlane((int)(slot_cur & 0xffffffff)) |
-                             ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot_cur >> 32)) << 32);
-        if (slot >= 0 && slot < a.num_blocks * BS) {
-          const int64_t b = slot / BS;
-          const int o = (int)(slot - b * BS);
-          const int64_t tile = (b * Hkv + cur.h) * kTile;
-          if (kn_lane)
-            *reinterpret_cast<uint32_t*>(a.k_cache_w + tile + ((kn_dim / kChunk) * BS + o) * kChunk +
-                                         kn_dim % kChunk) = kn_cur;
-#pragma unroll
-          for (int st = 0; st < kSets; ++st)
-            a.v_cache_w[tile + ((o / kChunk) * D + st * 64 + lane) * kChunk + o % kChunk] = vn_cur[st];
-        }
       }
     }
     if (run_end || !nxt.valid) {
@@ -819,13 +850,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       kn_cur = kn_nxt;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn_cur[st] = vn_nxt[st];
-      slot_cur = slot_nxt;
     }
     nxt2 = nxt3;
     __builtin_amdgcn_wave_barrier();
   }
 
   finish();
+  store_new_rows();
 }
 
 namespace {

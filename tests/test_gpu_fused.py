@@ -54,9 +54,8 @@ def run_fused(w, num_workers=0, label=""):
 @pytest.mark.parametrize("workers", [0, 1, 7, 64, 5000])
 def test_fused_shapes_and_work_splits(Hq, Hkv, D, workers):
     """workers = 5000: every unit its own share, so a run of length 64k + 1
-    ends in a piece holding the new token only.  With fewer workers than
-    rows to append (1, 7, and 64 for 8 KV heads) the call runs as two
-    launches; the results must not tell the two apart."""
+    ends in a piece holding the new token only; workers = 1: one worker
+    stores every row after its last unit."""
     w = wl.make_workload("fused", 300 + Hq + D, Hq, Hkv, D, context_lens=FUSED_LENS)
     run_fused(w, workers, f"fused Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
 
@@ -114,8 +113,8 @@ def test_fused_matches_separate_calls_bit_for_bit():
     tolerance (the new token's weight enters in fp32 in the fused path)."""
     w = wl.make_workload("fused-vs", 343, 32, 8, 128, len_range=(1, 900), num_seqs=24)
     d1, d2 = to_device(w), to_device(w)
-    a = gpu_step(w, d1, 256)
-    b = fused_step(w, d2, 256)  # 24 x 8 rows <= 256 workers: one launch
+    a = gpu_step(w, d1, 64)
+    b = fused_step(w, d2, 64)
     # bit patterns (the unaddressed tail slots hold NaN canaries)
     for pool in ("k_cache", "v_cache"):
         assert torch.equal(d1[pool].view(torch.int16), d2[pool].view(torch.int16)), pool
