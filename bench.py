@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--probe-gib", type=float, default=4.0,
+                    help="read-bandwidth probe size (0: skip the probe)")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="decode: a third pass of kernel timings, each step preceded by a write "
                          "of this many MB of scratch (flushes L2 and the Infinity Cache); 0 = skip")
@@ -96,6 +98,33 @@ def measured_traffic(workload, fused):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
         return None
     return int(round(rec["traffic_bytes_per_dispatch"]))
+
+
+def achievable_read(torch, pk, gib, reps=5):
+    """HBM read rates the probe reaches on this device (GB/s): a sequential
+    read of `gib` GiB, and the same bytes as 4 KiB tiles in a shuffled
+    order (the gather pattern of the block tables); kernel-bound events,
+    mean over `reps` launches each."""
+    n = int(gib * (1 << 30))
+    buf = torch.full((n,), 1, dtype=torch.uint8, device="cuda")  # pages written once before
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    order = torch.from_numpy(np.random.default_rng(5).permutation(n // 4096).astype(np.int32)).cuda()
+    rates = []
+    for tiles in (None, order):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps + 1)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for e in ev:  # the first launch warms up
+            pk.pa_read_probe(buf, sink, tiles, 4096, kernel_events=e)
+        torch.cuda.synchronize()
+        ms = np.mean([a.elapsed_time(b) for a, b in ev[1:]])
+        rates.append(n / (ms * 1e-3) / 1e9)
+    del buf, order
+    torch.cuda.empty_cache()
+    return rates
 
 
 def cpu_model():
@@ -438,6 +467,7 @@ def main():
         flushed_ms = np.array([a.elapsed_time(b) for a, b in fev])
         del scratch
 
+    probe = achievable_read(torch, pk, args.probe_gib) if args.probe_gib > 0 else None
     ms_per_step = wall * 1e3 / args.steps
     # One launch reads each new row once (for the attention and the store)
     # and writes it once; two launches read it twice.
@@ -487,6 +517,11 @@ def main():
             "flushed_mean_us": (None if flushed_ms is None
                                 else round(float(flushed_ms.mean()) * 1e3, 3)),
             "flush_mb": args.flush_mb,
+            "achievable": (None if probe is None else {
+                "sequential_gbs": round(probe[0], 1), "tiles_4k_gbs": round(probe[1], 1),
+                "probe": f"pa_read_probe over {args.probe_gib:g} GiB, 16-byte non-temporal "
+                         "loads; 4 KiB tiles in a shuffled order for the second rate"}),
+            "frac_of_achievable": (None if probe is None else round(achieved / probe[1], 4)),
             "call_frac": round(kernel_bytes / (float(call_ms.mean()) * 1e-3) / 1e9
                                / HBM_PEAK_GBS, 4),
         },

@@ -259,6 +259,27 @@ int pa_decode_append_timed(void* out, const void* q, const void* k_new, const vo
                            hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /*
+ * Read-bandwidth probe, for measurement: the HBM read rate this device
+ * reaches with the loads the decode kernel issues (16-byte non-temporal
+ * vector loads), to read a kernel's rate against it beside the part's
+ * nominal peak.  Not part of the decode path.
+ *
+ *   buf, bytes     device buffer, 16-byte aligned, bytes a multiple of 16
+ *   tile_order     NULL: read buf once, sequentially.  Else int32
+ *                  [num_tiles] on the device: read tiles of tile_bytes
+ *                  (a multiple of 16) at byte offsets tile_order[t] *
+ *                  tile_bytes, in that order (an entry outside buf reads
+ *                  tile 0)
+ *   sink           device uint32, zeroed by the caller: receives the XOR of
+ *                  every 32-bit word read, so no read is skipped
+ *   kernel_start/stop  optional timing events bound to the kernel, as in
+ *                  pa_decode_timed
+ */
+int pa_read_probe(const void* buf, int64_t bytes, const int32_t* tile_order, int64_t num_tiles,
+                  int32_t tile_bytes, uint32_t* sink, hipStream_t stream, hipEvent_t kernel_start,
+                  hipEvent_t kernel_stop);
+
+/*
  * Multi-query paged attention: each sequence's chunk of new query tokens
  * attends causally to its paged context -- chunked prefill ("KV Cache in
  * Serving Engines", section 3 "New Problem: Long Prefills Pause Decoding")

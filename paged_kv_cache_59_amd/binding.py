@@ -25,7 +25,7 @@ PA_ERR_HIP = -4
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
-            "pa_decode_timed", "pa_decode_append", "pa_decode_append_timed",
+            "pa_decode_timed", "pa_decode_append", "pa_decode_append_timed", "pa_read_probe",
             "pa_prefill", "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.restype = ctypes.c_int
     L.pa_decode_append_timed.argtypes = L.pa_decode_append.argtypes + [vp, vp]
     L.pa_decode_append_timed.restype = ctypes.c_int
+    L.pa_read_probe.argtypes = [vp, i64, vp, i64, i32, vp, vp, vp, vp]
+    L.pa_read_probe.restype = ctypes.c_int
     L.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32, i32, i32,
                              i32, i32, i64, i32, i32, vp]
     L.pa_prefill.restype = ctypes.c_int
@@ -268,6 +270,28 @@ def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block
         _check(lib().pa_decode_append_timed(*args, start.cuda_event, stop.cuda_event),
                "pa_decode_append_timed")
     return out
+
+
+def pa_read_probe(buf, sink, tile_order=None, tile_bytes=4096, stream=None, kernel_events=None):
+    """Read-bandwidth probe: read the uint8 GPU buffer ``buf`` once
+    (sequentially, or the tiles of ``tile_bytes`` that the int32 GPU tensor
+    ``tile_order`` lists, in that order); the int32 GPU tensor ``sink`` (one
+    element, zeroed by the caller) receives the XOR of every 32-bit word
+    read.  ``kernel_events`` as in pa_decode."""
+    _dev(buf, "buf", torch.uint8)
+    _dev(sink, "sink", torch.int32)
+    order, n = None, 0
+    if tile_order is not None:
+        _dev(tile_order, "tile_order", torch.int32)
+        order, n = tile_order.data_ptr(), int(tile_order.numel())
+    ev = (None, None)
+    if kernel_events is not None:
+        start, stop = kernel_events
+        if not start.cuda_event or not stop.cuda_event:
+            raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
+        ev = (start.cuda_event, stop.cuda_event)
+    _check(lib().pa_read_probe(buf.data_ptr(), int(buf.numel()), order, n, int(tile_bytes),
+                               sink.data_ptr(), _stream(buf, stream), *ev), "pa_read_probe")
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,

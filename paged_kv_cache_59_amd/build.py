@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip",
-           "pa_block_manager.cpp"]
+           "pa_probe.hip", "pa_block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

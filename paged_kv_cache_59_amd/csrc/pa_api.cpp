@@ -275,6 +275,22 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                          workspace_bytes, stream, nullptr, nullptr);
 }
 
+int pa_read_probe(const void* buf, int64_t bytes, const int32_t* tile_order, int64_t num_tiles,
+                  int32_t tile_bytes, uint32_t* sink, hipStream_t stream, hipEvent_t kernel_start,
+                  hipEvent_t kernel_stop) {
+  if (!buf || !sink || bytes <= 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
+    return PA_ERR_INVALID_ARG;
+  if (tile_order && (num_tiles <= 0 || tile_bytes < 16 || (tile_bytes & 15) || bytes < tile_bytes ||
+                     num_tiles > ((int64_t)1 << 40) / tile_bytes))
+    return PA_ERR_INVALID_ARG;
+  const int32_t w = auto_workers();  // 2 per compute unit
+  if (w < 0) return w;
+  (void)hipGetLastError();
+  const hipError_t e = pa::launch_read_probe(buf, bytes, tile_order, num_tiles, tile_bytes, sink,
+                                             4 * w, stream, kernel_start, kernel_stop);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int32_t num_tokens, float scale,

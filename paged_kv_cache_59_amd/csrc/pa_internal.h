@@ -85,6 +85,12 @@ struct DecodeArgs {
   half_t* v_cache_w;
 };
 
+// Read-bandwidth probe (sequential when order is null, else num_tiles tiles
+// of tile_bytes in the given order); grid workgroups of 256 lanes.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, const int32_t* order,
+                             int64_t num_tiles, int32_t tile_bytes, uint32_t* sink, int grid,
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 // One launch over a.num_seqs <= kMaxSeqsPerLaunch sequences.  Non-null
 // events are bound to the kernel itself (its start and end times).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
