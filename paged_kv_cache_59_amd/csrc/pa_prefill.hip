@@ -194,38 +194,49 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       nb3 = phys_of(NBS * st + 3);
     }
   };
-  // element offset of block i of the step
-  auto pick = [&](int b0, int b1, int b2, int b3, int i) -> int64_t {
-    const int64_t o0 = (int64_t)b0 * bstride, o1 = (int64_t)b1 * bstride;
-    const int64_t o2 = (int64_t)b2 * bstride, o3 = (int64_t)b3 * bstride;
-    if constexpr (NBS == 1) return o0;
-    else if constexpr (NBS == 2) return i == 0 ? o0 : o1;
-    else return i < 2 ? (i == 0 ? o0 : o1) : (i == 2 ? o2 : o3);
-  };
+  // Per-lane constant parts of the copies (element offsets inside a block's
+  // head tile, and which block of the step a lane's K piece lies in); per
+  // step only the blocks' offsets (uniform, scalar) and a select remain.
+  //   K tile: [chunk c of 8 dims][slot 16 kt + c][8 dims]; slot (kt, c)
+  //           holds key 8 (c / 4) + 4 kt + c % 4 (the MFMA's key order).
+  //   V tile: [8-key group jj][dim][8 keys].
+  int k_off[kDmaPerTile], k_blk[kDmaPerTile], v_off[kDmaPerTile], v_blk[kDmaPerTile];
+#pragma unroll
+  for (int i = 0; i < kDmaPerTile; ++i) {
+    const int ci = wave * kDmaPerTile + i;
+    const int c = 2 * ci + (lane >> 5), slot = lane & 31;
+    const int cs = slot & 15, key = 8 * (cs >> 2) + (cs & 3) + 4 * (slot >> 4);
+    k_blk[i] = key / BS;
+    k_off[i] = (c * BS + key % BS) * 8;
+    const int e = ci * 64 + lane, jj = e / D, d = e % D;
+    v_blk[i] = __builtin_amdgcn_readfirstlane((8 * jj) / BS);  // uniform per instruction
+    v_off[i] = ((8 * jj % BS) / 8 * D + d) * 8;
+  }
 
   // One step's K and V into ring stage `stage`: each wave writes its
   // kDmaPerTile KiB of each tile; lane L of wave instruction ci writes 16
   // bytes at ci KiB + 16 L.
-  //   K tile: [chunk c of 8 dims][slot 16 kt + c][8 dims]; slot (kt, c)
-  //           holds key 8 (c / 4) + 4 kt + c % 4 (the MFMA's key order).
-  //   V tile: [8-key group jj][dim][8 keys].
   auto issue = [&](int b0, int b1, int b2, int b3, int stage) {
     char* base = kv_lds + stage * kStepBytes;
+    // the step's blocks' offsets (uniform)
+    const int64_t o0 = (int64_t)b0 * bstride + hoff, o1 = (int64_t)b1 * bstride + hoff;
+    const int64_t o2 = (int64_t)b2 * bstride + hoff, o3 = (int64_t)b3 * bstride + hoff;
+    auto sel = [&](int i) -> int64_t {
+      if constexpr (NBS == 1) return o0;
+      else if constexpr (NBS == 2) return i == 0 ? o0 : o1;
+      else return i < 2 ? (i == 0 ? o0 : o1) : (i == 2 ? o2 : o3);
+    };
 #pragma unroll
     for (int i = 0; i < kDmaPerTile; ++i) {
       const int ci = wave * kDmaPerTile + i;
-      const int c = 2 * ci + (lane >> 5), slot = lane & 31;
-      const int cs = slot & 15, key = 8 * (cs >> 2) + (cs & 3) + 4 * (slot >> 4);
-      const half_t* src = a.k_cache + pick(b0, b1, b2, b3, key / BS) + hoff + (c * BS + key % BS) * 8;
+      const half_t* src = a.k_cache + sel(k_blk[i]) + k_off[i];
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + ci * 1024),
                                        16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kDmaPerTile; ++i) {
       const int ci = wave * kDmaPerTile + i;
-      const int e = ci * 64 + lane, jj = e / D, d = e % D;
-      const half_t* src = a.v_cache + pick(b0, b1, b2, b3, (8 * jj) / BS) + hoff +
-                          (int64_t)((8 * jj % BS) / 8 * D + d) * 8;
+      const half_t* src = a.v_cache + sel(v_blk[i]) + v_off[i];
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)(base + kTileBytes + ci * 1024), 16, 0, 0);
     }
