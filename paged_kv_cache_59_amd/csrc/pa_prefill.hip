@@ -67,15 +67,19 @@ __device__ __forceinline__ float sum8(half8_t v) {
   return acc;
 }
 
-// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 k-slot groups of one row),
-// with the gfx950 cross-row swaps: each swap of x with itself leaves lane
-// l's value and its partner's across the 16- (32-) lane boundary in its two
-// results.
-__device__ __forceinline__ float max_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(x, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(x, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 k-slot groups of one row)
+// of two values at once (the two row sub-tiles' maxima), with the gfx950
+// cross-row swaps, three in all: (m0, m1) -> rows 0..3 hold the maxima of
+// rows (0, 1) of m0, (0, 1) of m1, (2, 3) of m0, (2, 3) of m1; then the
+// halves are combined; then each result is spread over all four rows.
+__device__ __forceinline__ void max_rows2(float& m0, float& m1) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+  const float x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float z = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  m0 = __uint_as_float(r[0]);
+  m1 = __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float4v mfma16x16x32(half8_t a, half8_t b, float4v c) {
@@ -341,8 +345,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       mt[rt] = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mt[rt] = fmaxf(mt[rt], z[rt][e]);
-      mt[rt] = max_rows(mt[rt]) * a.scale_log2;
     }
+    max_rows2(mt[0], mt[1]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) mt[rt] *= a.scale_log2;
     // The reference max m_run is raised only when a row's max passes it by
     // more than kStale (log2 units); otherwise the weights exp2(z - m_run)
     // stay below 2^kStale, well inside fp16, and O and l need no rescale.
