@@ -46,6 +46,23 @@ def _run(cmd):
     return out
 
 
+def check_no_scratch(remarks: str) -> str:
+    """Raise if a kernel's resource-usage remarks report scratch use; else
+    a one-line summary."""
+    name, kernels, bad = None, 0, []
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+            kernels += 1
+        elif "ScratchSize [bytes/lane]:" in line:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0].strip())
+            if size:
+                bad.append(f"{name}: {size} bytes/lane")
+    if bad:
+        raise RuntimeError("kernels using scratch memory:\n" + "\n".join(bad))
+    return f"{kernels} device functions, none using scratch memory"
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -53,10 +70,16 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        # the resource-usage remarks let the build refuse kernels that spill
+        # to scratch memory (a register array indexed at run time, or too
+        # many live values): every kernel here is meant to run without it
+        remarks = [] if src.endswith(".cpp") else ["-Rpass-analysis=kernel-resource-usage"]
+        cmds.append([HIPCC, *FLAGS, *lang, *remarks, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
+    scratch = check_no_scratch("\n".join(outs))
+    outs = [o for o in outs if "kernel-resource-usage" not in o] + [scratch]
     tmp = LIB_PATH + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB_PATH)
