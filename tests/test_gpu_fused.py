@@ -75,6 +75,19 @@ def test_fused_long_run_many_pieces(n_len, workers):
     run_fused(w, workers, f"fused run of {n_len} over {workers} workers")
 
 
+def test_fused_batch_above_one_launch():
+    """More sequences than one launch takes: each launch's new rows, slots and
+    outputs start at its first sequence.  Pools bit for bit, outputs on both
+    launches' sequences."""
+    w = wl.make_workload("fused-wide", 347, 2, 1, 64, len_range=(1, 40), num_seqs=4100)
+    d = to_device(w)
+    out = fused_step(w, d, 0)
+    kc, vc = oracle_pools(w)
+    assert_pools_equal(d, kc, vc, "fused 4100")
+    seqs = np.r_[0:40, 4050:4100]
+    compare(out[seqs], oracle_decode(w, kc, vc, seqs), "fused 4100 sequences")
+
+
 def test_fused_zero_length_rows():
     w = wl.make_workload("fused-zero", 340, 8, 2, 64, context_lens=[0, 1, 0, 65, 0])
     out = run_fused(w, 0, "fused zero rows")
