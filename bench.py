@@ -358,7 +358,7 @@ def main():
         args.warmup = 300 if prefill else 20
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path", file=sys.stderr)
+              "the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe_mb:
         copy_probe(args)

@@ -127,7 +127,13 @@ class Simulator:
     every iteration also runs the library's kernels on real pools: copies,
     appends, prefill chunks, decode, swaps."""
 
-    def __init__(self, cfg: Config, gpu: bool = False, check_every: int = 0):
+    def __init__(self, cfg: Config, gpu: bool = False, check_every: int = 0, check_row=None):
+        """``check_every`` > 0 checks the decoded rows every that many steps
+        with ``check_row(request, position, row, scale) -> max abs error``
+        (a caller-supplied reference: a request's K, V and q at every position
+        follow from its token hashes through ``token_tensors``)."""
+        if check_every and check_row is None:
+            raise ValueError("checking rows needs a check_row callback")
         self.cfg = cfg
         self.bm = cbm.BlockManager(cfg.num_blocks, cfg.block_size, cfg.hash_kind)
         self.waiting: deque = deque()
@@ -142,6 +148,7 @@ class Simulator:
         self.trace = []
         self.gpu = gpu
         self.check_every = check_every
+        self.check_row = check_row
         self.checked_rows = 0
         self.max_abs_err = 0.0
         if gpu:
@@ -399,24 +406,9 @@ class Simulator:
             for out, items in checks:
                 o = out.cpu().numpy()
                 for req, p, row in items:
-                    self._check_row(req, p, o[row])
-
-    def _check_row(self, req: Request, p: int, got) -> None:
-        """Attention of the request's position p rebuilt from its tokens alone
-        (the oracle's attention, fp64)."""
-        import oracle
-        c = self.cfg
-        qkv = [token_tensors(h, c.num_q_heads, c.num_kv_heads, c.head_dim)
-               for h in req.hashes[:p + 1]]
-        K = np.stack([x[1] for x in qkv]).astype(np.float64)     # [p+1, Hkv, D]
-        V = np.stack([x[2] for x in qkv]).astype(np.float64)
-        q = qkv[-1][0].astype(np.float64)
-        G = c.num_q_heads // c.num_kv_heads
-        sc = np.float64(np.float32(self.scale))
-        for h in range(c.num_q_heads):
-            ref = oracle.attention_one_query(q[h], K[:, h // G], V[:, h // G], sc)
-            self.max_abs_err = max(self.max_abs_err, float(np.abs(got[h].astype(np.float64) - ref).max()))
-        self.checked_rows += 1
+                    err = self.check_row(req, p, o[row], self.scale)
+                    self.max_abs_err = max(self.max_abs_err, float(err))
+                    self.checked_rows += 1
 
 
 def synthetic_arrivals(num_requests: int, seed: int, rate: float, prompt_range, output_range,
