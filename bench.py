@@ -212,7 +212,6 @@ def bench_prefill(args):
     follows the chip's clock, which under sustained load dips and then settles
     over about 35 ms: the default warm-up (300 steps) runs past that."""
     import torch
-    import oracle
     from paged_kv_cache_59_amd import binding as pk
     from paged_kv_cache_59_amd import workloads as wl
 
@@ -225,7 +224,7 @@ def bench_prefill(args):
     kc, vc = t(w.k_cache), t(w.v_cache)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    flops = oracle.prefill_flops(w.context_lens, w.query_start, w.num_q_heads, w.head_dim)
+    flops = w.flops()
 
     def step(ev=None):
         pk.pa_reshape_and_cache(k_new, v_new, kc, vc, slots)

@@ -463,6 +463,14 @@ class PrefillWorkload:
     def kv_bytes_per_token_layer(self) -> int:
         return 2 * self.num_kv_heads * self.head_dim * 2
 
+    def flops(self) -> int:
+        """Algorithmic flops of the step's attention: the query at position p
+        meets the p + 1 keys at or before it, with 2 D flops per key for q.K
+        and 2 D for the weighted sum of V, per query head."""
+        lens = self.context_lens.astype(np.int64)
+        nq = np.diff(self.query_start.astype(np.int64))
+        keys = (lens * (lens + 1) - (lens - nq) * (lens - nq + 1)) // 2
+        return int(4 * int(keys.sum()) * self.num_q_heads * self.head_dim)
 
 def make_prefill_workload(name, seed, num_q_heads, num_kv_heads, head_dim, context_lens=None,
                           chunk_lens=None, num_seqs=None, cached_range=None, chunk=None,
