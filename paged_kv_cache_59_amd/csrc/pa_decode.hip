@@ -194,16 +194,16 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const bool streamer = role == 0;
   const int lane = threadIdx.x & 63;
   const int nw = gridDim.x;
-  // Logical worker numbering: runs of up to 16 consecutive logical workers
+  // Logical worker numbering: runs of up to 32 consecutive logical workers
   // on one XCD (workgroup i runs on XCD i % 8), the runs dealt to the XCDs in
   // turn.  Consecutive shares then meet in one L2 (sequences that share
   // prefix blocks are adjacent), while every XCD still draws on the whole
   // batch (its speed then depends less on which sequences it holds).
   const int bx = (int)blockIdx.x;
-  int kw = 1;  // run length: the largest power of two <= 16 dividing nw / 8
+  int kw = 1;  // run length: the largest power of two <= 32 dividing nw / 8
   if (nw % 8 == 0) {
     const int per_xcd = nw / 8;
-    kw = min(per_xcd & -per_xcd, 16);
+    kw = min(per_xcd & -per_xcd, 32);
   }
   const int w = (nw % 8 == 0) ? ((bx / 8) / kw) * 8 * kw + (bx % 8) * kw + (bx / 8) % kw : bx;
   const int S = a.num_seqs;
