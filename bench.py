@@ -388,6 +388,11 @@ def main():
     ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, workers)
     stream = torch.cuda.current_stream()
     has_copy = w.block_mapping.shape[0] > 0
+    # the caller's knowledge that sequences share blocks (prefix caching):
+    # some physical block appears in more than one table row
+    used = np.concatenate([w.block_tables[i, :-(-int(n) // w.block_size)]
+                           for i, n in enumerate(w.context_lens) if n > 0])
+    shared = np.unique(used).size < used.size
 
     def step(i, ev=None, kernel_ev=None):
         kc, vc = replicas[i % R]
@@ -404,7 +409,8 @@ def main():
         else:
             pk.pa_decode_append(out, q, k_new, v_new, slots, kc, vc, tab, lens, float(w.scale),
                                 w.num_kv_heads, max_context_len=w.max_context_len,
-                                num_workers=workers, workspace=ws, kernel_events=kernel_ev)
+                                num_workers=workers, workspace=ws, kernel_events=kernel_ev,
+                                shared_blocks=shared)
         if ev is not None:
             ev[1].record(stream)
 
@@ -500,6 +506,7 @@ def main():
             "copies_per_step": int(w.block_mapping.shape[0]), "placement": args.placement,
             "step_bytes": step_bytes, "decode_bytes": w.decode_bytes(),
             "kernel_bytes": kernel_bytes, "append": "fused" if fused else "separate launch",
+            "shared_blocks_flag": bool(shared and fused),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -225,6 +225,13 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  *   k_new, v_new   fp16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
  *   slot_mapping   int64 [num_seqs]: the slot of token s; negative (or past
  *                  the pool) = the row is attended but not stored
+ *   flags          0, or PA_DECODE_SHARED_BLOCKS when sequences of the batch
+ *                  share blocks (prefix caching, forks): K/V are then read
+ *                  through the caches, so that repeat reads of a shared
+ *                  block hit L2 (measured 20% faster on a batch of
+ *                  8-sequence groups sharing 1,024-token prefixes, 9-12%
+ *                  slower on batches that share nothing); any other bit is
+ *                  PA_ERR_INVALID_ARG.  Results do not depend on it.
  *   the rest       as pa_decode; k_cache and v_cache are written (the new
  *                  rows only)
  *
@@ -240,13 +247,15 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  * (Llama-3.1-8B layer, 64 sequences): 59.1 us per step, against 62.7 us for
  * pa_reshape_and_cache then pa_decode.
  */
+#define PA_DECODE_SHARED_BLOCKS 1u /* flag: sequences share blocks (prefix caching, forks) */
 int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
                      const int64_t* slot_mapping, void* k_cache, void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, float scale,
                      int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                      int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+                     uint32_t flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /* pa_decode_append with the kernel-bound timing events of pa_decode_timed. */
 int pa_decode_append_timed(void* out, const void* q, const void* k_new, const void* v_new,
@@ -255,8 +264,8 @@ int pa_decode_append_timed(void* out, const void* q, const void* k_new, const vo
                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                            int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t kernel_start, hipEvent_t kernel_stop);
+                           uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, hipEvent_t kernel_start, hipEvent_t kernel_stop);
 
 /*
  * Read-bandwidth probe, for measurement: the HBM read rate this device

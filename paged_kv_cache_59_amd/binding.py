@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_timed.argtypes = L.pa_decode.argtypes + [vp, vp]
     L.pa_decode_timed.restype = ctypes.c_int
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
-                                   i32, i32, i32, i32, i64, i32, i32, vp, sz, vp]
+                                   i32, i32, i32, i32, i64, i32, i32, ctypes.c_uint32, vp, sz, vp]
     L.pa_decode_append.restype = ctypes.c_int
     L.pa_decode_append_timed.argtypes = L.pa_decode_append.argtypes + [vp, vp]
     L.pa_decode_append_timed.restype = ctypes.c_int
@@ -218,15 +218,20 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
     return out
 
 
+PA_DECODE_SHARED_BLOCKS = 1
+
+
 def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                      context_lens, scale, num_kv_heads, max_context_len=None, num_workers=0,
-                     workspace=None, stream=None, kernel_events=None):
+                     workspace=None, stream=None, kernel_events=None, shared_blocks=False):
     """Append each sequence's new token and decode, in one launch: the same
     results as pa_reshape_and_cache(k_new, v_new, k_cache, v_cache,
     slot_mapping) followed by pa_decode(...), when token s is sequence s's
     token at position context_lens[s] - 1 and slot_mapping[s] is that
     position's slot (negative: attended, not stored).  k_new and v_new are
-    [num_seqs, Hkv, D] fp16; the other arguments as pa_decode."""
+    [num_seqs, Hkv, D] fp16; the other arguments as pa_decode.
+    ``shared_blocks``: sequences of the batch share blocks (prefix caching,
+    forks); K/V are then read through the caches (same results)."""
     _dev(out, "out", torch.float16)
     _dev(q, "q", torch.float16)
     _dev(k_new, "k_new", torch.float16)
@@ -259,8 +264,9 @@ def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block
     args = (out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
             slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), float(scale), hkv, S, hq, d, bs, mb,
-            nb, int(max_context_len), int(num_workers), workspace.data_ptr(), workspace.numel(),
-            _stream(q, stream))
+            nb, int(max_context_len), int(num_workers),
+            PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, workspace.data_ptr(),
+            workspace.numel(), _stream(q, stream))
     if kernel_events is None:
         _check(lib().pa_decode_append(*args), "pa_decode_append")
     else:

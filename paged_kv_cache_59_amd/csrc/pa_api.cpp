@@ -147,8 +147,9 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                 int32_t max_context_len, int32_t num_workers, void* workspace,
                 size_t workspace_bytes, hipStream_t stream, hipEvent_t kernel_start,
-                hipEvent_t kernel_stop) {
+                hipEvent_t kernel_stop, uint32_t flags = 0) {
   const bool fused = k_new || v_new || slot_mapping;
+  if (flags & ~(uint32_t)PA_DECODE_SHARED_BLOCKS) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || !std::isfinite(scale))
     return PA_ERR_INVALID_ARG;
@@ -192,6 +193,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_workers = w;
+  a.cached_loads = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
   (void)hipGetLastError();
   // launches on one stream run in order, so they share the workspace
   for (int64_t s0 = 0; s0 < num_seqs; s0 += per_launch) {
@@ -240,13 +242,13 @@ int pa_decode_append_timed(void* out, const void* q, const void* k_new, const vo
                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                            int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+                           uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, hipEvent_t kernel_start, hipEvent_t kernel_stop) {
   if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
   return decode_impl(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                      context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
                      block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
-                     workspace, workspace_bytes, stream, kernel_start, kernel_stop);
+                     workspace, workspace_bytes, stream, kernel_start, kernel_stop, flags);
 }
 
 int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
@@ -255,12 +257,13 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                      int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                     uint32_t flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   return pa_decode_append_timed(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
                                 block_tables, context_lens, scale, num_kv_heads, num_seqs,
                                 num_q_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                                max_context_len, num_workers, workspace, workspace_bytes, stream,
-                                nullptr, nullptr);
+                                max_context_len, num_workers, flags, workspace, workspace_bytes,
+                                stream, nullptr, nullptr);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

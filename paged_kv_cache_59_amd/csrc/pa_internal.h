@@ -83,6 +83,9 @@ struct DecodeArgs {
   const int64_t* slot_mapping;
   half_t* k_cache_w;
   half_t* v_cache_w;
+  // K/V loads through the caches (blocks shared between sequences meet in
+  // L2) instead of non-temporal loads (blocks read once)
+  int cached_loads;
 };
 
 // Read-bandwidth probe (sequential when order is null, else num_tiles tiles

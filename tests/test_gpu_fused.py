@@ -26,23 +26,23 @@ pytestmark = pytest.mark.gpu
 FUSED_LENS = [1, 2, 15, 16, 17, 63, 64, 65, 66, 127, 128, 129, 257, 511, 513, 1025, 1000]
 
 
-def fused_step(w, d, num_workers=0, workspace=None):
+def fused_step(w, d, num_workers=0, workspace=None, shared_blocks=False):
     """copy-on-write (if any), then one pa_decode_append; out as numpy fp16."""
     if w.block_mapping.shape[0]:
         pk.pa_copy_blocks(d["k_cache"], d["v_cache"], d["block_mapping"])
     pk.pa_decode_append(d["out"], d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
                         d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                         float(w.scale), w.num_kv_heads, max_context_len=w.max_context_len,
-                        num_workers=num_workers, workspace=workspace)
+                        num_workers=num_workers, workspace=workspace, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return d["out"].cpu().numpy()
 
 
-def run_fused(w, num_workers=0, label=""):
+def run_fused(w, num_workers=0, label="", shared_blocks=False):
     log(f"fused case {label}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_dim} BS={w.block_size} maxctx={w.max_context_len} workers={num_workers}")
     d = to_device(w)
-    out = fused_step(w, d, num_workers)
+    out = fused_step(w, d, num_workers, shared_blocks=shared_blocks)
     kc, vc = oracle_pools(w)
     assert_pools_equal(d, kc, vc, label)
     compare(out, oracle_decode(w, kc, vc), label)
@@ -94,12 +94,14 @@ def test_fused_zero_length_rows():
     assert not out[[0, 2, 4]].any()
 
 
-def test_fused_prefix_sharing_with_copies():
-    """Copy-on-write before the fused launch: the new token lands in the copy."""
+@pytest.mark.parametrize("shared_blocks", [False, True])
+def test_fused_prefix_sharing_with_copies(shared_blocks):
+    """Copy-on-write before the fused launch: the new token lands in the copy.
+    With the shared-blocks flag the K/V loads go through the caches."""
     w = wl.make_workload("fused-prefix", 341, 32, 8, 128, num_seqs=16, prefix_groups=4,
                          prefix_len=256, suffix_range=(1, 200))
     assert w.block_mapping.shape[0] > 0
-    run_fused(w, 0, "fused prefix")
+    run_fused(w, 0, f"fused prefix shared={shared_blocks}", shared_blocks=shared_blocks)
 
 
 def test_fused_padding_slot_attends_but_does_not_store():
@@ -173,7 +175,7 @@ def test_fused_errors():
                               d["v_cache"].data_ptr(), d["block_tables"].data_ptr(),
                               d["context_lens"].data_ptr(), 0.125, 2, 2, 8, 64, 16,
                               int(w.block_tables.shape[1]), int(w.num_blocks), w.max_context_len,
-                              0, None, 0, None)
+                              0, 0, None, 0, None)
     assert code == pk.PA_ERR_INVALID_ARG
     # a misaligned K row buffer
     kn = torch.empty(d["k_new"].numel() + 1, dtype=torch.float16, device="cuda")
@@ -183,7 +185,15 @@ def test_fused_errors():
                               d["k_cache"].data_ptr(), d["v_cache"].data_ptr(),
                               d["block_tables"].data_ptr(), d["context_lens"].data_ptr(), 0.125, 2,
                               2, 8, 64, 16, int(w.block_tables.shape[1]), int(w.num_blocks),
-                              w.max_context_len, 0, ws.data_ptr(), ws.numel(), None)
+                              w.max_context_len, 0, 0, ws.data_ptr(), ws.numel(), None)
+    assert code == pk.PA_ERR_INVALID_ARG
+    # an unknown flag bit
+    code = L.pa_decode_append(d["out"].data_ptr(), d["q"].data_ptr(), d["k_new"].data_ptr(),
+                              d["v_new"].data_ptr(), d["slot_mapping"].data_ptr(),
+                              d["k_cache"].data_ptr(), d["v_cache"].data_ptr(),
+                              d["block_tables"].data_ptr(), d["context_lens"].data_ptr(), 0.125, 2,
+                              2, 8, 64, 16, int(w.block_tables.shape[1]), int(w.num_blocks),
+                              w.max_context_len, 0, 2, ws.data_ptr(), ws.numel(), None)
     assert code == pk.PA_ERR_INVALID_ARG
 
 
@@ -194,7 +204,7 @@ def test_fused_full_size(name):
     OPT-shaped batch, with its longest and shortest)."""
     w = wl.make_named(name)
     d = to_device(w)
-    out = fused_step(w, d, 0)
+    out = fused_step(w, d, 0, shared_blocks=name == "prefix_b256")  # as the benchmark runs it
     kc, vc = oracle_pools(w)
     assert_pools_equal(d, kc, vc, name)
     if name == "opt13b_b128":
