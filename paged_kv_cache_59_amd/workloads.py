@@ -196,27 +196,49 @@ class Workload:
         return 2 * self.num_kv_heads * self.head_dim * 2
 
     def decode_bytes(self) -> int:
-        """Bytes the decode step must move: valid K/V, q and out, table, lengths.
+        """Logical bytes of the decode step: every sequence's valid K/V
+        positions (a block shared by several sequences counts once per
+        holder), q and out, the table entries it reads, the lengths.
 
-        Unused tail slots of last blocks, split-context partials and repeat
-        reads of shared blocks are not counted.
+        Unused tail slots of last blocks and split-context partials are not
+        counted.  ``unique_decode_bytes`` counts shared blocks once.
         """
         lens = self.context_lens.astype(np.int64)
         kv = int(lens.sum()) * self.kv_bytes_per_token_layer()
+        return kv + self._decode_side_bytes()
+
+    def _decode_side_bytes(self) -> int:
+        """q and out, table entries, lengths."""
+        lens = self.context_lens.astype(np.int64)
         qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * 2
         table = int((-(-lens // self.block_size)).sum()) * 4
-        return kv + qo + table + 4 * self.num_seqs
+        return qo + table + 4 * self.num_seqs
 
     def unique_kv_bytes(self) -> int:
-        """Valid K/V bytes counting each physical block position once."""
-        seen = set()
+        """Valid K/V bytes with each physical block counted once, at the
+        largest number of its positions any holder reads."""
+        fill = {}
         for s in range(self.num_seqs):
             n = int(self.context_lens[s])
             for pos in range(0, n, self.block_size):
-                j = pos // self.block_size
-                seen.add((int(self.block_tables[s, j]), min(self.block_size, n - pos)))
-        tokens = sum(t for _, t in seen)
-        return tokens * self.kv_bytes_per_token_layer()
+                b = int(self.block_tables[s, pos // self.block_size])
+                fill[b] = max(fill.get(b, 0), min(self.block_size, n - pos))
+        return sum(fill.values()) * self.kv_bytes_per_token_layer()
+
+    def unique_decode_bytes(self) -> int:
+        """Bytes the decode step must move when shared blocks are read once:
+        unique K/V plus q and out, table entries, lengths.  Equal to
+        ``decode_bytes`` for batches that share no block."""
+        return self.unique_kv_bytes() + self._decode_side_bytes()
+
+    def shares_blocks(self) -> bool:
+        """Some physical block appears in more than one table row."""
+        used = [self.block_tables[s, :-(-int(n) // self.block_size)]
+                for s, n in enumerate(self.context_lens) if n > 0]
+        if not used:
+            return False
+        used = np.concatenate(used)
+        return np.unique(used).size < used.size
 
     def append_bytes(self) -> int:
         """Bytes the append moves: read k, v rows and write them into the pool."""

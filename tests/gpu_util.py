@@ -7,11 +7,14 @@ compare.  Tolerances for decode (fp16 inputs, fp32 accumulation, fp16 out):
                                                                    <= 1e-2
 The oracle output is float64 and not rounded.  Append and copy are bit-exact.
 """
+import functools
+
 import numpy as np
 import torch
 
 import oracle
 from paged_kv_cache_59_amd import binding as pk
+from paged_kv_cache_59_amd import workloads as wl
 
 ABS_TOL = 5e-3
 ROW_REL_TOL = 1e-2
@@ -19,6 +22,13 @@ ROW_REL_TOL = 1e-2
 
 def log(*a):
     print(*a, flush=True)
+
+
+@functools.lru_cache(maxsize=4)
+def named(name):
+    """A named full-size workload, generated once per test session (tests
+    read its arrays and never write them)."""
+    return wl.make_named(name)
 
 
 def dev(a):

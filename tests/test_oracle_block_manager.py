@@ -36,11 +36,24 @@ def check_invariants(m: obm.BlockManagerModel):
 # hashes: published test vectors
 # ---------------------------------------------------------------------------
 
-def test_sha256_fips_180_4_example():
-    """FIPS 180-4 / its example 'abc' message digest."""
-    import hashlib
-    assert hashlib.sha256(b"abc").hexdigest() == \
-        "ba7816bf8f01cfea414140de5dae2223b00361a396177a9cb410ff61f20015ad"
+# FIPS 180-2, appendix B.2: the 448-bit two-block message and its SHA-256 digest
+_FIPS_B2_MSG = b"abcdbcdecdefdefgefghfghighijhijkijkljklmklmnlmnomnopnopq"
+_FIPS_B2_DIGEST = "248d6a61d20638b8e5c026930c3e6039a33ce45964ff2167f6ecedd419db06c1"
+
+
+def _as_tokens(data: bytes):
+    """The int32 token ids whose little-endian bytes are ``data``."""
+    return [int.from_bytes(data[i:i + 4], "little", signed=True) for i in range(0, len(data), 4)]
+
+
+def test_sha256_block_key_byte_layout_against_published_digest():
+    """The oracle's sha256 block key hashes exactly parent key || token ids
+    as little-endian int32 || extra bytes: the 56-byte FIPS message cut into
+    (parent, tokens, extra) three ways must give the published digest."""
+    m = _FIPS_B2_MSG
+    assert obm.block_key(b"", _as_tokens(m)).hex() == _FIPS_B2_DIGEST
+    assert obm.block_key(m[:32], _as_tokens(m[32:])).hex() == _FIPS_B2_DIGEST
+    assert obm.block_key(m[:8], _as_tokens(m[8:48]), m[48:]).hex() == _FIPS_B2_DIGEST
 
 
 def test_fnv1a64_reference_vectors():

@@ -106,7 +106,28 @@ def test_byte_accounting():
     qo = 2 * 2 * 32 * 128 * 2
     table = (7 + 125) * 4
     assert w.decode_bytes() == kv + qo + table + 8
+    assert w.unique_decode_bytes() == w.decode_bytes()  # nothing shared
     assert w.append_bytes() == 2 * 2 * per_tok
+
+
+def test_unique_bytes_count_a_shared_block_once_at_its_fullest():
+    """Two holders of one physical block with different fills (10 and 16
+    positions) count it once, at 16 positions; a private block counts once."""
+    w = wl.make_workload("u", 14, 4, 2, 64, context_lens=[10, 16, 40])
+    w.block_tables[1, 0] = w.block_tables[0, 0]
+    per_tok = 2 * 2 * 64 * 2
+    assert w.shares_blocks()
+    assert w.unique_kv_bytes() == (16 + 40) * per_tok
+    assert w.decode_bytes() - w.unique_decode_bytes() == 10 * per_tok
+
+
+def test_prefix_batch_unique_bytes():
+    """The shared-prefix batch: 32 prefixes of 1,024 tokens read once, plus
+    every sequence's private positions."""
+    w = wl.make_named("prefix_b256")
+    per_tok = 2 * 8 * 128 * 2
+    private = int(w.context_lens.sum()) - 256 * 1024
+    assert w.unique_kv_bytes() == (32 * 1024 + private) * per_tok
 
 
 def test_prefill_flops_match_the_oracle_count():
