@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--swap-blocks", type=int, default=0,
                     help="only measure swapping this many blocks (Llama-3.1-8B layer shape) "
                          "out to pinned host memory and back in")
+    ap.add_argument("--trace", action="store_true",
+                    help="decode: per-worker timeline from the measurement build "
+                         "(libpagedkv_trace.so, `python -m paged_kv_cache_59_amd.build --trace`), "
+                         "one launch per step with a synchronisation after each; prints a summary")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run `steps` plain device copies of this many MiB (an elementwise "
                          "kernel reading and writing known bytes, to calibrate HBM counters)")
@@ -358,6 +362,84 @@ def bench_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def trace_decode(args):
+    """Per-worker timeline of the decode kernel, from the stamps the
+    measurement build writes at the start of the workspace (100 MHz clock,
+    the same on every CU).  Each step is synchronised and its stamps read
+    back; times are relative to the step's earliest worker entry."""
+    import torch
+    from paged_kv_cache_59_amd import binding as pk
+    pk.use_trace_library()
+    from paged_kv_cache_59_amd import workloads as wl
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    w = wl.make_named(args.workload, placement=args.placement, block_size=args.block_size)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, tab, lens = t(w.q), t(w.block_tables), t(w.context_lens)
+    k_new, v_new, slots, pairs = t(w.k_new), t(w.v_new), t(w.slot_mapping), t(w.block_mapping)
+    kc0, vc0 = t(w.k_cache), t(w.v_cache)
+    pool_bytes = kc0.numel() * 2 + vc0.numel() * 2
+    R = max(1, int(np.ceil(args.replica_gb * 1e9 / pool_bytes)))
+    replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
+    out = torch.empty_like(q)
+    workers = args.num_workers or pk.pa_decode_num_workers()
+    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, workers)
+    shared = w.shares_blocks()
+    S = pk.TRACE_SLOTS
+    runs = []
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in kev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(args.warmup + args.steps):
+        kc, vc = replicas[i % R]
+        if pairs.shape[0]:
+            pk.pa_copy_blocks(kc, vc, pairs)
+        ws[:workers * S * 8].zero_()
+        pk.pa_decode_append(out, q, k_new, v_new, slots, kc, vc, tab, lens, float(w.scale),
+                            w.num_kv_heads, max_context_len=w.max_context_len,
+                            num_workers=workers, workspace=ws, shared_blocks=shared,
+                            kernel_events=kev[i - args.warmup] if i >= args.warmup else None)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            runs.append(ws[:workers * S * 8].view(torch.int64).view(workers, S).cpu().numpy())
+    kern_us = np.array([a.elapsed_time(b) * 1e3 for a, b in kev])
+    names = ["entry", "tables", "first_unit", "static_end", "stream_end", "stores_issued",
+             "helper_end"]
+    rel = {n: [] for n in names}
+    spans = []
+    per_xcd_end = []
+    for tr in runs:
+        live = tr[:, 0] > 0
+        tr = tr[live]
+        t0 = tr[:, 0].min()
+        for j, n in enumerate(names):
+            rel[n].append((tr[:, j] - t0) * 0.01)  # 100 MHz -> us
+        spans.append(((tr[:, 6].max() - t0) * 0.01, (tr[:, 4].max() - t0) * 0.01))
+        xcc = tr[:, 7] & 15
+        per_xcd_end.append([float(np.median((tr[xcc == x, 4] - t0) * 0.01)) for x in range(8)])
+    pct = lambda a: {"min": round(float(np.min(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+                     "median": round(float(np.median(a)), 2),
+                     "p90": round(float(np.percentile(a, 90)), 2), "max": round(float(np.max(a)), 2)}
+    last = runs[-1][runs[-1][:, 0] > 0]
+    res = {
+        "trace": w.name, "workers": workers, "steps": args.steps, "warmup": args.warmup,
+        "kernel_us_events": pct(kern_us),
+        "stamp_us_from_first_entry": {n: pct(np.concatenate(rel[n])) for n in names},
+        "last_helper_end_us": pct([a for a, _ in spans]),
+        "last_stream_end_us": pct([b for _, b in spans]),
+        "median_stream_end_by_xcd_us": [round(float(np.median([p[x] for p in per_xcd_end])), 2)
+                                        for x in range(8)],
+        "units_per_worker": pct(last[:, 8]), "pieces_per_worker": pct(last[:, 9]),
+        "merges_per_worker": pct(last[:, 10]), "claims_per_worker": pct(last[:, 11]),
+        "note": "one launch per step, synchronised after each; stamps in us from the step's "
+                "earliest worker entry (s_memrealtime, 100 MHz)",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     from paged_kv_cache_59_amd import workloads as wl_names
@@ -373,6 +455,9 @@ def main():
         return
     if args.swap_blocks:
         bench_swap(args)
+        return
+    if args.trace:
+        trace_decode(args)
         return
     if prefill:
         bench_prefill(args)

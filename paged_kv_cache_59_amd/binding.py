@@ -30,6 +30,21 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_deco
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
 
+def use_trace_library() -> None:
+    """Load the measurement build (libpagedkv_trace.so: the same entry
+    points; the decode kernel also writes per-worker timestamps at the start
+    of its workspace) instead of libpagedkv.so.  Call before the first call
+    into the library."""
+    global _LIB_PATH
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv_trace.so")
+    if _lib is not None and _LIB_PATH != path:
+        raise RuntimeError("the library is already loaded")
+    _LIB_PATH = path
+
+
+TRACE_SLOTS = 16  # per-worker 64-bit words the measurement build writes
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__(f"{what}: {pa_strerror(code)} ({code})")

@@ -145,6 +145,21 @@ __device__ __forceinline__ half8_t load_kv(const half_t* p) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Measurement builds: a 100 MHz timestamp (the same clock on every CU), and
+// the XCC_ID / HW_ID hardware registers of the wave.
+__device__ __forceinline__ uint64_t stamp_now() {
+  if constexpr (kTrace) return __builtin_amdgcn_s_memrealtime();
+  else return 0;
+}
+__device__ __forceinline__ uint64_t xcc_id() {
+  if constexpr (kTrace) return (uint64_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));
+  else return 0;
+}
+__device__ __forceinline__ uint64_t hw_id() {
+  if constexpr (kTrace) return (uint64_t)__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
+  else return 0;
+}
+
 // A compiler-only ordering point for LDS exchanged between the waves of a
 // workgroup.  The DS instructions of one wave execute in program order, so
 // keeping the compiler from reordering (or caching) the accesses is enough;
@@ -183,6 +198,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   static_assert(NBU * BS == kGroupTokens && kGroups * kChunk == BS, "block size 8, 16 or 32");
   static_assert(kChunks * kChunk == D && kSets * 64 == D, "head_dim must be 64 or 128");
 
+  // measurement builds: this worker's stamps, written at its end
+  uint64_t tr[kTraceSlots] = {};
+  tr[kTrEntry] = stamp_now();
   // [S] units (per KV head) of the sequences before s, [S] its length
   extern __shared__ int seq_lds[];
   // Rows padded so that the 4 rows of one access fall in different LDS banks
@@ -251,6 +269,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   if (w >= P) return;
   if (streamer && lane < 4) ctl[lane] = 0;
   __syncthreads();  // the LDS tables are complete
+  tr[kTrTables] = stamp_now();
+  auto write_trace = [&](int first, int last) {
+    if constexpr (kTrace) {
+      if (lane == 0 && a.ws.trace)
+        for (int i = first; i <= last; ++i) a.ws.trace[(int64_t)w * kTraceSlots + i] = tr[i];
+    }
+  };
 
   // ---- shares ------------------------------------------------------------------
   // share j: units [sb(j), sb(j+1)), sb(j) = floor(j U / P), in (sequence,
@@ -654,10 +679,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
           const int n = units_for(uniform(len_lds[ps[i]]));
-          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n)
+          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n) {
             merge_out(ps[i], ph[i], merge_pieces(ps[i], ph[i]));
+            if constexpr (kTrace) ++tr[kTrMerges];
+          }
         }
       }
+    }
+    if constexpr (kTrace) {
+      __builtin_amdgcn_s_waitcnt(0);
+      tr[kTrHelperEnd] = stamp_now();
+      write_trace(kTrHelperEnd, kTrHelperEnd);
+      write_trace(kTrMerges, kTrMerges);
     }
     return;
   }
@@ -748,6 +781,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       p_lds[g * kPRow + lane] = ph;
     }
 
+    if constexpr (kTrace) {
+      if (tr[kTrUnits]++ == 0) tr[kTrFirstUnit] = stamp_now();
+    }
     // positions past the end (tail of the last block, and re-read blocks past
     // it) in the sequence's last unit: V element := 0
     if (t0 + kGroupTokens > vis) {
@@ -855,6 +891,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           ring_meta[k][3] = cur.g - piece_g0 + 1;
         }
         lds_st(&ctl[kCtlRingMade], ++ring_made);
+        if constexpr (kTrace) ++tr[kTrPieces];
       }
       reset_run();
       q_pending = true;
@@ -874,8 +911,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
+  tr[kTrStreamEnd] = stamp_now();
+  tr[kTrStaticEnd] = tr[kTrStreamEnd];
   finish();
   store_new_rows();
+  if constexpr (kTrace) {
+    tr[kTrStoresIssued] = stamp_now();
+    tr[kTrXcc] = xcc_id();
+    tr[kTrHwId] = hw_id();
+    write_trace(kTrEntry, kTrStoresIssued);  // (the helper writes its own slots)
+    write_trace(kTrXcc, kTrPieces);
+    write_trace(kTrClaims, kTrHwId);
+  }
 }
 
 namespace {
@@ -887,15 +934,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // every call leaves at zero, and never another call's partial results.
 struct WorkspaceLayout {
   int64_t slots;
-  size_t ml, o, partial;  // partial slots: offsets, size
+  size_t ml, o, partial;  // partial slots: offsets, end
   size_t control;         // arrival counters: size
 };
 
 WorkspaceLayout workspace_layout(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
   WorkspaceLayout l;
   l.slots = S * Hkv + workers;
-  l.ml = 0;
-  l.o = align256((size_t)(l.slots * 8) * sizeof(float));
+  // measurement builds: per-worker stamps first
+  l.ml = kTrace ? align256((size_t)workers * kTraceSlots * sizeof(uint64_t)) : 0;
+  l.o = l.ml + align256((size_t)(l.slots * 8) * sizeof(float));
   l.partial = l.o + align256((size_t)(l.slots * 4 * D) * sizeof(float));
   l.control = align256((size_t)(S * Hkv) * sizeof(int));
   return l;
@@ -905,17 +953,6 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t Hkv, int64_t D, int64_t work
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
   const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
   return l.partial + l.control;
-}
-
-DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int64_t Hkv, int64_t D,
-                                       int64_t workers) {
-  const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
-  char* p = reinterpret_cast<char*>(base);
-  DecodeWorkspace w;
-  w.ml = reinterpret_cast<float*>(p + l.ml);
-  w.o = reinterpret_cast<float*>(p + l.o);
-  w.counters = reinterpret_cast<int*>(p + ((bytes - l.control) & ~(size_t)255));
-  return w;
 }
 
 template <int D, int BS, bool Fused, bool Cached>

@@ -39,6 +39,31 @@ struct DecodeWorkspace {
   float* ml;      // [slots][4][2]
   float* o;       // [slots][4][D]
   int* counters;  // [S][Hkv] units arrived
+  uint64_t* trace;  // measurement builds only: [workers][kTraceSlots] at the workspace's start
+};
+
+// Measurement builds (compiled with PA_DECODE_TRACE) put per-worker
+// timestamps and counts at the start of the decode workspace.
+#ifdef PA_DECODE_TRACE
+constexpr bool kTrace = true;
+#else
+constexpr bool kTrace = false;
+#endif
+constexpr int kTraceSlots = 16;
+enum {
+  kTrEntry = 0,     // kernel entry (s_memrealtime, 100 MHz)
+  kTrTables,        // lengths and unit offsets in LDS
+  kTrFirstUnit,     // first unit's logits and softmax done (its K has arrived)
+  kTrStaticEnd,     // last unit of the worker's static share done
+  kTrStreamEnd,     // streamer's last unit done
+  kTrStoresIssued,  // fused append: new rows' stores issued
+  kTrHelperEnd,     // helper wave done (last merge written)
+  kTrXcc,           // XCC (XCD) id of the workgroup
+  kTrUnits,         // units the streamer processed
+  kTrPieces,        // cut pieces handed to the helper
+  kTrMerges,        // runs the helper merged
+  kTrClaims,        // tail chunks claimed
+  kTrHwId,          // HW_ID register (CU, SIMD) of the streamer
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
