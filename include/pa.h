@@ -40,8 +40,9 @@
  *  - A slot index is  physical_block * BS + offset  (offset < BS).
  *  - Pointers are device pointers unless stated; all buffers are owned and
  *    allocated by the caller.  The library allocates nothing and keeps no
- *    state beyond a per-device cache of the compute-unit count; it never
- *    synchronises and never reads device data on the host.
+ *    state beyond a per-device cache of the compute-unit count and the
+ *    device array of pa_decode_append_noalloc; it never synchronises and
+ *    never reads device data on the host.
  *  - Every call only enqueues work on `stream` (0 = the null stream) and
  *    returns.  Faults inside a kernel surface at the caller's next
  *    synchronisation.  The library clears the HIP error state on entry.
@@ -70,6 +71,7 @@ enum {
   PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block size, G > 4        */
   PA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
   PA_ERR_HIP = -4,         /* a HIP call or kernel launch failed              */
+  PA_ERR_SCRATCH_LIMIT = -5, /* pa_decode_append_noalloc: batch above its array */
 };
 
 #define PA_BLOCK_SIZE 16 /* the default block size; 8 and 32 are also accepted */
@@ -256,6 +258,37 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      int64_t num_blocks, int32_t max_context_len, int32_t num_workers,
                      uint32_t flags, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * pa_decode_append for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, work and results as pa_decode_append, without the
+ * workspace: the partial results and arrival counters live in a device array
+ * of 32 MiB that the library holds in each GPU's memory from its first use
+ * until the process ends (a file-scope __device__ array, reached through
+ * hipGetSymbolAddress once per device).  Nothing here allocates or frees.
+ *
+ *   - The first call on a device also enqueues, on `stream`, a kernel that
+ *     zeroes the array's last 1 MiB, where the counters live (a graph
+ *     captured around that first call replays it: harmless).  Every call
+ *     leaves the counters at zero again.
+ *   - All calls on one GPU share the array: calls that overlap in time on one
+ *     GPU (different streams, or concurrent graph replays) race and give
+ *     wrong results.  Serialise them, or use pa_decode_append with a
+ *     workspace per stream.
+ *   - A batch whose workspace (pa_decode_workspace_size of the same sizes)
+ *     exceeds 32 MiB returns PA_ERR_SCRATCH_LIMIT before anything is enqueued
+ *     (e.g. a 128-sequence batch of 40 KV heads at 512 workers needs 12 MB).
+ *   - Other errors as pa_decode_append.
+ */
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, int32_t num_kv_heads, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, int32_t num_workers, uint32_t flags,
+                             hipStream_t stream);
 
 /* pa_decode_append with the kernel-bound timing events of pa_decode_timed. */
 int pa_decode_append_timed(void* out, const void* q, const void* k_new, const void* v_new,

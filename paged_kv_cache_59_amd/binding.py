@@ -22,10 +22,12 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_SCRATCH_LIMIT = -5
 BLOCK_SIZE = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode",
-            "pa_decode_timed", "pa_decode_append", "pa_decode_append_timed", "pa_read_probe",
+            "pa_decode_timed", "pa_decode_append", "pa_decode_append_timed",
+            "pa_decode_append_noalloc", "pa_read_probe",
             "pa_prefill", "pa_decode_workspace_size",
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.restype = ctypes.c_int
     L.pa_decode_append_timed.argtypes = L.pa_decode_append.argtypes + [vp, vp]
     L.pa_decode_append_timed.restype = ctypes.c_int
+    # pa_decode_append without the workspace pointer and size
+    L.pa_decode_append_noalloc.argtypes = L.pa_decode_append.argtypes[:20] + [vp]
+    L.pa_decode_append_noalloc.restype = ctypes.c_int
     L.pa_read_probe.argtypes = [vp, i64, vp, i64, i32, vp, vp, vp, vp]
     L.pa_read_probe.restype = ctypes.c_int
     L.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, i32, i32, i32, i32,
@@ -290,6 +295,44 @@ def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block
             raise ValueError("kernel_events must have been recorded once (torch creates them lazily)")
         _check(lib().pa_decode_append_timed(*args, start.cuda_event, stop.cuda_event),
                "pa_decode_append_timed")
+    return out
+
+
+def pa_decode_append_noalloc(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                             context_lens, scale, num_kv_heads, max_context_len=None,
+                             num_workers=0, stream=None, shared_blocks=False):
+    """pa_decode_append without a workspace: the library's own device array
+    (32 MiB per GPU) holds the partial results.  Calls that overlap in time
+    on one GPU race.  Arguments as pa_decode_append."""
+    for t, n in ((out, "out"), (q, "q"), (k_new, "k_new"), (v_new, "v_new"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n, torch.float16)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if hkv != int(num_kv_heads):
+        raise ValueError("num_kv_heads does not match k_cache")
+    S, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if slot_mapping.numel() != S:
+        raise ValueError("slot_mapping must be [num_seqs]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], context_lens [num_seqs]")
+    mb = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = mb * bs
+    if not math.isfinite(float(scale)):
+        raise ValueError("scale must be finite")
+    code = lib().pa_decode_append_noalloc(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        float(scale), hkv, S, hq, d, bs, mb, nb, int(max_context_len), int(num_workers),
+        PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(q, stream))
+    _check(code, "pa_decode_append_noalloc")
     return out
 
 

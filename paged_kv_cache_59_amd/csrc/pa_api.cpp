@@ -57,6 +57,9 @@ const char* pa_strerror(int code) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case PA_ERR_SCRATCH_LIMIT:
+      return "batch needs more decode scratch than the library's static array holds "
+             "(32 MiB); pass a workspace to pa_decode_append instead";
     default: return "unknown error code";
   }
 }
@@ -147,7 +150,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                 int32_t max_context_len, int32_t num_workers, void* workspace,
                 size_t workspace_bytes, hipStream_t stream, hipEvent_t kernel_start,
-                hipEvent_t kernel_stop, uint32_t flags = 0) {
+                hipEvent_t kernel_stop, uint32_t flags = 0, bool static_scratch = false) {
   const bool fused = k_new || v_new || slot_mapping;
   if (flags & ~(uint32_t)PA_DECODE_SHARED_BLOCKS) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -176,6 +179,14 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   if (w < 0) return w;
   const size_t need =
       pa::decode_workspace_bytes(per_launch, num_kv_heads, head_dim, w);
+  if (static_scratch) {
+    // the library's own device array stands in for the workspace
+    if (need > pa::kStaticScratchBytes ||
+        pa::decode_control_bytes(per_launch, num_kv_heads) > pa::kStaticControlBytes)
+      return PA_ERR_SCRATCH_LIMIT;
+    if (pa::decode_static_scratch(stream, &workspace) != hipSuccess) return PA_ERR_HIP;
+    workspace_bytes = pa::kStaticScratchBytes;
+  }
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return PA_ERR_WORKSPACE;
 
@@ -264,6 +275,21 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                                 num_q_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
                                 max_context_len, num_workers, flags, workspace, workspace_bytes,
                                 stream, nullptr, nullptr);
+}
+
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, int32_t num_kv_heads, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, int32_t num_workers, uint32_t flags,
+                             hipStream_t stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                     context_lens, scale, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, num_workers,
+                     nullptr, 0, stream, nullptr, nullptr, flags, /*static_scratch=*/true);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -54,6 +54,7 @@
 //  * Positions at or past the length are removed by selection (logit -inf,
 //    V element 0), never by multiplication, so NaN or huge values in the
 //    unused tail of the last block cannot leak.
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -953,6 +954,64 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t Hkv, int64_t D, int64_t work
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
   const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
   return l.partial + l.control;
+}
+
+size_t decode_control_bytes(int64_t S, int64_t Hkv) { return align256((size_t)(S * Hkv) * sizeof(int)); }
+
+// ---- the allocation-free decode's workspace --------------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops).  Every call on one GPU uses this same array; calls
+// that overlap in time on one GPU race.  In host code its name is only a
+// stand-in: kernels get the device address from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_static_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidSymbol;
+    // the arrival counters must start at zero (every call leaves them so);
+    // a fill kernel rather than a memset, so that a caller's graph capture
+    // may hold it
+    uint32_t* control = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + kStaticScratchBytes -
+                                                    kStaticControlBytes);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, control,
+                       (int64_t)(kStaticControlBytes / sizeof(uint32_t)));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int64_t Hkv, int64_t D,
+                                       int64_t workers) {
+  const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
+  char* p = reinterpret_cast<char*>(base);
+  DecodeWorkspace w;
+  w.trace = kTrace ? reinterpret_cast<uint64_t*>(p) : nullptr;
+  w.ml = reinterpret_cast<float*>(p + l.ml);
+  w.o = reinterpret_cast<float*>(p + l.o);
+  w.counters = reinterpret_cast<int*>(p + ((bytes - l.control) & ~(size_t)255));
+  return w;
 }
 
 template <int D, int BS, bool Fused, bool Cached>

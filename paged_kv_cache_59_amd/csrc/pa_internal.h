@@ -67,6 +67,19 @@ enum {
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
+// Bytes of arrival counters a launch over S sequences keeps against the end
+// of its workspace.
+size_t decode_control_bytes(int64_t S, int64_t Hkv);
+
+// The allocation-free decode takes its workspace from a file-scope device
+// array of this size (one per GPU, held until the process ends).  Its last
+// kStaticControlBytes, where the arrival counters live, are zeroed on the
+// first call on each device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr size_t kStaticControlBytes = (size_t)1 << 20;
+// The device address of the current device's array (looked up once per
+// device; the first call also enqueues the counters' clear on `stream`).
+hipError_t decode_static_scratch(hipStream_t stream, void** ptr);
 // The layout of one launch in a workspace of `bytes` >= decode_workspace_bytes.
 DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int64_t Hkv, int64_t D,
                                        int64_t workers);

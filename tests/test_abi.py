@@ -135,3 +135,14 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4, dtype=torch.float16)
     with pytest.raises(ValueError):
         binding.pa_copy_blocks(t, t, torch.zeros(1, 2, dtype=torch.int64))
+
+
+def test_noalloc_rejects_a_batch_above_its_array_on_the_host(L):
+    """With the worker count given, the size check needs no device: a batch
+    whose partial results exceed the library's 32 MiB array is refused
+    before any HIP call (the pointers are never dereferenced)."""
+    fake = ctypes.c_void_p(0x1000)
+    code = L.pa_decode_append_noalloc(fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                      0.125, 64, 256, 64, 128, 16, 4, 1000, 40, 512, 0, None)
+    assert code == binding.PA_ERR_SCRATCH_LIMIT
+    assert b"static" in L.pa_strerror(code)
