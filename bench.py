@@ -68,6 +68,8 @@ def parse():
                     help="decode: per-worker timeline from the measurement build "
                          "(libpagedkv_trace.so, `python -m paged_kv_cache_59_amd.build --trace`), "
                          "one launch per step with a synchronisation after each; prints a summary")
+    ap.add_argument("--trace-dump", default=None,
+                    help="with --trace: also save every step's raw per-worker stamps (.npy)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run `steps` plain device copies of this many MiB (an elementwise "
                          "kernel reading and writing known bytes, to calibrate HBM counters)")
@@ -406,24 +408,29 @@ def trace_decode(args):
         if i >= args.warmup:
             runs.append(ws[:workers * S * 8].view(torch.int64).view(workers, S).cpu().numpy())
     kern_us = np.array([a.elapsed_time(b) * 1e3 for a, b in kev])
-    names = ["entry", "tables", "first_unit", "static_end", "stream_end", "stores_issued",
-             "helper_end"]
+    if args.trace_dump:
+        np.save(args.trace_dump, np.stack(runs))
+    names = ["entry", "tables", "first_unit", "stream_end", "stores_issued", "helper_end"]
     rel = {n: [] for n in names}
     spans = []
     per_xcd_end = []
+    per_xcd_rate = []
     for tr in runs:
-        live = tr[:, 0] > 0
-        tr = tr[live]
+        tr = tr[tr[:, 0] > 0]
         t0 = tr[:, 0].min()
         for j, n in enumerate(names):
             rel[n].append((tr[:, j] - t0) * 0.01)  # 100 MHz -> us
-        spans.append(((tr[:, 6].max() - t0) * 0.01, (tr[:, 4].max() - t0) * 0.01))
-        xcc = tr[:, 7] & 15
-        per_xcd_end.append([float(np.median((tr[xcc == x, 4] - t0) * 0.01)) for x in range(8)])
+        spans.append(((tr[:, 5].max() - t0) * 0.01, (tr[:, 3].max() - t0) * 0.01))
+        xcc = tr[:, 6] & 15
+        rate = (tr[:, 3] - tr[:, 2]) * 0.01 / np.maximum(tr[:, 7] - 1, 1)
+        per_xcd_end.append([float(np.median((tr[xcc == x, 3] - t0) * 0.01)) for x in range(8)])
+        per_xcd_rate.append([float(np.median(rate[xcc == x])) for x in range(8)])
     pct = lambda a: {"min": round(float(np.min(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
                      "median": round(float(np.median(a)), 2),
                      "p90": round(float(np.percentile(a, 90)), 2), "max": round(float(np.max(a)), 2)}
-    last = runs[-1][runs[-1][:, 0] > 0]
+    allw = np.concatenate([r[r[:, 0] > 0] for r in runs])
+    merges = allw[:, 9]
+    t_end = np.concatenate(rel["stream_end"])
     res = {
         "trace": w.name, "workers": workers, "steps": args.steps, "warmup": args.warmup,
         "kernel_us_events": pct(kern_us),
@@ -432,10 +439,17 @@ def trace_decode(args):
         "last_stream_end_us": pct([b for _, b in spans]),
         "median_stream_end_by_xcd_us": [round(float(np.median([p[x] for p in per_xcd_end])), 2)
                                         for x in range(8)],
-        "units_per_worker": pct(last[:, 8]), "pieces_per_worker": pct(last[:, 9]),
-        "merges_per_worker": pct(last[:, 10]), "claims_per_worker": pct(last[:, 11]),
+        "us_per_unit_by_xcd": [round(float(np.median([p[x] for p in per_xcd_rate])), 3)
+                               for x in range(8)],
+        "stream_end_us_by_merges": {int(m): round(float(np.median(t_end[merges == m])), 2)
+                                    for m in np.unique(merges) if (merges == m).sum() >= 20},
+        "units_per_worker": pct(allw[:, 7]), "pieces_per_worker": pct(allw[:, 8]),
+        "merges_per_worker": pct(merges),
+        "helper_busy_us_per_worker": pct(allw[:, 12] * 0.01),
+        "ring_wait_us_per_worker": pct(allw[:, 11] * 0.01),
         "note": "one launch per step, synchronised after each; stamps in us from the step's "
-                "earliest worker entry (s_memrealtime, 100 MHz)",
+                "earliest worker entry (s_memrealtime, 100 MHz); us_per_unit = (stream end - "
+                "first unit) / (units - 1)",
     }
     print(json.dumps(res), flush=True)
 

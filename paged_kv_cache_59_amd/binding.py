@@ -44,7 +44,7 @@ def use_trace_library() -> None:
     _LIB_PATH = path
 
 
-TRACE_SLOTS = 16  # per-worker 64-bit words the measurement build writes
+TRACE_SLOTS = 32  # per-worker 64-bit words the measurement build writes
 
 
 class PagedKVError(RuntimeError):

@@ -152,11 +152,11 @@ __device__ __forceinline__ uint64_t stamp_now() {
   if constexpr (kTrace) return __builtin_amdgcn_s_memrealtime();
   else return 0;
 }
-__device__ __forceinline__ uint64_t xcc_id() {
+[[maybe_unused]] __device__ __forceinline__ uint64_t xcc_id() {
   if constexpr (kTrace) return (uint64_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));
   else return 0;
 }
-__device__ __forceinline__ uint64_t hw_id() {
+[[maybe_unused]] __device__ __forceinline__ uint64_t hw_id() {
   if constexpr (kTrace) return (uint64_t)__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
   else return 0;
 }
@@ -622,6 +622,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         continue;
       }
       idle = 0;
+      const uint64_t t_round = stamp_now();
       int ps[kRing], ph[kRing], pu[kRing];
       int64_t pslot[kRing];
 #pragma unroll
@@ -686,12 +687,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           }
         }
       }
+      if constexpr (kTrace) {
+        __builtin_amdgcn_s_waitcnt(0);
+        tr[kTrHelperBusy] += stamp_now() - t_round;
+        ++tr[kTrHelperRounds];
+      }
     }
     if constexpr (kTrace) {
       __builtin_amdgcn_s_waitcnt(0);
       tr[kTrHelperEnd] = stamp_now();
       write_trace(kTrHelperEnd, kTrHelperEnd);
       write_trace(kTrMerges, kTrMerges);
+      write_trace(kTrHelperBusy, kTrHelperRounds);
     }
     return;
   }
@@ -728,6 +735,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   store_q();
   __builtin_amdgcn_wave_barrier();
   reset_run();
+  uint64_t t_iter = stamp_now();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
@@ -870,9 +878,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         // handed to the merger through the LDS ring (wait while the ring is
         // full, which the merger rarely lets happen).
         const int slot = piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
+        const uint64_t t_ring = stamp_now();
         for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
              ++spin)
           __builtin_amdgcn_s_sleep(1);
+        if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
         const int k = ring_made % kRing;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -909,11 +919,16 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int st = 0; st < kSets; ++st) vn_cur[st] = vn_nxt[st];
     }
     nxt2 = nxt3;
+    if constexpr (kTrace) {
+      const uint64_t now = stamp_now();
+      for (int i = 0; i < 7; ++i) tr[kTrLastIters + i] = tr[kTrLastIters + i + 1];
+      tr[kTrLastIters + 7] = now - t_iter;
+      t_iter = now;
+    }
     __builtin_amdgcn_wave_barrier();
   }
 
   tr[kTrStreamEnd] = stamp_now();
-  tr[kTrStaticEnd] = tr[kTrStreamEnd];
   finish();
   store_new_rows();
   if constexpr (kTrace) {
@@ -922,7 +937,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     tr[kTrHwId] = hw_id();
     write_trace(kTrEntry, kTrStoresIssued);  // (the helper writes its own slots)
     write_trace(kTrXcc, kTrPieces);
-    write_trace(kTrClaims, kTrHwId);
+    write_trace(kTrHwId, kTrRingWait);
+    write_trace(kTrLastIters, kTrLastIters + 7);
   }
 }
 

@@ -49,12 +49,11 @@ constexpr bool kTrace = true;
 #else
 constexpr bool kTrace = false;
 #endif
-constexpr int kTraceSlots = 16;
+constexpr int kTraceSlots = 32;
 enum {
   kTrEntry = 0,     // kernel entry (s_memrealtime, 100 MHz)
   kTrTables,        // lengths and unit offsets in LDS
   kTrFirstUnit,     // first unit's logits and softmax done (its K has arrived)
-  kTrStaticEnd,     // last unit of the worker's static share done
   kTrStreamEnd,     // streamer's last unit done
   kTrStoresIssued,  // fused append: new rows' stores issued
   kTrHelperEnd,     // helper wave done (last merge written)
@@ -62,8 +61,11 @@ enum {
   kTrUnits,         // units the streamer processed
   kTrPieces,        // cut pieces handed to the helper
   kTrMerges,        // runs the helper merged
-  kTrClaims,        // tail chunks claimed
   kTrHwId,          // HW_ID register (CU, SIMD) of the streamer
+  kTrRingWait,      // streamer: ticks waiting for room in the ring to the helper
+  kTrHelperBusy,    // helper: ticks in rounds (pieces written, counted, merged)
+  kTrHelperRounds,  // helper: rounds
+  kTrLastIters = 16,  // streamer: durations (ticks) of its last 8 iterations, oldest first
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
