@@ -22,7 +22,7 @@ TRACE_LIB_PATH = os.path.join(PKG, "libpagedkv_trace.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip",
-           "pa_probe.hip", "pa_block_manager.cpp"]
+           "pa_prefix.hip", "pa_probe.hip", "pa_block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

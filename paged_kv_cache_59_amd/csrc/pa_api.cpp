@@ -11,7 +11,7 @@
 namespace {
 
 constexpr int kVersion = 500;  // 0.5.0
-constexpr int kMaxGroup = 4;   // query heads per KV head the decode kernel holds
+using pa::kMaxGroup;
 constexpr int kMaxGridYZ = 65535;
 
 bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
@@ -204,7 +204,15 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_workers = w;
-  a.cached_loads = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
+  // Batches whose sequences share prefix blocks: per launch, the prefix pass
+  // (pa_prefix.hip) finds the groups of sequences with a common prefix and
+  // attends every group's query rows to its prefix once; the decode kernel
+  // covers the rest of each sequence and folds both together.
+  const bool shared = fused && (flags & PA_DECODE_SHARED_BLOCKS);
+  // chunks of the longest prefix a group can have (one short of the
+  // longest context, in whole 64-token units)
+  const int max_chunks = pa::prefix_chunks(
+      (max_context_len > 0 ? max_context_len - 1 : 0) / pa::kGroupTokens * pa::kGroupTokens);
   (void)hipGetLastError();
   // launches on one stream run in order, so they share the workspace
   for (int64_t s0 = 0; s0 < num_seqs; s0 += per_launch) {
@@ -225,6 +233,32 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     }
     hipEvent_t start = s0 == 0 ? kernel_start : nullptr;
     hipEvent_t stop = s0 + n >= num_seqs ? kernel_stop : nullptr;
+    if (shared) {
+      pa::PrefixArgs p{};
+      p.q = a.q;
+      p.k_cache = a.k_cache;
+      p.v_cache = a.v_cache;
+      p.block_tables = a.block_tables;
+      p.context_lens = a.context_lens;
+      p.scale_log2 = a.scale_log2;
+      p.num_seqs = (int)n;
+      p.num_q_heads = num_q_heads;
+      p.num_kv_heads = num_kv_heads;
+      p.head_dim = head_dim;
+      p.block_size = block_size;
+      p.max_blocks_per_seq = max_blocks_per_seq;
+      p.num_blocks = num_blocks;
+      p.max_context_len = max_context_len;
+      p.max_chunks = max_chunks > 0 ? max_chunks : 1;  // (the workgroups of chunk 0 write pre_len)
+      p.pre_len = a.ws.pre_len;
+      p.pre_o = a.ws.pre_o;
+      p.pre_lse = a.ws.pre_lse;
+      if (pa::launch_prefix(p, stream, start) != hipSuccess) return PA_ERR_HIP;
+      start = nullptr;
+      a.pre_len = a.ws.pre_len;
+      a.pre_o = a.ws.pre_o;
+      a.pre_lse = a.ws.pre_lse;
+    }
     if (pa::launch_decode(a, stream, start, stop) != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

@@ -134,15 +134,10 @@ __device__ __forceinline__ half8_t load_nt(const half_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(p));
 }
 
-// K/V tile loads: non-temporal when every block is read once (measured
-// 9-12% faster on batches that share nothing), through the caches when
-// sequences share blocks, whose repeat reads then hit L2 (20% faster on a
-// batch of 8-sequence groups sharing 1,024-token prefixes).
-template <bool Cached>
-__device__ __forceinline__ half8_t load_kv(const half_t* p) {
-  if constexpr (Cached) return *reinterpret_cast<const half8_t*>(p);
-  else return load_nt(p);
-}
+// K/V tile loads: non-temporal, every block is read once (measured 9-12%
+// faster than loads through the caches on batches that share nothing).
+// Prefix blocks that sequences share are read by the prefix pass instead.
+__device__ __forceinline__ half8_t load_kv(const half_t* p) { return load_nt(p); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -188,7 +183,11 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 
 }  // namespace
 
-template <int D, int BS, bool Fused, bool Cached>
+// Shared: the batch's shared prefixes were attended by the prefix pass (one
+// pass per group over its common blocks, results in out and pre_lse); each
+// run covers its sequence's positions from a.pre_len[s] on, and its result
+// is folded together with the prefix pass's.
+template <int D, int BS, bool Fused, bool Shared>
 __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
@@ -241,27 +240,50 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int G = Hq / Hkv;
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
+  int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
 
   auto units_for = [](int c) { return (c + kGroupTokens - 1) / kGroupTokens; };
+  // units of each of s's runs (Shared: of the positions after its prefix pass's)
+  auto run_units = [&](int s) {
+    return units_for(Shared ? len_lds[s] - base_lds[s] : len_lds[s]);
+  };
 
   // ---- lengths into LDS; zero the rows of empty sequences ----------------
+  // (the lengths of up to 4 x 64 sequences are loaded at once: one memory
+  // latency per 256 sequences rather than per 64)
+  constexpr int kLenBatch = 4;
   int carry = 0;  // uniform
-  for (int c0 = 0; c0 < S; c0 += 64) {
-    const int s = c0 + lane;
-    const int c = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
-    const int n = units_for(c);
-    const int incl = wave_inclusive_scan(n, lane);
-    if (streamer && s < S) {
-      off_lds[s] = carry + incl - n;
-      len_lds[s] = c;
+  for (int cb = 0; cb < S; cb += 64 * kLenBatch) {
+    int len_in[kLenBatch], pre_in[kLenBatch];
+#pragma unroll
+    for (int b = 0; b < kLenBatch; ++b) {
+      const int s = cb + 64 * b + lane;
+      len_in[b] = s < S ? a.context_lens[s] : 0;
+      pre_in[b] = (Shared && s < S) ? a.pre_len[s] : 0;
     }
-    carry += __builtin_amdgcn_readlane(incl, 63);
-    uint64_t empty = streamer ? __ballot(s < S && n == 0 && (s % nw) == w) : 0;
-    while (empty) {
-      const int se = c0 + __builtin_ctzll(empty);
-      empty &= empty - 1;
-      half_t* o = a.out + (int64_t)se * Hq * D;
-      for (int e = lane; e < Hq * D; e += 64) o[e] = (half_t)0.0f;
+#pragma unroll
+    for (int b = 0; b < kLenBatch; ++b) {
+      const int c0 = cb + 64 * b;
+      if (c0 >= S) break;
+      const int s = c0 + lane;
+      const int c = s < S ? min(max(len_in[b], 0), a.max_context_len) : 0;
+      // Shared: positions [0, pre) were attended by the prefix pass (pre <= c - 1)
+      const int pre = (Shared && s < S) ? min(max(pre_in[b], 0), max(c - 1, 0)) : 0;
+      const int n = units_for(c - pre);
+      const int incl = wave_inclusive_scan(n, lane);
+      if (streamer && s < S) {
+        off_lds[s] = carry + incl - n;
+        len_lds[s] = c;
+        if constexpr (Shared) base_lds[s] = pre;
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+      uint64_t empty = streamer ? __ballot(s < S && n == 0 && (s % nw) == w) : 0;
+      while (empty) {
+        const int se = c0 + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        half_t* o = a.out + (int64_t)se * Hq * D;
+        for (int e = lane; e < Hq * D; e += 64) o[e] = (half_t)0.0f;
+      }
     }
   }
   const int U = carry * Hkv;  // all units (the host bounds this below 2^31)
@@ -277,21 +299,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         for (int i = first; i <= last; ++i) a.ws.trace[(int64_t)w * kTraceSlots + i] = tr[i];
     }
   };
-
-  // ---- shares ------------------------------------------------------------------
-  // share j: units [sb(j), sb(j+1)), sb(j) = floor(j U / P), in (sequence,
-  // head, unit) order
-  const bool narrow = (int64_t)U * P < ((int64_t)1 << 31);  // 32-bit share arithmetic suffices
-  auto sb = [&](int j) -> int {
-    return narrow ? (int)((unsigned)(j * U) / (unsigned)P) : (int)((int64_t)j * U / P);
-  };
-  auto share_of = [&](int u) -> int {  // the share holding unit u
-    return narrow ? (int)((unsigned)((u + 1) * P - 1) / (unsigned)U)
-                  : (int)(((int64_t)(u + 1) * P - 1) / U);
-  };
-  // Partial slots: [0, R) the piece that starts run r, R + j the piece that
-  // starts share j inside a run.
-  const int R = S * Hkv;
 
   // the sequence holding head index `key`: the last s with off[s] <= key (a
   // 64-ary search over the LDS prefix sums)
@@ -309,17 +316,117 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     return uniform(lo);
   };
 
+  // ---- shares ------------------------------------------------------------------
+  // The streamer's time goes to units and, at the end of each run, to the
+  // run's sums, its hand-over to the merger and the next run's q rows (on
+  // batches of short runs about 2.4 us per unit and 1.1 us per run end).
+  // With more runs than workers, shares are equal in that cost, kUnitCost
+  // per unit and kRunCost per run:
+  // unit g of run (s, h) sits at position
+  //   Hkv (kUnitCost off[s] + kRunCost s) + h (kUnitCost n_s + kRunCost) + kRunCost + kUnitCost g
+  // of a total C, and share j holds the units at positions in
+  // [ceil(j C / P), ceil((j + 1) C / P)), in (sequence, head, unit) order.
+  // Otherwise (a few long runs per worker at most, where the run ends weigh
+  // little) shares are equal in units, share j = [floor(j U / P),
+  // floor((j + 1) U / P)), which costs the workers less to find.
+  const bool by_cost = S * Hkv > P;
+  constexpr int kUnitCost = 4, kRunCost = 2;
+  const int64_t C = (int64_t)kUnitCost * U + (int64_t)kRunCost * S * Hkv;
+  // 32-bit arithmetic when j C and pos P fit (64-bit division is emulated,
+  // several times slower)
+  const bool narrow = (int64_t)P * C < ((int64_t)1 << 31);
+  auto seq_pos = [&](int s) -> int64_t {
+    return (int64_t)Hkv * ((int64_t)kUnitCost * uniform(off_lds[s]) + (int64_t)kRunCost * s);
+  };
+  // the last sequences s with seq_pos(s) <= T0 and <= T1 (one pass of the
+  // 64-ary search of find_head for both)
+  auto find_pos2 = [&](int64_t T0, int64_t T1, int& s0, int& s1) {
+    int stride = 1;
+    while (stride * 64 < S) stride *= 64;
+    int lo0 = 0, lo1 = 0;
+    while (true) {
+      const int i0 = lo0 + lane * stride, i1 = lo1 + lane * stride;
+      const int64_t p0 = i0 < S ? (int64_t)Hkv * ((int64_t)kUnitCost * off_lds[i0] + (int64_t)kRunCost * i0) : T0 + 1;
+      const int64_t p1 = i1 < S ? (int64_t)Hkv * ((int64_t)kUnitCost * off_lds[i1] + (int64_t)kRunCost * i1) : T1 + 1;
+      lo0 += (__popcll(__ballot(p0 <= T0)) - 1) * stride;
+      lo1 += (__popcll(__ballot(p1 <= T1)) - 1) * stride;
+      if (stride == 1) break;
+      stride >>= 6;
+    }
+    s0 = uniform(lo0);
+    s1 = uniform(lo1);
+  };
+  // the first unit at cost position >= T inside sequence s (the last with
+  // seq_pos(s) <= T), or the next sequence's first: unit u = (s, h, g), or
+  // h = Hkv / g = n_s when it is the next run's (the caller's cursor steps)
+  struct ShareStart {
+    int u, h, g;
+  };
+  auto start_in = [&](int64_t T, int s) -> ShareStart {
+    const int n_s = uniform(run_units(s));
+    const int u_s = Hkv * uniform(off_lds[s]);
+    if (n_s == 0) return {u_s, Hkv, 0};  // (the next sequence's first unit)
+    const int t1 = (int)(T - seq_pos(s));  // < Hkv (kUnitCost n_s + kRunCost)
+    const int cr = kUnitCost * n_s + kRunCost;
+    const int h = (int)((unsigned)t1 / (unsigned)cr);
+    const int t2 = t1 - h * cr;
+    const int g = t2 <= kRunCost ? 0 : (t2 - kRunCost + kUnitCost - 1) / kUnitCost;
+    return {g >= n_s ? u_s + (h + 1) * n_s : u_s + h * n_s + g, h, g};
+  };
+  auto share_pos = [&](int j) -> int64_t {  // ceil(j C / P)
+    return narrow ? (int64_t)(((unsigned)j * (unsigned)C + P - 1) / (unsigned)P)
+                  : ((int64_t)j * C + P - 1) / P;
+  };
+  // the share holding unit u
+  const bool narrow_u = (int64_t)U * P < ((int64_t)1 << 31);
+  auto share_of = [&](int u) -> int {
+    if (!by_cost)
+      return narrow_u ? (int)((unsigned)((u + 1) * P - 1) / (unsigned)U)
+                      : (int)(((int64_t)(u + 1) * P - 1) / U);
+    const int s = find_head(u / Hkv);
+    const int n_s = uniform(run_units(s));
+    const int r = u - Hkv * uniform(off_lds[s]);
+    const int h = r / n_s, g = r - h * n_s;
+    const int64_t pos = seq_pos(s) + (int64_t)h * (kUnitCost * n_s + kRunCost) + kRunCost + kUnitCost * g;
+    return narrow ? (int)((unsigned)pos * (unsigned)P / (unsigned)C) : (int)(pos * P / C);
+  };
+  // this worker's share [my_first, my_end) (a share can come out empty when
+  // C / P is small)
+  auto unit_sb = [&](int j) -> int {
+    return narrow_u ? (int)((unsigned)(j * U) / (unsigned)P) : (int)((int64_t)j * U / P);
+  };
+  int first_s = -1;
+  ShareStart first{0, Hkv, 0};
+  int my_first, my_end;
+  if (by_cost) {
+    int end_s;
+    const int64_t T_first = share_pos(w), T_end = share_pos(w + 1);
+    find_pos2(T_first, w + 1 < P ? T_end : T_first, first_s, end_s);
+    first = start_in(T_first, first_s);
+    my_first = first.u;
+    my_end = w + 1 < P ? start_in(T_end, end_s).u : U;
+  } else {
+    my_first = unit_sb(w);
+    my_end = unit_sb(w + 1);
+  }
+  if (my_first >= my_end) return;
+  // Partial slots: [0, R) the piece that starts run r, R + j the piece that
+  // starts share j inside a run.
+  const int R = S * Hkv;
+
   // ---- cursors over units --------------------------------------------------
   struct Cursor {
     int s, h, g;   // sequence, KV head, unit of the run
     int n_s, len;  // units and length of s
+    int base;      // positions before the run's unit 0 (Shared: its prefix pass's)
     int left;      // units of the worker's share from this one on
     bool valid;    // false past the worker's last unit (then a copy of it)
   };
   auto set_seq = [&](Cursor& c, int s) {
     c.s = s;
     c.len = uniform(len_lds[s]);
-    c.n_s = units_for(c.len);
+    c.base = Shared ? uniform(base_lds[s]) : 0;
+    c.n_s = units_for(c.len - c.base);
   };
   auto locate = [&](int u) {
     Cursor c;
@@ -381,7 +488,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   auto load_table = [&](const Cursor& c) {
     const int32_t* row = a.block_tables + (int64_t)c.s * a.max_blocks_per_seq;
     const int last = (c.len + BS - 1) / BS - 1;
-    return row[min(NBU * c.g + (lane % NBU), last)];
+    return row[min(c.base / BS + NBU * c.g + (lane % NBU), last)];
   };
   // The NBU physical ids (uniform) from such a load; an id outside the pool
   // (a broken table) reads pool block 0 instead.
@@ -404,8 +511,21 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int phys = (e >= 0 && e < a.num_blocks) ? e : 0;
     const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
                        (lane % BS) * kChunk;
+    if constexpr (Fused) {
+      // the run's last unit holds the new token (position len - 1, which the
+      // pools do not hold yet): its lane reads the K row from k_new
+      const int tn = c.len - 1 - (c.base + c.g * kGroupTokens);
+      if (tn < kGroupTokens) {  // (uniform)
+        const half_t* np = a.k_new + ((int64_t)c.s * Hkv + c.h) * D;
+        const bool mine = lane == tn;
 #pragma unroll
-    for (int cc = 0; cc < kChunks; ++cc) kreg[cc] = load_kv<Cached>(kp + cc * (BS * kChunk));
+        for (int cc = 0; cc < kChunks; ++cc)
+          kreg[cc] = load_kv(mine ? np + cc * kChunk : kp + cc * (BS * kChunk));
+        return;
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < kChunks; ++cc) kreg[cc] = load_kv(kp + cc * (BS * kChunk));
   };
   // V group g (tokens 8g..8g+7 of the unit) is group g % kGroups of the
   // unit's block g / kGroups: for a fixed 64-dim range one 1 KiB load
@@ -415,7 +535,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const half_t* vp = a.v_cache + (int64_t)pb[g / kGroups] * block_stride +
                          (int64_t)c.h * kTile + (int64_t)(g % kGroups) * D * kChunk;
 #pragma unroll
-      for (int st = 0; st < kSets; ++st) vreg[g][st] = load_kv<Cached>(vp + (st * 64 + lane) * kChunk);
+      for (int st = 0; st < kSets; ++st) vreg[g][st] = load_kv(vp + (st * 64 + lane) * kChunk);
     }
   };
   // q rows of c's run; every lane loads (rows past G and lanes past the rows
@@ -432,18 +552,15 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       *reinterpret_cast<half8_t*>(q_lds + q_row * kQRow + q_chunk * kChunk) = v;
     }
   };
-  // Fused append: the new token of sequence s sits at position len - 1.  The
-  // units attend to positions < len - 1 from the pools; the piece that ends
-  // the run folds the new row in from k_new / v_new.  The rows of a unit's
-  // run are loaded with the unit's K in every iteration, whether or not the
-  // unit ends its run, so that every iteration issues the same loads.  Lane l holds dims 2l, 2l+1
-  // of the K row (lanes past D/2 take no part) and dims 64 st + l of the V row.
-  const int kn_dim = (2 * lane) % D;
-  const bool kn_lane = 2 * lane < D;
-  auto load_new = [&](const Cursor& c, uint32_t& kn, half_t (&vn)[kSets]) {
+  // Fused append: the new token of sequence s sits at position len - 1, in
+  // the last unit of each of s's runs, where it takes part in the unit's
+  // logits and weights like any other position: its lane's K row comes from
+  // k_new (load_k), and its V element is put into the unit's V tile from
+  // v_new.  The V row is loaded with every unit (lane l: dims 64 st + l), so
+  // that every iteration issues the same loads.
+  auto load_new = [&](const Cursor& c, half_t (&vn)[kSets]) {
     if constexpr (Fused) {
       const int64_t row = ((int64_t)c.s * Hkv + c.h) * D;
-      kn = *reinterpret_cast<const uint32_t*>(a.k_new + row + kn_dim);
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
     }
@@ -457,7 +574,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // [chunk][slot][8], V as 8 elements at [slot / 8][dim][slot % 8].
   auto store_new_rows = [&]() {
     if constexpr (Fused) {
-      const int first = sb(w), end = sb(w + 1);
+      const int first = my_first, end = my_end;
       const int ch = lane & 15;
       int my_s = -1, my_h = 0, grp = 0;
       auto flush = [&]() {
@@ -555,7 +672,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     m.lsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kF; ++j) m.acc[j] = 0.0f;
-    const int n = units_for(uniform(len_lds[s]));
+    const int n = uniform(run_units(s));
     const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
     const int r = s * Hkv + kvh;
     const int va = share_of(u0), vb = share_of(u0 + n - 1);
@@ -572,6 +689,26 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         absorb(std::integral_constant<int, 4>{}, m, sl, nb);
       else
         absorb(std::integral_constant<int, 16>{}, m, sl, nb);
+    }
+    // Shared: the prefix pass's chunks, each a piece of weight 1 (in lane
+    // pq = 0 of each row) at its log-sum-exp
+    if constexpr (Shared) {
+      const int nch = prefix_chunks(uniform(base_lds[s]));
+      for (int c = 0; c < nch; ++c) {
+        const bool valid = gq < G;
+        const int64_t qrow = (int64_t)c * S * Hq + (int64_t)s * Hq + kvh * G + (valid ? gq : 0);
+        const float m_p = valid ? a.pre_lse[qrow] : -INFINITY;
+        float ov[kF];
+#pragma unroll
+        for (int j = 0; j < kF; ++j) ov[j] = (float)a.pre_o[qrow * D + pq * kF + j];
+        const float m_new = fmaxf(m.mx, m_p);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m.mx - m_new);
+        const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
+        m.lsum = m.lsum * alpha + (pq == 0 ? wt : 0.0f);
+        m.mx = m_new;
+#pragma unroll
+        for (int j = 0; j < kF; ++j) m.acc[j] = m.acc[j] * alpha + wt * ov[j];
+      }
     }
     return m;
   };
@@ -611,6 +748,55 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // others count their arrivals (one lane each, by units); wait once; the
     // piece that completes its run's count merges.
     int cons = 0;
+    // Shared: the items come in the order of the runs of this worker's
+    // share.  The prefix pieces of the next run, when it will end whole here,
+    // are loaded into registers at the end of a round, while the streamer is
+    // still on that run; a whole run without them loads them when it comes.
+    int pf_run = -1;  // s * Hkv + h of the run whose pieces pf_* hold
+    half_t pf_o[kPrefixMaxChunks][4][kSets];  // dims 64 st + lane of head g, chunk c
+    float pf_m[kPrefixMaxChunks];             // lane g < G: head g's log-sum-exp, chunk c
+    auto load_pieces = [&](int s, int hh) {
+      const int nch = prefix_chunks(uniform(base_lds[s]));
+#pragma unroll
+      for (int c = 0; c < kPrefixMaxChunks; ++c) {
+        const int64_t row0 = ((int64_t)c * S + s) * Hq + hh * G;
+        pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, G - 1)] : -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int st = 0; st < kSets; ++st)
+            pf_o[c][g][st] = (c < nch && g < G) ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
+      }
+      pf_run = s * Hkv + hh;
+    };
+    // the run after (s, hh) in (sequence, head) order, and whether it lies
+    // whole in this worker's share with a prefix
+    int nx_s = -1, nx_h = 0;
+    auto next_run = [&](int s, int hh) {
+      Cursor c;
+      set_seq(c, s);
+      c.h = hh;
+      c.g = c.n_s - 1;
+      c.left = 2;
+      c = step(c);
+      const int u0 = Hkv * uniform(off_lds[c.s]) + c.h * c.n_s;
+      const bool whole = u0 >= my_first && u0 + c.n_s <= my_end && uniform(base_lds[c.s]) > 0 &&
+                         (c.s != s || c.h != hh);
+      nx_s = whole ? c.s : -1;
+      nx_h = c.h;
+    };
+    if constexpr (Shared) {
+      // the share's first run, when it starts the share and ends in it, else the next
+      Cursor c = locate(my_first);
+      if (c.g == 0 && Hkv * uniform(off_lds[c.s]) + (c.h + 1) * c.n_s <= my_end &&
+          uniform(base_lds[c.s]) > 0) {
+        nx_s = c.s;
+        nx_h = c.h;
+      } else {
+        next_run(c.s, c.h);
+      }
+      if (nx_s >= 0) load_pieces(nx_s, nx_h);
+    }
     for (int idle = 0; idle < kSpinLimit;) {
       const int avail = min(lds_ld(&ctl[kCtlRingMade]) - cons, kRing);
       if (avail == 0) {
@@ -625,6 +811,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const uint64_t t_round = stamp_now();
       int ps[kRing], ph[kRing], pu[kRing];
       int64_t pslot[kRing];
+      int last_s = 0, last_h = 0;  // the round's last item
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
@@ -633,54 +820,113 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           ph[i] = lds_ld(&ring_meta[k][1]);
           pslot[i] = lds_ld(&ring_meta[k][2]);
           pu[i] = lds_ld(&ring_meta[k][3]);
+          last_s = ps[i];
+          last_h = ph[i];
         }
       }
-      // lane i < avail: piece i's run counter and units
+      // lane i < avail: piece i's run counter and units (whole runs: none)
       int ci = 0, ui = 0, seen = 0;
+      bool counted = false;
       if (lane < avail) {
         int si = ps[0], hi = ph[0];
+        int64_t sli = pslot[0];
         ui = pu[0];
 #pragma unroll
         for (int i = 1; i < kRing; ++i)
-          if (lane == i) si = ps[i], hi = ph[i], ui = pu[i];
+          if (lane == i) si = ps[i], hi = ph[i], ui = pu[i], sli = pslot[i];
         ci = si * Hkv + hi;
-        seen = load_through_i(a.ws.counters + ci);
+        counted = sli >= 0;
+        if (counted) seen = load_through_i(a.ws.counters + ci);
       }
-      // the pieces: into registers, release their entries, write them through
+      // the entries into registers, then release them
+      float pv[kRing][4][kSets], pml[kRing];
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
           const int k = (cons + i) % kRing;
-          float pv[4][kSets];
 #pragma unroll
           for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int st = 0; st < kSets; ++st) pv[g][st] = ring_o[k][g * D + st * 64 + lane];
-          const float pml = lane < 8 ? ring_ml[k][lane] : 0.0f;
+            for (int st = 0; st < kSets; ++st) pv[i][g][st] = ring_o[k][g * D + st * 64 + lane];
+          pml[i] = lane < 8 ? ring_ml[k][lane] : 0.0f;
+        }
+      }
+      cons += avail;
+      lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        if (i < avail && pslot[i] < 0) {
+          // a whole run: its output rows (Shared: with the prefix pass's
+          // chunks folded in, each a piece of weight 1 at its log-sum-exp)
+          const int s_i = ps[i];
+          const int nch = Shared ? prefix_chunks(uniform(base_lds[s_i])) : 0;
+          if (Shared && nch > 0 && pf_run != s_i * Hkv + ph[i]) load_pieces(s_i, ph[i]);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if (g < G) {
+              const float mr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g));
+              const float lt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g + 1));
+              const int64_t row = (int64_t)s_i * Hq + ph[i] * G + g;
+              float v[kSets], den = lt;
+#pragma unroll
+              for (int st = 0; st < kSets; ++st) v[st] = pv[i][g][st];
+              if (Shared && nch > 0) {
+                float mp[kPrefixMaxChunks], mx = mr;
+#pragma unroll
+                for (int c = 0; c < kPrefixMaxChunks; ++c) {
+                  mp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pf_m[c]), g));
+                  mx = fmaxf(mx, mp[c]);
+                }
+                const float a1 = fast_exp2(mr - mx);
+                den = lt * a1;
+#pragma unroll
+                for (int st = 0; st < kSets; ++st) v[st] *= a1;
+#pragma unroll
+                for (int c = 0; c < kPrefixMaxChunks; ++c) {
+                  const float wc = c < nch ? fast_exp2(mp[c] - mx) : 0.0f;
+                  den += wc;
+#pragma unroll
+                  for (int st = 0; st < kSets; ++st) v[st] += wc * (float)pf_o[c][g][st];
+                }
+              }
+              const float inv = 1.0f / den;
+              half_t* o = a.out + row * D;
+#pragma unroll
+              for (int st = 0; st < kSets; ++st) o[st * 64 + lane] = (half_t)(v[st] * inv);
+            }
+          }
+          if constexpr (kTrace) ++tr[kTrMerges];
+        } else if (i < avail) {
+          // a cut piece: written through to its slot
           float* po = a.ws.o + pslot[i] * 4 * D;
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             if (g < G)
 #pragma unroll
               for (int st = 0; st < kSets; ++st)
-                store_through(po + g * D + st * 64 + lane, pv[g][st]);
-          if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml);
+                store_through(po + g * D + st * 64 + lane, pv[i][g][st]);
+          if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml[i]);
         }
       }
-      cons += avail;
-      lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
-      __builtin_amdgcn_s_waitcnt(0);      // the slots are written through before they are counted
+      if constexpr (Shared) {
+        // the run after this round's last item: its pieces, if it will end whole here
+        next_run(last_s, last_h);
+        if (nx_s >= 0 && pf_run != nx_s * Hkv + nx_h) load_pieces(nx_s, nx_h);
+      }
+      // the slots are written through before they are counted (a round of
+      // whole runs alone waits for nothing)
+      if (__ballot(counted)) __builtin_amdgcn_s_waitcnt(0);
       int arr = 0;
-      if (lane < avail) {
-        const int n_i = units_for(len_lds[ci / Hkv]);
+      if (counted) {
+        const int n_i = run_units(ci / Hkv);
         arr = seen + ui == n_i ? seen
                                : __hip_atomic_fetch_add(a.ws.counters + ci, ui, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
-        if (i < avail) {
-          const int n = units_for(uniform(len_lds[ps[i]]));
+        if (i < avail && pslot[i] >= 0) {
+          const int n = uniform(run_units(ps[i]));
           if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n) {
             merge_out(ps[i], ph[i], merge_pieces(ps[i], ph[i]));
             if constexpr (kTrace) ++tr[kTrMerges];
@@ -713,8 +959,16 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // Lookahead: cur is computed, nxt has its K/V loads in flight and its ids in
   // pb_nxt, nxt2 has its table entries loading into tbl_nxt2.
   // the first unit: the start of this worker's share
-  Cursor cur = locate(sb(w));
-  cur.left = sb(w + 1) - sb(w);
+  Cursor cur;
+  if (first_s >= 0 && first.h < Hkv && first.g < uniform(run_units(first_s))) {
+    set_seq(cur, first_s);  // (found by the share search)
+    cur.h = first.h;
+    cur.g = first.g;
+    cur.valid = true;
+  } else {
+    cur = locate(my_first);
+  }
+  cur.left = my_end - my_first;
   Cursor nxt = next(cur);
   Cursor nxt2 = next(nxt);
   int pb_cur[NBU], pb_nxt[NBU];
@@ -725,10 +979,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // keep the prologue in loop order (all K loads, then all V loads): the
   // wait counts at the loop head are merged over both ways in
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t kn_cur = 0, kn_nxt = 0;
   half_t vn_cur[kSets] = {}, vn_nxt[kSets] = {};
   load_k(cur, tbl_cur);
-  load_new(cur, kn_cur, vn_cur);
+  load_new(cur, vn_cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, pb_cur);
   __builtin_amdgcn_sched_barrier(0);
@@ -740,9 +993,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
   while (cur.valid) {
-    const int t0 = cur.g * kGroupTokens;
-    // positions the pools supply (a fused append supplies the last one)
-    const int vis = Fused ? cur.len - 1 : cur.len;
+    const int t0 = cur.base + cur.g * kGroupTokens;  // position of the unit's first token
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.
@@ -765,23 +1016,21 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     blocks_of(tbl_nxt, pb_nxt);
     load_k(nxt, tbl_nxt);
     load_q(nxt);
-    load_new(nxt, kn_nxt, vn_nxt);
+    load_new(nxt, vn_nxt);
     // the unit after nxt2, computed while this unit's V is in flight
     const Cursor nxt3 = next(nxt2);
 
     // online softmax over these 64 positions
-    const bool live = (t0 + lane) < vis;
+    // (every unit holds at least one position: its first, t0 < len)
+    const bool live = (t0 + lane) < cur.len;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       half_t ph = (half_t)0.0f;
       if (g < G) {
         const float z = live ? sacc[g] * a.scale_log2 : -INFINITY;
         const float m_new = fmaxf(m_run[g], wave_max(z));
-        // a fused append's run can end in a unit with no pool position: a
-        // piece of that unit alone has no max yet (exponentials then 0)
-        const float m_ref = (Fused && m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run[g] - m_ref);
-        ph = (half_t)fast_exp2(z - m_ref);
+        const float alpha = fast_exp2(m_run[g] - m_new);  // 0 at the piece's first unit
+        ph = (half_t)fast_exp2(z - m_new);
         l_lane[g] = l_lane[g] * alpha + (float)ph;
 #pragma unroll
         for (int st = 0; st < kSets; ++st) acc_o[st][g] *= alpha;
@@ -793,17 +1042,33 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     if constexpr (kTrace) {
       if (tr[kTrUnits]++ == 0) tr[kTrFirstUnit] = stamp_now();
     }
-    // positions past the end (tail of the last block, and re-read blocks past
-    // it) in the sequence's last unit: V element := 0
-    if (t0 + kGroupTokens > vis) {
+    // The run's last unit: positions past the end (the tail of the last
+    // block, and blocks past it re-read) hold any bits, NaN included, and
+    // 0 * NaN is not 0, so their V elements are cleared; a fused append's
+    // new token (offset tn) takes its V element from v_new.  Lane l holds
+    // dim 64 st + l of 8 positions per 8-position group, two per 32-bit
+    // word, so each word takes one mask (uniform) and at most one insert.
+    const int t_end = cur.len - t0;  // positions of the unit (uniform)
+    if (Fused ? t_end <= kGroupTokens : t_end < kGroupTokens) {
+      const int tn = Fused ? t_end - 1 : kGroupTokens;
+      const int keep_end = Fused ? tn : t_end;  // positions < keep_end come from the pools
+      uint32_t vnw[kSets];
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+      for (int st = 0; st < kSets; ++st)
+        vnw[st] = (uint32_t)__builtin_bit_cast(uint16_t, vn_cur[st]) << (16 * (tn & 1));
+      static_for<0, 32>([&](auto iw) {
+        constexpr int word = decltype(iw)::value;  // word w: positions 2w, 2w + 1
+        constexpr int g = word / 4, i = word % 4;
+        const uint32_t keep = (2 * word < keep_end ? 0x0000ffffu : 0u) |
+                              (2 * word + 1 < keep_end ? 0xffff0000u : 0u);
+        const bool put = Fused && word == (tn >> 1);
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const bool dead = t0 + g * kChunk + e >= vis;
-#pragma unroll
-          for (int st = 0; st < kSets; ++st) vreg[g][st][e] = dead ? (half_t)0.0f : vreg[g][st][e];
+        for (int st = 0; st < kSets; ++st) {
+          uint4_t w = __builtin_bit_cast(uint4_t, vreg[g][st]);
+          w[i] = (w[i] & keep) | (put ? vnw[st] : 0u);
+          vreg[g][st] = __builtin_bit_cast(half8_t, w);
         }
+      });
     }
 
     __builtin_amdgcn_wave_barrier();
@@ -826,84 +1091,44 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
     // ---- end of a piece: the run or the share ends ------------------------
     const bool run_end = cur.g + 1 == cur.n_s;
-    if constexpr (Fused) {
-      if (run_end) {
-        // the new token: logits q_g . k_new (q rows of this run are in LDS),
-        // folded in with the running-max rescale
-        float zn[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          zn[g] = -INFINITY;
-          if (g < G) {
-            const half_t* qr = q_lds + g * kQRow + kn_dim;
-            const half_t k0 = __builtin_bit_cast(half_t, (uint16_t)(kn_cur & 0xffffu));
-            const half_t k1 = __builtin_bit_cast(half_t, (uint16_t)(kn_cur >> 16));
-            const float part = kn_lane ? (float)qr[0] * (float)k0 + (float)qr[1] * (float)k1 : 0.0f;
-            zn[g] = wave_sum(part) * a.scale_log2;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (g < G) {
-            const float m_new = fmaxf(m_run[g], zn[g]);
-            const float alpha = fast_exp2(m_run[g] - m_new);  // 0 when no position came before
-            const float pn = fast_exp2(zn[g] - m_new);
-            l_lane[g] = l_lane[g] * alpha + (lane == 0 ? pn : 0.0f);
-#pragma unroll
-            for (int st = 0; st < kSets; ++st)
-              acc_o[st][g] = acc_o[st][g] * alpha + pn * (float)vn_cur[st];
-            m_run[g] = m_new;
-          }
-        }
-      }
-    }
     if (run_end || !nxt.valid) {
       float l_tot[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) l_tot[g] = (g < G) ? wave_sum(l_lane[g]) : 1.0f;
-      if (piece_g0 == 0 && run_end) {
-        // the whole run is in this piece
+      // The piece goes to the merger through the LDS ring (wait while the
+      // ring is full, which the merger rarely lets happen): a whole run
+      // (slot -1), which the merger normalises and stores, or a cut piece: a
+      // piece that starts a run goes to slot r, the piece that starts this
+      // worker's share inside a run to slot R + w.  The streamer itself
+      // stores nothing inside the loop: a wave's memory operations complete
+      // in order, so a store here would hold back the K/V loads issued after
+      // it, a memory latency at every run end.
+      const int slot = (piece_g0 == 0 && run_end) ? -1 : piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
+      const uint64_t t_ring = stamp_now();
+      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
+           ++spin)
+        __builtin_amdgcn_s_sleep(1);
+      if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
+      const int k = ring_made % kRing;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (g < G) {
-            const float inv = 1.0f / l_tot[g];
-            half_t* o = a.out + ((int64_t)cur.s * Hq + cur.h * G + g) * D;
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int st = 0; st < kSets; ++st) o[st * 64 + lane] = (half_t)(acc_o[st][g] * inv);
-          }
-        }
-      } else {
-        // a cut piece: a piece that starts a run goes to slot r, the piece
-        // that starts this worker's share inside a run to slot R + w.  It is
-        // handed to the merger through the LDS ring (wait while the ring is
-        // full, which the merger rarely lets happen).
-        const int slot = piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
-        const uint64_t t_ring = stamp_now();
-        for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
-             ++spin)
-          __builtin_amdgcn_s_sleep(1);
-        if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
-        const int k = ring_made % kRing;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int st = 0; st < kSets; ++st)
-            ring_o[k][g * D + st * 64 + lane] = acc_o[st][g];
-        if (lane < 8) {  // (max, sum) of head lane/2
-          const int gi = lane >> 1;
-          const float mv = gi == 0 ? m_run[0] : gi == 1 ? m_run[1] : gi == 2 ? m_run[2] : m_run[3];
-          const float lv = gi == 0 ? l_tot[0] : gi == 1 ? l_tot[1] : gi == 2 ? l_tot[2] : l_tot[3];
-          ring_ml[k][lane] = (lane & 1) ? lv : mv;
-        }
-        if (lane == 0) {
-          ring_meta[k][0] = cur.s;
-          ring_meta[k][1] = cur.h;
-          ring_meta[k][2] = slot;
-          ring_meta[k][3] = cur.g - piece_g0 + 1;
-        }
-        lds_st(&ctl[kCtlRingMade], ++ring_made);
-        if constexpr (kTrace) ++tr[kTrPieces];
+        for (int st = 0; st < kSets; ++st)
+          ring_o[k][g * D + st * 64 + lane] = acc_o[st][g];
+      if (lane < 8) {  // (max, sum) of head lane/2
+        const int gi = lane >> 1;
+        const float mv = gi == 0 ? m_run[0] : gi == 1 ? m_run[1] : gi == 2 ? m_run[2] : m_run[3];
+        const float lv = gi == 0 ? l_tot[0] : gi == 1 ? l_tot[1] : gi == 2 ? l_tot[2] : l_tot[3];
+        ring_ml[k][lane] = (lane & 1) ? lv : mv;
       }
+      if (lane == 0) {
+        ring_meta[k][0] = cur.s;
+        ring_meta[k][1] = cur.h;
+        ring_meta[k][2] = slot;
+        ring_meta[k][3] = cur.g - piece_g0 + 1;
+      }
+      lds_st(&ctl[kCtlRingMade], ++ring_made);
+      if constexpr (kTrace) ++tr[kTrPieces];
       reset_run();
       q_pending = true;
       piece_g0 = nxt.g;
@@ -914,7 +1139,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     nxt = nxt2;
     tbl_nxt = tbl_nxt2;
     if constexpr (Fused) {
-      kn_cur = kn_nxt;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn_cur[st] = vn_nxt[st];
     }
@@ -952,6 +1176,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WorkspaceLayout {
   int64_t slots;
   size_t ml, o, partial;  // partial slots: offsets, end
+  size_t pre_len, pre_lse, pre_o, end;  // shared-prefix area (DecodeWorkspace)
   size_t control;         // arrival counters: size
 };
 
@@ -962,14 +1187,19 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t Hkv, int64_t D, int64_t work
   l.ml = kTrace ? align256((size_t)workers * kTraceSlots * sizeof(uint64_t)) : 0;
   l.o = l.ml + align256((size_t)(l.slots * 8) * sizeof(float));
   l.partial = l.o + align256((size_t)(l.slots * 4 * D) * sizeof(float));
-  l.control = align256((size_t)(S * Hkv) * sizeof(int));
+  const size_t pre_rows = (size_t)kPrefixMaxChunks * S * Hkv * kMaxGroup;
+  l.pre_len = l.partial;
+  l.pre_lse = l.pre_len + align256((size_t)S * sizeof(int));
+  l.pre_o = l.pre_lse + align256(pre_rows * sizeof(float));
+  l.end = l.pre_o + align256(pre_rows * D * sizeof(half_t));
+  l.control = decode_control_bytes(S, Hkv);
   return l;
 }
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers) {
   const WorkspaceLayout l = workspace_layout(S, Hkv, D, workers);
-  return l.partial + l.control;
+  return l.end + l.control;
 }
 
 size_t decode_control_bytes(int64_t S, int64_t Hkv) { return align256((size_t)(S * Hkv) * sizeof(int)); }
@@ -1027,23 +1257,26 @@ DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int6
   w.ml = reinterpret_cast<float*>(p + l.ml);
   w.o = reinterpret_cast<float*>(p + l.o);
   w.counters = reinterpret_cast<int*>(p + ((bytes - l.control) & ~(size_t)255));
+  w.pre_len = reinterpret_cast<int*>(p + l.pre_len);
+  w.pre_lse = reinterpret_cast<float*>(p + l.pre_lse);
+  w.pre_o = reinterpret_cast<half_t*>(p + l.pre_o);
   return w;
 }
 
-template <int D, int BS, bool Fused, bool Cached>
+template <int D, int BS, bool Fused, bool Shared>
 void launch_decode_f(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
-  const uint32_t lds = (uint32_t)((size_t)a.num_seqs * 2 * sizeof(int));
+  const uint32_t lds = (uint32_t)((size_t)a.num_seqs * (Shared ? 3 : 2) * sizeof(int));
   if (!start && !stop)
-    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Cached>), grid, dim3(128), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared>), grid, dim3(128), lds, stream, a);
   else  // the events take the kernel's own start and end times
-    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Cached>), grid, dim3(128), lds, stream,
+    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared>), grid, dim3(128), lds, stream,
                           start, stop, 0, a);
 }
 
 template <int D, int BS>
 void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (a.k_new && a.cached_loads)
+  if (a.k_new && a.pre_len)
     launch_decode_f<D, BS, true, true>(a, stream, start, stop);
   else if (a.k_new)
     launch_decode_f<D, BS, true, false>(a, stream, start, stop);

@@ -11,12 +11,14 @@ typedef _Float16 half_t;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockSize = 16;    // token slots per block (the default; 8 and 32 also built)
 constexpr int kChunk = 8;         // fp16 elements per 16-byte chunk
 constexpr int kGroupTokens = 64;  // tokens one wave handles per step of its loop (a "unit")
 constexpr int kWorkersPerCU = 2;  // decode waves per compute unit
 constexpr int kMaxWorkers = 1 << 16;
+constexpr int kMaxGroup = 4;      // query heads per KV head the decode kernel holds
 // Sequences one decode launch takes (their unit offsets and lengths sit in
 // LDS, 8 bytes each); the host splits larger batches into several launches.
 constexpr int kMaxSeqsPerLaunch = 4096;
@@ -40,6 +42,14 @@ struct DecodeWorkspace {
   float* o;       // [slots][4][D]
   int* counters;  // [S][Hkv] units arrived
   uint64_t* trace;  // measurement builds only: [workers][kTraceSlots] at the workspace's start
+  // Batches that share prefix blocks: per sequence the prefix length its
+  // group's pass attended ([S]), and per (chunk, sequence, query head) that
+  // pass's normalised row ([kPrefixMaxChunks][S][4 Hkv][D], fp16) and its
+  // log2-domain log-sum-exp ([kPrefixMaxChunks][S][4 Hkv]); rows are indexed
+  // (chunk * S + s) * num_q_heads + head.
+  int* pre_len;
+  half_t* pre_o;
+  float* pre_lse;
 };
 
 // Measurement builds (compiled with PA_DECODE_TRACE) put per-worker
@@ -123,9 +133,14 @@ struct DecodeArgs {
   const int64_t* slot_mapping;
   half_t* k_cache_w;
   half_t* v_cache_w;
-  // K/V loads through the caches (blocks shared between sequences meet in
-  // L2) instead of non-temporal loads (blocks read once)
-  int cached_loads;
+  // Batches whose sequences share prefix blocks (null otherwise): the
+  // prefix pass attended positions [0, pre_len[s]) of sequence s for every
+  // query head, in prefix_chunks(pre_len[s]) chunks, each a normalised row
+  // and a log-sum-exp (DecodeWorkspace); the decode covers the positions
+  // from pre_len[s] on and folds the pieces together.
+  const int* pre_len;
+  const half_t* pre_o;
+  const float* pre_lse;
 };
 
 // Read-bandwidth probe (sequential when order is null, else num_tiles tiles
@@ -165,5 +180,45 @@ struct PrefillArgs {
 constexpr int kPrefillStages = 4;
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Shared prefixes of a decode batch (pa_prefix.hip).  Sequences are taken
+// in windows of kPrefixWindow; a group is a run of at least two consecutive
+// sequences of one window, each holding its first 64-token units in the same
+// physical blocks as the one before, and its prefix P the multiple of 64
+// tokens they all hold so, short of every member's last position.  The pass
+// attends each group's query rows (members x heads of a KV group, at most 32)
+// to its P keys in prefix_chunks(P) chunks of prefix_chunk_len(P) keys (the
+// last shorter), one workgroup per (window, KV head, chunk).
+constexpr int kPrefixWindow = 8;
+constexpr int kPrefixMaxChunks = 4;
+constexpr int kPrefixChunkKeys = 512;  // chunk length while fewer than kPrefixMaxChunks
+__host__ __device__ inline int prefix_chunks(int P) {
+  if (P <= 0) return 0;
+  const int c = (P + kPrefixChunkKeys - 1) / kPrefixChunkKeys;
+  return c < kPrefixMaxChunks ? c : kPrefixMaxChunks;
+}
+__host__ __device__ inline int prefix_chunk_len(int P) {  // a multiple of 128 (4 waves x 32 keys)
+  const int c = prefix_chunks(P);
+  return c ? ((P + c - 1) / c + 127) / 128 * 128 : 0;
+}
+struct PrefixArgs {
+  const half_t* q;
+  const half_t* k_cache;
+  const half_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale_log2;  // softmax scale times log2(e)
+  int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int block_size;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_context_len;
+  int max_chunks;  // chunks of the longest possible prefix (grid dimension)
+  int* pre_len;    // [S] out
+  half_t* pre_o;   // out, as DecodeWorkspace
+  float* pre_lse;  // out, as DecodeWorkspace
+};
+// `start`, when not null, is an event bound to this launch's start.
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream, hipEvent_t start);
 
 }  // namespace pa

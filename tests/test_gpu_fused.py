@@ -107,6 +107,36 @@ def test_fused_prefix_sharing_with_copies(shared_blocks, BS, D):
               shared_blocks=shared_blocks)
 
 
+# Shared-prefix batches (shared-blocks flag): groups of sequences with a
+# common prefix are attended to it once by the prefix pass; the decode
+# covers the rest and folds both.  (groups, seqs, prefix tokens, suffix
+# range): groups across the 8-sequence windows the pass groups in, several
+# groups in one window, a prefix that is not a multiple of 64 (the pass
+# takes 64 of 96), one-token suffixes, groups of one (nothing shared), a
+# prefix in four chunks of 512 keys and one in four chunks of 768.
+PREFIX_CASES = [(2, 20, 256, (1, 150)), (4, 12, 96, (1, 80)), (3, 24, 1024, (1, 3)),
+                (8, 8, 128, (1, 40)), (2, 6, 2048, (100, 700)), (2, 6, 3072, (1, 64))]
+
+
+@pytest.mark.parametrize("groups,seqs,plen,suffix", PREFIX_CASES)
+@pytest.mark.parametrize("workers", [0, 1, 5000])
+def test_fused_shared_prefix_groups(groups, seqs, plen, suffix, workers):
+    w = wl.make_workload("prefix-groups", 350 + groups + seqs + plen, 16, 4, 128, num_seqs=seqs,
+                         prefix_groups=groups, prefix_len=plen, suffix_range=suffix)
+    run_fused(w, workers, f"prefix groups {groups}x{seqs // groups} P{plen} workers{workers}",
+              shared_blocks=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (8, 4, 128), (32, 8, 64)])
+@pytest.mark.parametrize("scale", [None, -0.3])
+def test_fused_shared_prefix_shapes(Hq, Hkv, D, scale):
+    """MHA, G = 2 and G = 4, both head dims; a negative scale (the prefix
+    pass flips q's sign)."""
+    w = wl.make_workload("prefix-shapes", 360 + Hq + Hkv + D, Hq, Hkv, D, num_seqs=18,
+                         prefix_groups=3, prefix_len=512, suffix_range=(1, 300), scale=scale)
+    run_fused(w, 0, f"prefix shapes Hq{Hq} Hkv{Hkv} D{D} scale{scale}", shared_blocks=True)
+
+
 def test_fused_padding_slot_attends_but_does_not_store():
     """slot < 0: the row enters the attention but the pools keep their bits."""
     w = wl.make_workload("fused-pad", 342, 8, 2, 128, context_lens=[70, 3, 200, 64])
