@@ -546,6 +546,27 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     qreg = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)c.s * Hq + c.h * G + row) * D +
                                              q_chunk * kChunk);
   };
+  // Shared: the prefix pass's first chunk for a run, loaded for a unit that
+  // starts the run one iteration ahead, ahead of that unit's K (rows: dims
+  // 64 st + lane of head g; lane g < G: head g's log-sum-exp).  A piece that
+  // starts a run begins from it, a piece of weight 1 at its log-sum-exp,
+  // instead of from nothing: the run's online softmax then takes the prefix
+  // in with no fold afterwards.  (Further chunks, of prefixes above one
+  // chunk, are folded by the merger.)
+  half_t pre_o[4][kSets];
+  float pre_m = 0.0f;
+  auto load_pre = [&](const Cursor& c) {
+    if constexpr (Shared) {
+      const int64_t row0 = (int64_t)c.s * Hq + c.h * G;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int st = 0; st < kSets; ++st)
+          pre_o[g][st] = g < G ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
+      pre_m = a.pre_lse[row0 + min(lane, G - 1)];
+    }
+  };
+  auto starts_with_pre = [&](const Cursor& c) { return Shared && c.valid && c.g == 0 && c.base > 0; };
   auto store_q = [&]() {
     if (q_row < 4) {
       const half8_t v = q_row < G ? qreg : half8_t{};
@@ -675,6 +696,24 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int n = uniform(run_units(s));
     const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
     const int r = s * Hkv + kvh;
+    // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
+    // starts the run began from chunk 0), loaded before the pieces so that
+    // the two round trips overlap
+    constexpr int NC = Shared ? kPrefixMaxChunks : 1;
+    typedef half_t hvec_t __attribute__((ext_vector_type(kF)));
+    float m_c[NC];
+    hvec_t o_c[NC];
+    int nch = 0;
+    if constexpr (Shared) {
+      nch = prefix_chunks(uniform(base_lds[s]));
+      const bool valid = gq < G;
+#pragma unroll
+      for (int c = 1; c < NC; ++c) {
+        const int64_t qrow = ((int64_t)min(c, max(nch - 1, 0)) * S + s) * Hq + kvh * G + (valid ? gq : 0);
+        m_c[c] = (c < nch && valid) ? a.pre_lse[qrow] : -INFINITY;
+        o_c[c] = c < nch ? *reinterpret_cast<const hvec_t*>(a.pre_o + qrow * D + pq * kF) : hvec_t{};
+      }
+    }
     const int va = share_of(u0), vb = share_of(u0 + n - 1);
     const int np_all = vb - va + 1;
     for (int p0 = 0; p0 < np_all; p0 += 16) {
@@ -690,24 +729,20 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       else
         absorb(std::integral_constant<int, 16>{}, m, sl, nb);
     }
-    // Shared: the prefix pass's chunks, each a piece of weight 1 (in lane
-    // pq = 0 of each row) at its log-sum-exp
+    // Shared: each chunk a piece of weight 1 (in lane pq = 0 of each row)
+    // at its log-sum-exp
     if constexpr (Shared) {
-      const int nch = prefix_chunks(uniform(base_lds[s]));
-      for (int c = 0; c < nch; ++c) {
-        const bool valid = gq < G;
-        const int64_t qrow = (int64_t)c * S * Hq + (int64_t)s * Hq + kvh * G + (valid ? gq : 0);
-        const float m_p = valid ? a.pre_lse[qrow] : -INFINITY;
-        float ov[kF];
 #pragma unroll
-        for (int j = 0; j < kF; ++j) ov[j] = (float)a.pre_o[qrow * D + pq * kF + j];
-        const float m_new = fmaxf(m.mx, m_p);
-        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m.mx - m_new);
-        const float wt = valid ? fast_exp2(m_p - m_new) : 0.0f;
-        m.lsum = m.lsum * alpha + (pq == 0 ? wt : 0.0f);
-        m.mx = m_new;
+      for (int c = 1; c < NC; ++c) {
+        if (c < nch) {
+          const float m_new = fmaxf(m.mx, m_c[c]);
+          const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m.mx - m_new);
+          const float wt = gq < G ? fast_exp2(m_c[c] - m_new) : 0.0f;
+          m.lsum = m.lsum * alpha + (pq == 0 ? wt : 0.0f);
+          m.mx = m_new;
 #pragma unroll
-        for (int j = 0; j < kF; ++j) m.acc[j] = m.acc[j] * alpha + wt * ov[j];
+          for (int j = 0; j < kF; ++j) m.acc[j] = m.acc[j] * alpha + wt * (float)o_c[c][j];
+        }
       }
     }
     return m;
@@ -738,6 +773,17 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
+  auto seed_pre = [&]() {  // a piece that starts a run with a prefix: begin from its first chunk
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (g < G) {
+        m_run[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre_m), g));
+        l_lane[g] = lane == 0 ? 1.0f : 0.0f;
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) acc_o[st][g] = (float)pre_o[g][st];
+      }
+    }
+  };
 
   // ---- the merger wave --------------------------------------------------------
   if (!streamer) {
@@ -748,17 +794,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // others count their arrivals (one lane each, by units); wait once; the
     // piece that completes its run's count merges.
     int cons = 0;
-    // Shared: the items come in the order of the runs of this worker's
-    // share.  The prefix pieces of the next run, when it will end whole here,
-    // are loaded into registers at the end of a round, while the streamer is
-    // still on that run; a whole run without them loads them when it comes.
-    int pf_run = -1;  // s * Hkv + h of the run whose pieces pf_* hold
+    // Shared: chunks 1.. of a whole run's prefix (the streamer began the run
+    // from chunk 0), loaded when the run comes
     half_t pf_o[kPrefixMaxChunks][4][kSets];  // dims 64 st + lane of head g, chunk c
     float pf_m[kPrefixMaxChunks];             // lane g < G: head g's log-sum-exp, chunk c
-    auto load_pieces = [&](int s, int hh) {
-      const int nch = prefix_chunks(uniform(base_lds[s]));
+    auto load_pieces = [&](int s, int hh, int nch) {
 #pragma unroll
-      for (int c = 0; c < kPrefixMaxChunks; ++c) {
+      for (int c = 1; c < kPrefixMaxChunks; ++c) {
         const int64_t row0 = ((int64_t)c * S + s) * Hq + hh * G;
         pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, G - 1)] : -INFINITY;
 #pragma unroll
@@ -767,36 +809,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           for (int st = 0; st < kSets; ++st)
             pf_o[c][g][st] = (c < nch && g < G) ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
       }
-      pf_run = s * Hkv + hh;
     };
-    // the run after (s, hh) in (sequence, head) order, and whether it lies
-    // whole in this worker's share with a prefix
-    int nx_s = -1, nx_h = 0;
-    auto next_run = [&](int s, int hh) {
-      Cursor c;
-      set_seq(c, s);
-      c.h = hh;
-      c.g = c.n_s - 1;
-      c.left = 2;
-      c = step(c);
-      const int u0 = Hkv * uniform(off_lds[c.s]) + c.h * c.n_s;
-      const bool whole = u0 >= my_first && u0 + c.n_s <= my_end && uniform(base_lds[c.s]) > 0 &&
-                         (c.s != s || c.h != hh);
-      nx_s = whole ? c.s : -1;
-      nx_h = c.h;
-    };
-    if constexpr (Shared) {
-      // the share's first run, when it starts the share and ends in it, else the next
-      Cursor c = locate(my_first);
-      if (c.g == 0 && Hkv * uniform(off_lds[c.s]) + (c.h + 1) * c.n_s <= my_end &&
-          uniform(base_lds[c.s]) > 0) {
-        nx_s = c.s;
-        nx_h = c.h;
-      } else {
-        next_run(c.s, c.h);
-      }
-      if (nx_s >= 0) load_pieces(nx_s, nx_h);
-    }
     for (int idle = 0; idle < kSpinLimit;) {
       const int avail = min(lds_ld(&ctl[kCtlRingMade]) - cons, kRing);
       if (avail == 0) {
@@ -811,7 +824,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const uint64_t t_round = stamp_now();
       int ps[kRing], ph[kRing], pu[kRing];
       int64_t pslot[kRing];
-      int last_s = 0, last_h = 0;  // the round's last item
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail) {
@@ -820,8 +832,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           ph[i] = lds_ld(&ring_meta[k][1]);
           pslot[i] = lds_ld(&ring_meta[k][2]);
           pu[i] = lds_ld(&ring_meta[k][3]);
-          last_s = ps[i];
-          last_h = ph[i];
         }
       }
       // lane i < avail: piece i's run counter and units (whole runs: none)
@@ -857,10 +867,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int i = 0; i < kRing; ++i) {
         if (i < avail && pslot[i] < 0) {
           // a whole run: its output rows (Shared: with the prefix pass's
-          // chunks folded in, each a piece of weight 1 at its log-sum-exp)
+          // chunks 1.. folded in, each a piece of weight 1 at its log-sum-exp)
           const int s_i = ps[i];
           const int nch = Shared ? prefix_chunks(uniform(base_lds[s_i])) : 0;
-          if (Shared && nch > 0 && pf_run != s_i * Hkv + ph[i]) load_pieces(s_i, ph[i]);
+          if (Shared && nch > 1) load_pieces(s_i, ph[i], nch);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             if (g < G) {
@@ -870,10 +880,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
               float v[kSets], den = lt;
 #pragma unroll
               for (int st = 0; st < kSets; ++st) v[st] = pv[i][g][st];
-              if (Shared && nch > 0) {
+              if (Shared && nch > 1) {
                 float mp[kPrefixMaxChunks], mx = mr;
 #pragma unroll
-                for (int c = 0; c < kPrefixMaxChunks; ++c) {
+                for (int c = 1; c < kPrefixMaxChunks; ++c) {
                   mp[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pf_m[c]), g));
                   mx = fmaxf(mx, mp[c]);
                 }
@@ -882,7 +892,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
                 for (int st = 0; st < kSets; ++st) v[st] *= a1;
 #pragma unroll
-                for (int c = 0; c < kPrefixMaxChunks; ++c) {
+                for (int c = 1; c < kPrefixMaxChunks; ++c) {
                   const float wc = c < nch ? fast_exp2(mp[c] - mx) : 0.0f;
                   den += wc;
 #pragma unroll
@@ -907,11 +917,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
                 store_through(po + g * D + st * 64 + lane, pv[i][g][st]);
           if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml[i]);
         }
-      }
-      if constexpr (Shared) {
-        // the run after this round's last item: its pieces, if it will end whole here
-        next_run(last_s, last_h);
-        if (nx_s >= 0 && pf_run != nx_s * Hkv + nx_h) load_pieces(nx_s, nx_h);
       }
       // the slots are written through before they are counted (a round of
       // whole runs alone waits for nothing)
@@ -975,6 +980,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int tbl_cur = load_table(cur);
   int tbl_nxt = load_table(nxt);
   load_q(cur);
+  if (starts_with_pre(cur)) load_pre(cur);
   blocks_of(tbl_cur, pb_cur);
   // keep the prologue in loop order (all K loads, then all V loads): the
   // wait counts at the loop head are merged over both ways in
@@ -988,6 +994,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   store_q();
   __builtin_amdgcn_wave_barrier();
   reset_run();
+  if (starts_with_pre(cur)) seed_pre();
   uint64_t t_iter = stamp_now();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
@@ -997,7 +1004,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.
-    if (q_pending) store_q();
+    if (q_pending) {
+      store_q();
+      if (starts_with_pre(cur)) seed_pre();
+    }
     q_pending = false;
 
     // logits: S[g][token lane] = q_g . K_token  (rows = heads, columns = tokens)
@@ -1010,6 +1020,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     }
     // keep the next unit's address work below the logits: hoisted above
     // them it would wait for this unit's whole K (and table) first
+    __builtin_amdgcn_sched_barrier(0);
+    // the next unit's prefix piece when it starts a run (issued ahead of its
+    // K, so that the waits for that K stay the same on both ways)
+    if (starts_with_pre(nxt)) load_pre(nxt);
     __builtin_amdgcn_sched_barrier(0);
     // table entries two units ahead, then the next unit's K and q
     const int tbl_nxt2 = load_table(nxt2);

@@ -188,18 +188,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // tokens they all hold so, short of every member's last position.  The pass
 // attends each group's query rows (members x heads of a KV group, at most 32)
 // to its P keys in prefix_chunks(P) chunks of prefix_chunk_len(P) keys (the
-// last shorter), one workgroup per (window, KV head, chunk).
+// last shorter), one workgroup of kPrefixWaves waves per (chunk, window, KV
+// head).
 constexpr int kPrefixWindow = 8;
+constexpr int kPrefixWaves = 8;
 constexpr int kPrefixMaxChunks = 4;
-constexpr int kPrefixChunkKeys = 512;  // chunk length while fewer than kPrefixMaxChunks
+constexpr int kPrefixChunkKeys = 1024;  // chunk length while fewer than kPrefixMaxChunks
 __host__ __device__ inline int prefix_chunks(int P) {
   if (P <= 0) return 0;
   const int c = (P + kPrefixChunkKeys - 1) / kPrefixChunkKeys;
   return c < kPrefixMaxChunks ? c : kPrefixMaxChunks;
 }
-__host__ __device__ inline int prefix_chunk_len(int P) {  // a multiple of 128 (4 waves x 32 keys)
+__host__ __device__ inline int prefix_chunk_len(int P) {  // a multiple of kPrefixWaves x 32 keys
+  constexpr int q = kPrefixWaves * 32;
   const int c = prefix_chunks(P);
-  return c ? ((P + c - 1) / c + 127) / 128 * 128 : 0;
+  return c ? ((P + c - 1) / c + q - 1) / q * q : 0;
 }
 struct PrefixArgs {
   const half_t* q;

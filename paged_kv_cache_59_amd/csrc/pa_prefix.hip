@@ -18,7 +18,7 @@
 // (seven comparisons of table rows), so no pass over the whole batch comes
 // first.
 //
-// Work: one workgroup per (chunk, window, KV head); its 4 waves take equal
+// Work: one workgroup per (chunk, window, KV head); its 8 waves take equal
 // slices of the chunk's keys, 32 keys per step, each wave reading its own
 // slice straight into registers, for the group's
 // rows (members x query heads of the KV group, at most 32):
@@ -62,14 +62,15 @@ __device__ __forceinline__ float sum4(float x) {
   return x + __shfl_xor(x, 32);
 }
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
+__global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const PrefixArgs a) {
+  constexpr int W = kPrefixWaves;
   constexpr int KS = D / 32;  // 32-dim steps of the contraction over D
   constexpr int DT = D / 16;  // 16-dim tiles of the output
   constexpr int NBS = 32 / BS;  // blocks per 32-key step
   static_assert(NBS * BS == 32 && KS * 32 == D, "block size 8, 16 or 32; head_dim 64 or 128");
   constexpr int64_t kTile = (int64_t)BS * D;
   constexpr int kORow = D + 4;  // floats per row of the waves' partial outputs in LDS
-  extern __shared__ __attribute__((aligned(16))) float comb_lds[];  // [4][kRows][kORow], [4][kRows][2]
+  extern __shared__ __attribute__((aligned(16))) float comb_lds[];  // [W][kRows][kORow], [W][kRows][2]
   constexpr int kQRow = D + 8;  // halves per query row in LDS
   __shared__ __attribute__((aligned(16))) half_t q_lds[kRows * kQRow];
   __shared__ int len_lds[kPrefixWindow];
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
     len_lds[threadIdx.x] = min(max(a.context_lens[s0 + threadIdx.x], 0), a.max_context_len);
   __syncthreads();
   // pair (p - 1, p): the leading table entries they agree on, up to the
-  // blocks both hold (wave w takes p = w + 1 and p = w + 5)
-  for (int p = 1 + wave; p < n; p += 4) {
+  // blocks both hold (wave w takes p = w + 1)
+  for (int p = 1 + wave; p < n; p += W) {
     const int la = len_lds[p - 1], lb = len_lds[p];
     const int nblk = (min(la, lb) + BS - 1) / BS;
     const int32_t* ra = a.block_tables + (int64_t)(s0 + p - 1) * a.max_blocks_per_seq;
@@ -130,15 +131,15 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
     const int rows = M * G;
     const int cl = prefix_chunk_len(P);
     const int k0 = chunk * cl, k1 = min(k0 + cl, P);
-    const int wk0 = k0 + wave * (cl / 4);  // this wave's keys: [wk0, wk1), whole 32-key steps
-    const int wk1 = min(wk0 + cl / 4, k1);
+    const int wk0 = k0 + wave * (cl / W);  // this wave's keys: [wk0, wk1), whole 32-key steps
+    const int wk1 = min(wk0 + cl / W, k1);
     const int nsteps = wk1 > wk0 ? (wk1 - wk0) / 32 : 0;
 
     // the group's query rows into LDS (rows past the group: zero), read as
     // the Q^T operands at every step (held in registers they would crowd
     // out the second step in flight)
     __syncthreads();  // (the previous group's steps have read q_lds)
-    for (int e = threadIdx.x; e < kRows * (D / 8); e += 256) {
+    for (int e = threadIdx.x; e < kRows * (D / 8); e += 64 * W) {
       const int r = e / (D / 8), c = e % (D / 8);
       half8_t v = {};
       if (r < rows)
@@ -274,9 +275,9 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- the four waves' pieces combined through LDS ------------------------
+    // ---- the waves' pieces combined through LDS -------------------------------
     float* o_lds = comb_lds;
-    float* ml_lds = comb_lds + 4 * kRows * kORow;
+    float* ml_lds = comb_lds + W * kRows * kORow;
     __syncthreads();  // (the previous group's combine has read the LDS)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -291,13 +292,16 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
       }
     }
     __syncthreads();
-    // wave w: rows 8w .. 8w + 7; lane: row 8w + lane / 8, dims kDL (lane % 8) ..
-    constexpr int kDL = D / 8;
-    const int r = 8 * wave + (lane >> 3);
-    const int d0 = (lane & 7) * kDL;
-    float mw[4], mx = -INFINITY;
+    // wave w: rows kRW w .. + kRW - 1; lane: row kRW w + lane / kLR, dims
+    // kDL (lane % kLR) ..
+    constexpr int kRW = kRows / W;   // rows per wave
+    constexpr int kLR = 64 / kRW;    // lanes per row
+    constexpr int kDL = D / kLR;     // dims per lane (a multiple of 4)
+    const int r = kRW * wave + lane / kLR;
+    const int d0 = (lane % kLR) * kDL;
+    float mw[W], mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < W; ++w) {
       mw[w] = ml_lds[(w * kRows + r) * 2];
       mx = fmaxf(mx, mw[w]);
     }
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
 #pragma unroll
     for (int d = 0; d < kDL; ++d) acc[d] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float wt = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - mx);  // 0 for a wave without keys
       L += wt * ml_lds[(w * kRows + r) * 2 + 1];
 #pragma unroll
@@ -319,13 +323,13 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(const PrefixArgs a) {
       const int64_t ro = ((int64_t)chunk * S + (s0 + gf + r / G)) * Hq + h * G + r % G;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-      for (int d = 0; d < kDL; d += 8) {
-        half8_t v;
+      for (int d = 0; d < kDL; d += 4) {
+        half4_t v;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (half_t)(acc[d + i] * inv);
-        *reinterpret_cast<half8_t*>(a.pre_o + ro * D + d0 + d) = v;
+        for (int i = 0; i < 4; ++i) v[i] = (half_t)(acc[d + i] * inv);
+        *reinterpret_cast<half4_t*>(a.pre_o + ro * D + d0 + d) = v;
       }
-      if ((lane & 7) == 0) a.pre_lse[ro] = L > 0.0f ? mx + __builtin_log2f(L) : -INFINITY;
+      if (lane % kLR == 0) a.pre_lse[ro] = L > 0.0f ? mx + __builtin_log2f(L) : -INFINITY;
     }
   };
 
@@ -354,12 +358,12 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream, hipEvent_t sta
   const dim3 grid((unsigned)(windows * a.num_kv_heads * a.max_chunks));
 #define PA_PREFIX(D, BS)                                                                       \
   if (a.head_dim == D && a.block_size == BS) {                                                \
-    const size_t lds = (size_t)4 * kRows * ((D + 4) + 2) * sizeof(float);                     \
+    const size_t lds = (size_t)kPrefixWaves * kRows * ((D + 4) + 2) * sizeof(float);          \
     if (!start)                                                                                \
-      hipLaunchKernelGGL((prefix_kernel<D, BS>), grid, dim3(256), lds, stream, a);            \
+      hipLaunchKernelGGL((prefix_kernel<D, BS>), grid, dim3(64 * kPrefixWaves), lds, stream, a); \
     else                                                                                       \
-      hipExtLaunchKernelGGL((prefix_kernel<D, BS>), grid, dim3(256), lds, stream, start,      \
-                            nullptr, 0, a);                                                    \
+      hipExtLaunchKernelGGL((prefix_kernel<D, BS>), grid, dim3(64 * kPrefixWaves), lds, stream,    \
+                            start, nullptr, 0, a);                                             \
   }
   PA_PREFIX(128, 16) PA_PREFIX(64, 16) PA_PREFIX(128, 8) PA_PREFIX(64, 8) PA_PREFIX(128, 32)
   PA_PREFIX(64, 32)

@@ -113,9 +113,9 @@ def test_fused_prefix_sharing_with_copies(shared_blocks, BS, D):
 # range): groups across the 8-sequence windows the pass groups in, several
 # groups in one window, a prefix that is not a multiple of 64 (the pass
 # takes 64 of 96), one-token suffixes, groups of one (nothing shared), a
-# prefix in four chunks of 512 keys and one in four chunks of 768.
+# prefix in two chunks of 1024 keys and one in four chunks of 1280.
 PREFIX_CASES = [(2, 20, 256, (1, 150)), (4, 12, 96, (1, 80)), (3, 24, 1024, (1, 3)),
-                (8, 8, 128, (1, 40)), (2, 6, 2048, (100, 700)), (2, 6, 3072, (1, 64))]
+                (8, 8, 128, (1, 40)), (2, 6, 2048, (100, 700)), (2, 6, 5120, (1, 64))]
 
 
 @pytest.mark.parametrize("groups,seqs,plen,suffix", PREFIX_CASES)
