@@ -88,11 +88,13 @@ def copy_probe(args):
                       "launches": args.steps}), flush=True)
 
 
-def measured_traffic(workload, fused):
-    """HBM bytes per decode dispatch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or None when
-    there are none for this workload and kernel variant (append fused or
-    not) or the kernel source changed since."""
+def measured_traffic(workload, fused, shared):
+    """HBM bytes per step of the timed kernels (the decode kernel, and the
+    prefix pass before it on a shared-blocks batch) from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, calibrated against a
+    plain copy), or None when there are none for this workload and variant
+    (append fused or not, shared-blocks flag) or a kernel source changed
+    since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_counters.json")
     if not os.path.exists(path):
@@ -100,10 +102,15 @@ def measured_traffic(workload, fused):
     rec = json.load(open(path))
     if bool(rec.get("append_fused", False)) != bool(fused):
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    if bool(rec.get("shared_blocks_flag", False)) != bool(shared):
         return None
-    return int(round(rec["traffic_bytes_per_dispatch"]))
+    digests = rec.get("source_sha256")
+    if not isinstance(digests, dict):  # (a record of one kernel source, from before)
+        return None
+    for src, digest in digests.items():
+        if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != digest:
+            return None
+    return int(round(rec["traffic_bytes_per_step"]))
 
 
 def achievable_read(torch, pk, gib, reps=5):
@@ -622,14 +629,19 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (measured_traffic(w.name, fused) if w.block_size == 16 else None),
-            "kernel": "decode_kernel" + (" (append fused)" if fused else ""),
+            "traffic": (measured_traffic(w.name, fused, shared and fused)
+                        if w.block_size == 16 else None),
+            "kernel": ("prefix_kernel + " if shared and fused else "")
+                      + "decode_kernel" + (" (append fused)" if fused else ""),
             "mean_us": round(dec_mean_s * 1e6, 3),
             "median_us": round(float(np.median(dec_ms)) * 1e3, 3),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
             "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
-            "timing": "HIP events bound to the decode kernel (hipExtLaunchKernel), over "
-                      "the timed steps run again right after the wall-clock region",
+            "timing": ("HIP events bound to the start of the prefix pass and the end of "
+                       "the decode kernel" if shared and fused else
+                       "HIP events bound to the decode kernel")
+                      + " (hipExtLaunchKernel), over the timed steps run again right after "
+                        "the wall-clock region",
             "call_mean_us": round(float(call_ms.mean()) * 1e3, 3),
             "flushed_mean_us": (None if flushed_ms is None
                                 else round(float(flushed_ms.mean()) * 1e3, 3)),
