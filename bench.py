@@ -68,6 +68,10 @@ def parse():
                     help="decode: per-worker timeline from the measurement build "
                          "(libpagedkv_trace.so, `python -m paged_kv_cache_59_amd.build --trace`), "
                          "one launch per step with a synchronisation after each; prints a summary")
+    ap.add_argument("--decode-variant", default=None, choices=["valu"],
+                    help="decode: time the measurement build libpagedkv_<variant>.so "
+                         "(`python -m paged_kv_cache_59_amd.build --valu`: q.K and P.V on the "
+                         "vector ALUs with v_dot2_f32_f16 instead of the 4x4x4 MFMA)")
     ap.add_argument("--trace-dump", default=None,
                     help="with --trace: also save every step's raw per-worker stamps (.npy)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -487,6 +491,8 @@ def main():
     from paged_kv_cache_59_amd import binding as pk
     from paged_kv_cache_59_amd import workloads as wl
 
+    if args.decode_variant:
+        pk.use_variant_library(args.decode_variant)
     assert torch.cuda.is_available()
     torch.cuda.set_device(0)
     w = wl.make_named(args.workload, placement=args.placement, block_size=args.block_size)
@@ -625,12 +631,13 @@ def main():
             "logical_decode_bytes": w.decode_bytes(),
             "kernel_bytes": kernel_bytes, "append": "fused" if fused else "separate launch",
             "shared_blocks_flag": bool(shared and fused),
+            "decode_variant": args.decode_variant or "mfma",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (measured_traffic(w.name, fused, shared and fused)
-                        if w.block_size == 16 else None),
+                        if w.block_size == 16 and not args.decode_variant else None),
             "kernel": ("prefix_kernel + " if shared and fused else "")
                       + "decode_kernel" + (" (append fused)" if fused else ""),
             "mean_us": round(dec_mean_s * 1e6, 3),

@@ -16,6 +16,11 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 _lib = None
+# PA_LIBRARY_VARIANT=<variant> loads a measurement build instead (the test
+# suite run against it: see use_variant_library)
+if os.environ.get("PA_LIBRARY_VARIANT"):
+    _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                             f"libpagedkv_{os.environ['PA_LIBRARY_VARIANT']}.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1
@@ -32,16 +37,21 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_deco
             "pa_decode_num_workers", "pa_strerror", "pa_version")
 
 
-def use_trace_library() -> None:
-    """Load the measurement build (libpagedkv_trace.so: the same entry
-    points; the decode kernel also writes per-worker timestamps at the start
-    of its workspace) instead of libpagedkv.so.  Call before the first call
-    into the library."""
+def use_variant_library(variant: str) -> None:
+    """Load a measurement build, libpagedkv_<variant>.so (the same entry
+    points; "trace": the decode kernel also writes per-worker timestamps at
+    the start of its workspace; "valu": it forms q.K and P.V on the vector
+    ALUs), instead of libpagedkv.so.  Call before the first call into the
+    library."""
     global _LIB_PATH
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv_trace.so")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"libpagedkv_{variant}.so")
     if _lib is not None and _LIB_PATH != path:
         raise RuntimeError("the library is already loaded")
     _LIB_PATH = path
+
+
+def use_trace_library() -> None:
+    use_variant_library("trace")
 
 
 TRACE_SLOTS = 32  # per-worker 64-bit words the measurement build writes

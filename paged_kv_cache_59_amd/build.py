@@ -1,6 +1,6 @@
 """Build the HIP library ``libpagedkv.so`` in-tree for gfx950 with hipcc.
 
-Usage: ``python -m paged_kv_cache_59_amd.build [--trace]`` (or ``build()``).
+Usage: ``python -m paged_kv_cache_59_amd.build [--trace | --valu]`` (or ``build()``).
 Every call recompiles.  Objects go to ``_build/`` at the repository root; the
 shared library lands next to this file, where the binding loads it.
 """
@@ -19,6 +19,15 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 TRACE_LIB_PATH = os.path.join(PKG, "libpagedkv_trace.so")
+# measurement builds: the same library with one compile-time switch
+VARIANTS = {
+    # the decode kernel also writes per-worker timestamps at the start of
+    # its workspace (the benchmark's --trace mode)
+    "trace": "-DPA_DECODE_TRACE",
+    # the decode kernel forms q.K and P.V with v_dot2_f32_f16 on the vector
+    # ALUs instead of v_mfma_f32_4x4x4f16 (the benchmark's --decode-variant)
+    "valu": "-DPA_DECODE_VALU",
+}
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip",
@@ -64,13 +73,19 @@ def check_no_scratch(remarks: str) -> str:
     return f"{kernels} device functions, none using scratch memory"
 
 
-def build(verbose: bool = False, trace: bool = False) -> str:
-    """Build libpagedkv.so; with ``trace``, the measurement build
-    libpagedkv_trace.so instead: the same library, whose decode kernel also
-    writes per-worker timestamps at the start of its workspace (for the
-    benchmark's ``--trace`` mode only)."""
-    out_dir = os.path.join(BUILD_DIR, "trace") if trace else BUILD_DIR
-    lib_path = TRACE_LIB_PATH if trace else LIB_PATH
+def variant_lib_path(variant: str) -> str:
+    return os.path.join(PKG, f"libpagedkv_{variant}.so")
+
+
+def build(verbose: bool = False, trace: bool = False, variant: str | None = None) -> str:
+    """Build libpagedkv.so; with ``variant`` (or ``trace``, for "trace") a
+    measurement build libpagedkv_<variant>.so instead (VARIANTS)."""
+    if trace:
+        variant = "trace"
+    if variant is not None and variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    out_dir = os.path.join(BUILD_DIR, variant) if variant else BUILD_DIR
+    lib_path = variant_lib_path(variant) if variant else LIB_PATH
     os.makedirs(out_dir, exist_ok=True)
     objs = []
     cmds = []
@@ -81,7 +96,7 @@ def build(verbose: bool = False, trace: bool = False) -> str:
         # to scratch memory (a register array indexed at run time, or too
         # many live values): every kernel here is meant to run without it
         remarks = [] if src.endswith(".cpp") else ["-Rpass-analysis=kernel-resource-usage"]
-        defs = ["-DPA_DECODE_TRACE"] if trace else []
+        defs = [VARIANTS[variant]] if variant else []
         cmds.append([HIPCC, *FLAGS, *defs, *lang, *remarks, "-c", os.path.join(CSRC, src), "-o",
                      obj])
         objs.append(obj)
@@ -101,4 +116,5 @@ def build(verbose: bool = False, trace: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv, trace="--trace" in sys.argv)
+    build(verbose="-q" not in sys.argv,
+          variant="trace" if "--trace" in sys.argv else "valu" if "--valu" in sys.argv else None)

@@ -127,6 +127,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef _Float16 half2x __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half4_t lo4(half8_t v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
 __device__ __forceinline__ half4_t hi4(half8_t v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
 
@@ -1012,11 +1013,31 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
     // logits: S[g][token lane] = q_g . K_token  (rows = heads, columns = tokens)
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (kValu) {
+      // (measurement build) lane = token: its K row against each head's q
+      // row, read from LDS by every lane at once, in pairs of dims
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g_lane * kQRow + c * kChunk);
-      sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
+      for (int g = 0; g < 4; ++g) {
+        if (g < G) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) {
+            const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g * kQRow + c * kChunk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc = __builtin_amdgcn_fdot2(half2x{qv[2 * i], qv[2 * i + 1]},
+                                           half2x{kreg[c][2 * i], kreg[c][2 * i + 1]}, acc, false);
+          }
+          sacc[g] = acc;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g_lane * kQRow + c * kChunk);
+        sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
+      }
     }
     // keep the next unit's address work below the logits: hoisted above
     // them it would wait for this unit's whole K (and table) first
@@ -1086,20 +1107,42 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     }
 
     __builtin_amdgcn_wave_barrier();
-    // lane 4c+g: weights of head g for tokens 4c..4c+3
-    const half4_t pfrag =
-        *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * kPRow + (lane >> 2) * 4);
-
-    // out[g][d] += sum_t P[g][t] V[t][d]; chunk c = tokens 4c..4c+3 of the unit
-    static_for<0, 16>([&](auto ic) {
-      constexpr int c = decltype(ic)::value;
-      constexpr int g = c / 2, sub = c % 2;  // 8-token group, its half
+    if constexpr (kValu) {
+      // (measurement build) lane = dim 64 st + lane: each head's weights,
+      // read from LDS by every lane at once, against its 8-token V groups, in
+      // pairs of tokens
 #pragma unroll
-      for (int st = 0; st < kSets; ++st) {
-        const half4_t vf = sub ? hi4(vreg[g][st]) : lo4(vreg[g][st]);
-        acc_o[st] = __builtin_amdgcn_mfma_f32_4x4x4f16(pfrag, vf, acc_o[st], 4, c, 0);
+      for (int g = 0; g < 4; ++g) {
+        if (g < G) {
+#pragma unroll
+          for (int grp = 0; grp < 8; ++grp) {
+            const half8_t pv = *reinterpret_cast<const half8_t*>(p_lds + g * kPRow + grp * 8);
+#pragma unroll
+            for (int st = 0; st < kSets; ++st)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc_o[st][g] = __builtin_amdgcn_fdot2(
+                    half2x{pv[2 * i], pv[2 * i + 1]},
+                    half2x{vreg[grp][st][2 * i], vreg[grp][st][2 * i + 1]}, acc_o[st][g], false);
+          }
+        }
       }
-    });
+    } else {
+      // lane 4c+g: weights of head g for tokens 4c..4c+3
+      const half4_t pfrag =
+          *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * kPRow + (lane >> 2) * 4);
+
+      // out[g][d] += sum_t P[g][t] V[t][d]; chunk c = tokens 4c..4c+3 of the unit
+      static_for<0, 16>([&](auto ic) {
+        constexpr int c = decltype(ic)::value;
+        constexpr int g = c / 2, sub = c % 2;  // 8-token group, its half
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) {
+          const half4_t vf = sub ? hi4(vreg[g][st]) : lo4(vreg[g][st]);
+          acc_o[st] = __builtin_amdgcn_mfma_f32_4x4x4f16(pfrag, vf, acc_o[st], 4, c, 0);
+        }
+      });
+    }
     load_v(nxt, pb_nxt);
     __builtin_amdgcn_wave_barrier();
 

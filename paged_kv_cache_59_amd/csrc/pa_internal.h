@@ -60,6 +60,13 @@ constexpr bool kTrace = true;
 constexpr bool kTrace = false;
 #endif
 constexpr int kTraceSlots = 32;
+// Measurement builds compiled with PA_DECODE_VALU form the decode's q.K and
+// P.V with v_dot2_f32_f16 on the vector ALUs instead of the 4x4x4 MFMA.
+#ifdef PA_DECODE_VALU
+constexpr bool kValu = true;
+#else
+constexpr bool kValu = false;
+#endif
 enum {
   kTrEntry = 0,     // kernel entry (s_memrealtime, 100 MHz)
   kTrTables,        // lengths and unit offsets in LDS
