@@ -21,6 +21,31 @@
  *        Blocks" (reference counts; copy when a holder appends).
  *   [AG] "Continuous batching and paged attention", abhi-g.dev - "Paged
  *        attention": K and V are gathered through the block table.
+ *   [CB] "Continuous batching, paged attention, prefix caching",
+ *        backplane.click - "Prefix caching": one stored copy of a prompt
+ *        prefix serves every request that starts with it.
+ *
+ * Departures from the plain decode interface (pa_reshape_and_cache,
+ * pa_copy_blocks, pa_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+ * max_context_len), pa_decode without a pool size or worker count, pools
+ * [NB][Hkv][16][D]), each for a reason stated where it applies:
+ *  - the pools are tiled inside each (block, head) tile (layout below): the
+ *    tile stays BS*D contiguous elements, and the order inside it gives the
+ *    kernels' 16-byte loads the operand layouts of their matrix instructions;
+ *  - pa_decode and pa_copy_blocks take num_blocks, the pool size (as
+ *    pa_reshape_and_cache does), so that ids outside the pool are skipped
+ *    instead of read or written out of bounds; token and pair counts are
+ *    int64;
+ *  - pa_decode takes num_workers (0 = automatic), the size of its
+ *    persistent grid, and pa_decode_workspace_size takes num_kv_heads and
+ *    num_workers instead of num_q_heads: the workspace holds one partial
+ *    result per (sequence, KV head) run and one per worker;
+ *  - the library keeps two pieces of state: a per-device cache of the
+ *    compute-unit count and the device array of pa_decode_append_noalloc;
+ *  - further entry points: the timed variants, the fused append
+ *    (pa_decode_append, with the shared-prefix flag, and its allocation-free
+ *    form), block swaps, the multi-query (chunked prefill) kernel, and
+ *    pa_read_probe, which is for measurement only and not part of the path.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -142,8 +167,13 @@ int32_t pa_decode_num_workers(void);
  * Workspace bytes pa_decode needs for these sizes; max_context_len and
  * num_workers as for pa_decode (0 workers = automatic, on the current
  * device).  Returns 0 for invalid sizes.  The workspace holds, from its
- * start, the partial results of sequences cut between workers and, against
- * its end, one arrival counter per (sequence, KV head).
+ * start, the partial results of sequences cut between workers (one per
+ * (sequence, KV head) run and one per worker, 4 query-head rows each), then
+ * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
+ * its prefix length, per (chunk, sequence, query head) up to 4 normalised
+ * fp16 rows and their log-sum-exps) and, against its end, one arrival
+ * counter per (sequence, KV head).  The size does not depend on
+ * max_context_len (kept for a stable signature).
  * Batches above 4096 sequences need no more than 4096 do (they run as
  * several launches).
  */
@@ -228,12 +258,24 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  *   slot_mapping   int64 [num_seqs]: the slot of token s; negative (or past
  *                  the pool) = the row is attended but not stored
  *   flags          0, or PA_DECODE_SHARED_BLOCKS when sequences of the batch
- *                  share blocks (prefix caching, forks): K/V are then read
- *                  through the caches, so that repeat reads of a shared
- *                  block hit L2 (measured 20% faster on a batch of
- *                  8-sequence groups sharing 1,024-token prefixes, 9-12%
- *                  slower on batches that share nothing); any other bit is
- *                  PA_ERR_INVALID_ARG.  Results do not depend on it.
+ *                  share blocks (prefix caching, forks; [TT] "Sharing
+ *                  Blocks", [CB] "Prefix caching"); any other bit is
+ *                  PA_ERR_INVALID_ARG.  With the flag a prefix pass runs
+ *                  first: in each aligned window of 8 consecutive
+ *                  sequences, runs of at least two sequences whose tables
+ *                  start with the same physical blocks form a group, whose
+ *                  prefix P is the multiple of 64 tokens every member holds
+ *                  in those blocks short of its last position (the new
+ *                  token's).  The pass attends all the group's query rows
+ *                  (members x query heads of a KV head, at most 32) to
+ *                  those P positions once, and the decode covers each
+ *                  member's positions from P on, starting its online
+ *                  softmax from that result.  Results equal the flagless
+ *                  ones up to rounding.  Measured on MI355X (256 sequences
+ *                  in 32 groups of 8 sharing 1,024-token prefixes): 104 us
+ *                  for both kernels, 1.11x the distinct K/V bytes read from
+ *                  HBM, against 171 us and 2.78x when every sequence read
+ *                  its prefix.
  *   the rest       as pa_decode; k_cache and v_cache are written (the new
  *                  rows only)
  *
