@@ -657,20 +657,34 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // one batch of nb <= B pieces whose slot lane pq holds in sl (lanes past
   // the batch repeat its last), B = 2, 4 or 16 so that small batches load
   // only what they use
-  auto absorb = [&](auto batch, Merged& m, int sl, int nb) {
+  // (own_slot >= 0: the piece of that slot is not in the workspace but in
+  // ring entry own_k, where the merger still holds it)
+  auto absorb = [&](auto batch, Merged& m, int sl, int nb, int own_slot, int own_k) {
     constexpr int B = decltype(batch)::value;
     const bool valid = pq < nb && gq < G;
-    const float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
-    const float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
+    const bool own = sl == own_slot;
+    float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
+    float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
+    if (own_slot >= 0) {
+      const float mo = ring_ml[own_k][2 * (gq & 3)], lo = ring_ml[own_k][2 * (gq & 3) + 1];
+      m_p = (valid && own) ? mo : m_p;
+      l_p = (valid && own) ? lo : l_p;
+    }
     float ov[B][kF];
 #pragma unroll
     for (int qi = 0; qi < B; ++qi) {
-      const float* base = a.ws.o + (int64_t)__builtin_amdgcn_readlane(sl, qi) * 4 * D;
+      const int sq = __builtin_amdgcn_readlane(sl, qi);
+      if (sq == own_slot) {
 #pragma unroll
-      for (int st = 0; st < kSets; ++st) {
-        const float4_t x = load_through16(base, ((gq & 3) * D + pq * kF + st * 4) * 4);
+        for (int j = 0; j < kF; ++j) ov[qi][j] = ring_o[own_k][(gq & 3) * D + pq * kF + j];
+      } else {
+        const float* base = a.ws.o + (int64_t)sq * 4 * D;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[qi][st * 4 + e] = x[e];
+        for (int st = 0; st < kSets; ++st) {
+          const float4_t x = load_through16(base, ((gq & 3) * D + pq * kF + st * 4) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[qi][st * 4 + e] = x[e];
+        }
       }
     }
     const float m_new = fmaxf(m.mx, row_max16(m_p));
@@ -688,7 +702,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     }
   };
   // all pieces of run (s, kvh)
-  auto merge_pieces = [&](int s, int kvh) {
+  auto merge_pieces = [&](int s, int kvh, int own_slot, int own_k) {
     Merged m;
     m.mx = -INFINITY;
     m.lsum = 0.0f;
@@ -724,11 +738,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const int v = va + p;
       const int sl = v == va ? r : R + v;
       if (nb <= 2)
-        absorb(std::integral_constant<int, 2>{}, m, sl, nb);
+        absorb(std::integral_constant<int, 2>{}, m, sl, nb, own_slot, own_k);
       else if (nb <= 4)
-        absorb(std::integral_constant<int, 4>{}, m, sl, nb);
+        absorb(std::integral_constant<int, 4>{}, m, sl, nb, own_slot, own_k);
       else
-        absorb(std::integral_constant<int, 16>{}, m, sl, nb);
+        absorb(std::integral_constant<int, 16>{}, m, sl, nb, own_slot, own_k);
     }
     // Shared: each chunk a piece of weight 1 (in lane pq = 0 of each row)
     // at its log-sum-exp
@@ -862,8 +876,15 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           pml[i] = lane < 8 ? ring_ml[k][lane] : 0.0f;
         }
       }
+      // Pieces that complete their run, known at this point (every other
+      // unit of the run already counted): merged straight from the ring,
+      // neither written through nor counted.  Their ring entries are released
+      // after the merge, the others' at once.
+      const bool last_known = counted && seen + ui == run_units(ci / Hkv);
+      const uint64_t fast = __ballot(last_known);  // bit i: piece i
+      const int cons0 = cons;
       cons += avail;
-      lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
+      if (!fast) lds_st(&ctl[kCtlRingTaken], cons);  // (the ring reads above precede this write)
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail && pslot[i] < 0) {
@@ -907,7 +928,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
             }
           }
           if constexpr (kTrace) ++tr[kTrMerges];
-        } else if (i < avail) {
+        } else if (i < avail && !((fast >> i) & 1)) {
           // a cut piece: written through to its slot
           float* po = a.ws.o + pslot[i] * 4 * D;
 #pragma unroll
@@ -919,26 +940,25 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml[i]);
         }
       }
-      // the slots are written through before they are counted (a round of
-      // whole runs alone waits for nothing)
-      if (__ballot(counted)) __builtin_amdgcn_s_waitcnt(0);
+      // the slots are written through before they are counted (a round
+      // without pieces to count waits for nothing)
+      if (__ballot(counted && !last_known)) __builtin_amdgcn_s_waitcnt(0);
       int arr = 0;
-      if (counted) {
-        const int n_i = run_units(ci / Hkv);
-        arr = seen + ui == n_i ? seen
-                               : __hip_atomic_fetch_add(a.ws.counters + ci, ui, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (counted && !last_known)
+        arr = __hip_atomic_fetch_add(a.ws.counters + ci, ui, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int i = 0; i < kRing; ++i) {
         if (i < avail && pslot[i] >= 0) {
+          const bool fi = (fast >> i) & 1;
           const int n = uniform(run_units(ps[i]));
-          if (__builtin_amdgcn_readlane(arr, i) + pu[i] == n) {
-            merge_out(ps[i], ph[i], merge_pieces(ps[i], ph[i]));
+          if (fi || __builtin_amdgcn_readlane(arr, i) + pu[i] == n) {
+            merge_out(ps[i], ph[i],
+                      merge_pieces(ps[i], ph[i], fi ? (int)pslot[i] : -1, (cons0 + i) % kRing));
             if constexpr (kTrace) ++tr[kTrMerges];
           }
         }
       }
+      if (fast) lds_st(&ctl[kCtlRingTaken], cons);  // (after the merges read the ring)
       if constexpr (kTrace) {
         __builtin_amdgcn_s_waitcnt(0);
         tr[kTrHelperBusy] += stamp_now() - t_round;
