@@ -216,6 +216,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *                     again, so a workspace is reusable without clearing,
  *                     also by calls of smaller shapes.  Two calls
  *                     that overlap in time must not share one workspace.
+ *                     Its last int32 is a status word: 0, or 1 once a
+ *                     bounded wait between a worker's two waves (about
+ *                     0.5 s; a broken invariant) gave up.  The kernel then
+ *                     still ends, with that call's results undefined and
+ *                     counters possibly non-zero: the caller, reading the
+ *                     word after its synchronisation, zeroes the workspace
+ *                     before reusing it.  (PA_DECODE_SPIN_LIMIT=n in the
+ *                     environment lowers the bound to n polls, for tests.)
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.

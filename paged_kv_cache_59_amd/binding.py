@@ -198,6 +198,15 @@ def new_workspace(num_seqs, num_kv_heads, head_dim, max_context_len, num_workers
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
+def decode_status(workspace) -> int:
+    """The workspace's status word (its last int32, read after the caller's
+    synchronisation): 0, or 1 once a bounded wait between a decode worker's
+    waves gave up (that call's results are undefined; zero the workspace
+    before reusing it)."""
+    n = workspace.numel() // 4 * 4
+    return int(workspace[n - 4:n].view(torch.int32).item())
+
+
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
               max_context_len=None, num_workers=0, workspace=None, stream=None,
               kernel_events=None):

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 
 #include "pa_internal.h"
 
@@ -12,6 +13,19 @@ namespace {
 
 constexpr int kVersion = 500;  // 0.5.0
 using pa::kMaxGroup;
+
+// Bound on the waits between a decode worker's waves: pa::kSpinLimit, or
+// PA_DECODE_SPIN_LIMIT (0 .. kSpinLimit) from the environment, read at each
+// call, with which tests force a wait to give up and check that the status
+// word reports it.
+int spin_limit() {
+  const char* e = std::getenv("PA_DECODE_SPIN_LIMIT");
+  if (!e || !*e) return pa::kSpinLimit;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  if (end == e || v < 0) return pa::kSpinLimit;
+  return v < pa::kSpinLimit ? (int)v : pa::kSpinLimit;
+}
 constexpr int kMaxGridYZ = 65535;
 
 bool head_dim_supported(int32_t d) { return d == 64 || d == 128; }
@@ -204,6 +218,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_workers = w;
+  a.spin_limit = spin_limit();
   // Batches whose sequences share prefix blocks: per launch, the prefix pass
   // (pa_prefix.hip) finds the groups of sequences with a common prefix and
   // attends every group's query rows to its prefix once; the decode kernel

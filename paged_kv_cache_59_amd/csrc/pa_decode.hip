@@ -825,7 +825,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
             pf_o[c][g][st] = (c < nch && g < G) ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
       }
     };
-    for (int idle = 0; idle < kSpinLimit;) {
+    int idle = 0;
+    for (; idle < a.spin_limit;) {
       const int avail = min(lds_ld(&ctl[kCtlRingMade]) - cons, kRing);
       if (avail == 0) {
         // the streamer writes its last entry before its done flag: once the
@@ -965,6 +966,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         ++tr[kTrHelperRounds];
       }
     }
+    // the streamer never said it was done: give up (reported in the status word)
+    if (idle >= a.spin_limit && lane == 0)
+      __hip_atomic_store(a.ws.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (kTrace) {
       __builtin_amdgcn_s_waitcnt(0);
       tr[kTrHelperEnd] = stamp_now();
@@ -1182,9 +1186,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // it, a memory latency at every run end.
       const int slot = (piece_g0 == 0 && run_end) ? -1 : piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
       const uint64_t t_ring = stamp_now();
-      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing && spin < kSpinLimit;
-           ++spin)
+      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing; ++spin) {
+        if (spin >= a.spin_limit) {  // give up (reported in the status word)
+          if (lane == 0)
+            __hip_atomic_store(a.ws.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
+      }
       if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
       const int k = ring_made % kRing;
 #pragma unroll
@@ -1279,7 +1288,10 @@ size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers
   return l.end + l.control;
 }
 
-size_t decode_control_bytes(int64_t S, int64_t Hkv) { return align256((size_t)(S * Hkv) * sizeof(int)); }
+// arrival counters, then 256 bytes whose last 4 are the status word
+size_t decode_control_bytes(int64_t S, int64_t Hkv) {
+  return align256((size_t)(S * Hkv) * sizeof(int)) + 256;
+}
 
 // ---- the allocation-free decode's workspace --------------------------------
 // For callers that cannot allocate device memory (code under graph capture,
@@ -1337,6 +1349,7 @@ DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int6
   w.pre_len = reinterpret_cast<int*>(p + l.pre_len);
   w.pre_lse = reinterpret_cast<float*>(p + l.pre_lse);
   w.pre_o = reinterpret_cast<half_t*>(p + l.pre_o);
+  w.status = reinterpret_cast<int*>(p + (bytes & ~(size_t)3)) - 1;
   return w;
 }
 

@@ -29,7 +29,7 @@ constexpr int kRing = 4;
 enum { kCtlRingMade = 0, kCtlRingTaken, kCtlDone };
 // Bound on every wait between the waves (about 0.5 s of s_sleep): a wait
 // that long means a broken invariant, and the kernel then ends with wrong
-// results rather than never.
+// results rather than never, and sets the workspace's status word.
 constexpr int kSpinLimit = 1 << 23;
 
 // Decode workspace.  Partial slots first: one per (sequence, KV head) run
@@ -50,6 +50,9 @@ struct DecodeWorkspace {
   int* pre_len;
   half_t* pre_o;
   float* pre_lse;
+  // the workspace's last int32: 0, or 1 once a bounded wait of a call gave up
+  // (that call's results are undefined); the caller clears it
+  int* status;
 };
 
 // Measurement builds (compiled with PA_DECODE_TRACE) put per-worker
@@ -130,6 +133,7 @@ struct DecodeArgs {
   int64_t num_blocks;
   int max_context_len;
   int num_workers;        // grid size: persistent workgroups sharing the work
+  int spin_limit;         // bound on the waits between a worker's waves (kSpinLimit)
   DecodeWorkspace ws;
   // Fused append (null when plain decode): token s's new K and V rows
   // ([S][Hkv][D]), its slot, and writable views of the pools.  Position

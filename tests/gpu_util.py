@@ -54,10 +54,11 @@ def gpu_decode(w, d, num_workers=0, max_context_len=None, workspace=None):
 
 
 def decode_control_bytes(num_seqs, num_kv_heads):
-    """Bytes of arrival counters at the end of a decode workspace sized for
-    num_seqs (one int32 per (sequence, KV head) run, 256-byte aligned), which
-    every call, of whatever shape, leaves at zero."""
-    return -(-num_seqs * num_kv_heads * 4 // 256) * 256
+    """Bytes of control words at the end of a decode workspace sized for
+    num_seqs (one int32 arrival counter per (sequence, KV head) run, 256-byte
+    aligned, then 256 bytes ending in the status word), which every call, of
+    whatever shape, leaves at zero."""
+    return -(-num_seqs * num_kv_heads * 4 // 256) * 256 + 256
 
 
 def gpu_step(w, d, num_workers=0):

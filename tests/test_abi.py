@@ -96,13 +96,14 @@ def test_workspace_sizes(L):
     # (2 + 128) floats, (max, sum) pairs and vectors 256-byte aligned; then
     # the shared-prefix area: prefix lengths (64 ints), and for 4 chunks x 64
     # sequences x 8 KV heads x 4 query heads a log-sum-exp (fp32) and a row of
-    # 128 fp16; then one arrival counter per run
+    # 128 fp16; then one arrival counter per run and 256 bytes ending in the
+    # status word
     need = L.pa_decode_workspace_size(64, 8, 128, 2048, 2048)
     slots = 64 * 8 + 2048
     a256 = lambda x: -(-x // 256) * 256
     pre_rows = 4 * 64 * 8 * 4
     assert need == (slots * 8 * 4 + slots * 4 * 128 * 4 + a256(64 * 4) + a256(pre_rows * 4)
-                    + a256(pre_rows * 128 * 2) + 64 * 8 * 4)
+                    + a256(pre_rows * 128 * 2) + 64 * 8 * 4 + 256)
     # batches above one launch (4096 sequences) reuse the counters
     assert (L.pa_decode_workspace_size(10000, 8, 128, 100, 64)
             == L.pa_decode_workspace_size(4096, 8, 128, 100, 64))

@@ -1,0 +1,57 @@
+"""The decode workspace's status word: a bounded wait between a worker's two
+waves that gives up is reported there, and the kernel still ends.
+
+The give-up is forced from the host: PA_DECODE_SPIN_LIMIT=0 (read by the
+library at each call) makes every such wait give up at once, so the merger
+wave leaves before the streamer hands it anything.  Nothing then waits
+without bound and every access stays in bounds; the call's results are
+undefined, and the workspace is zeroed before it is used again.
+"""
+import os
+
+import pytest
+import torch
+
+from paged_kv_cache_59_amd import binding as pk
+from paged_kv_cache_59_amd import workloads as wl
+from tests.gpu_util import compare, log, oracle_decode, oracle_pools, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def step(w, d, ws):
+    if w.block_mapping.shape[0]:
+        pk.pa_copy_blocks(d["k_cache"], d["v_cache"], d["block_mapping"])
+    pk.pa_decode_append(d["out"], d["q"], d["k_new"], d["v_new"], d["slot_mapping"],
+                        d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                        float(w.scale), w.num_kv_heads, max_context_len=w.max_context_len,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    return d["out"].cpu().numpy()
+
+
+def test_status_word_reports_a_wait_that_gives_up():
+    # 6 sequences of 100-400 tokens over the automatic worker count: every
+    # unit its own share, so runs are cut and the merger has work
+    w = wl.make_workload("status", 77, 8, 2, 64, num_seqs=6, len_range=(100, 400))
+    d = to_device(w)
+    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len)
+    kc, vc = oracle_pools(w)
+    ref = oracle_decode(w, kc, vc)
+
+    log("status: normal call")
+    compare(step(w, d, ws), ref, "status: normal")
+    assert pk.decode_status(ws) == 0
+
+    log("status: PA_DECODE_SPIN_LIMIT=0")
+    os.environ["PA_DECODE_SPIN_LIMIT"] = "0"
+    try:
+        step(w, d, ws)  # results undefined
+    finally:
+        del os.environ["PA_DECODE_SPIN_LIMIT"]
+    assert pk.decode_status(ws) == 1
+
+    log("status: workspace zeroed, normal call again")
+    ws.zero_()
+    compare(step(w, d, ws), ref, "status: after the give-up")
+    assert pk.decode_status(ws) == 0
