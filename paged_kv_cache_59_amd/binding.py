@@ -270,7 +270,9 @@ def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block
     position's slot (negative: attended, not stored).  k_new and v_new are
     [num_seqs, Hkv, D] fp16; the other arguments as pa_decode.
     ``shared_blocks``: sequences of the batch share blocks (prefix caching,
-    forks); K/V are then read through the caches (same results)."""
+    forks); a prefix pass then attends each group of sequences that start
+    with the same blocks to their common prefix once, and the decode covers
+    the rest (same results up to rounding)."""
     _dev(out, "out", torch.float16)
     _dev(q, "q", torch.float16)
     _dev(k_new, "k_new", torch.float16)

@@ -98,8 +98,8 @@ def test_fused_zero_length_rows():
 @pytest.mark.parametrize("BS,D", [(16, 128), (16, 64), (8, 128), (8, 64), (32, 128), (32, 64)])
 def test_fused_prefix_sharing_with_copies(shared_blocks, BS, D):
     """Copy-on-write before the fused launch: the new token lands in the copy.
-    With the shared-blocks flag the K/V loads go through the caches; every
-    block size and head dimension of that variant runs."""
+    With the shared-blocks flag the prefix pass and the decode's shared
+    variant run, at every block size and head dimension."""
     w = wl.make_workload("fused-prefix", 341 + BS + D, 32, 8, D, num_seqs=16, prefix_groups=4,
                          prefix_len=256, suffix_range=(1, 200), block_size=BS)
     assert w.block_mapping.shape[0] > 0 and w.shares_blocks()
