@@ -396,7 +396,8 @@ def trace_decode(args):
     replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     workers = args.num_workers or pk.pa_decode_num_workers()
-    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, workers)
+    ws = pk.new_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                          workers)
     shared = w.shares_blocks()
     S = pk.TRACE_SLOTS
     runs = []
@@ -506,7 +507,8 @@ def main():
     replicas = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     workers = args.num_workers or pk.pa_decode_num_workers()
-    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, workers)
+    ws = pk.new_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                          workers)
     stream = torch.cuda.current_stream()
     has_copy = w.block_mapping.shape[0] > 0
     # the caller's knowledge that sequences share blocks (prefix caching):

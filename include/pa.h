@@ -38,7 +38,7 @@
  *    int64;
  *  - pa_decode takes num_workers (0 = automatic), the size of its
  *    persistent grid, and pa_decode_workspace_size takes num_kv_heads and
- *    num_workers instead of num_q_heads: the workspace holds one partial
+ *    num_workers besides num_q_heads: the workspace holds one partial
  *    result per (sequence, KV head) run and one per worker;
  *  - the library keeps two pieces of state: a per-device cache of the
  *    compute-unit count and the device array of pa_decode_append_noalloc;
@@ -166,9 +166,11 @@ int32_t pa_decode_num_workers(void);
 /*
  * Workspace bytes pa_decode needs for these sizes; max_context_len and
  * num_workers as for pa_decode (0 workers = automatic, on the current
- * device).  Returns 0 for invalid sizes.  The workspace holds, from its
- * start, the partial results of sequences cut between workers (one per
- * (sequence, KV head) run and one per worker, 4 query-head rows each), then
+ * device).  Returns 0 for invalid sizes (num_q_heads not a multiple of
+ * num_kv_heads included).  The workspace holds, from its start, the partial
+ * results of sequences cut between workers (one per (sequence, KV head)
+ * run and one per worker, 4 query-head rows each; a KV head of G > 4 query
+ * heads counts as ceil(G / 4) heads here and below), then
  * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
  * its prefix length, per (chunk, sequence, query head) up to 4 normalised
  * fp16 rows and their log-sum-exps) and, against its end, one arrival
@@ -177,8 +179,8 @@ int32_t pa_decode_num_workers(void);
  * Batches above 4096 sequences need no more than 4096 do (they run as
  * several launches).
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t num_workers);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t num_workers);
 
 /*
  * Decode attention through the block table ([AQ] "PagedAttention: a block
@@ -210,7 +212,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *                     is merged by the last piece to finish (log-sum-exp
  *                     rescaling).
  *   workspace         device buffer of at least pa_decode_workspace_size(
- *                     num_seqs, num_kv_heads, head_dim, max_context_len,
+ *                     num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
  *                     num_workers) bytes, 256-byte aligned, ZERO-FILLED before
  *                     its first use; each call leaves its counters at zero
  *                     again, so a workspace is reusable without clearing,
@@ -227,7 +229,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t 
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.
- * 1 <= G <= 4.  num_seqs == 0 is a no-op.
+ * Any G >= 1: the grouped query heads of a KV head (up to 4 at a time, the
+ * rows of the decode's matrix instruction) share each K and V load, so a
+ * group of G > 4 reads its KV head's K and V ceil(G / 4) times.
+ * num_seqs == 0 is a no-op.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.pa_swap_blocks.restype = ctypes.c_int
     L.pa_decode_num_workers.argtypes = []
     L.pa_decode_num_workers.restype = i32
-    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.pa_decode_workspace_size.restype = sz
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, i32,
                             i32, i64, i32, i32, vp, sz, vp]
@@ -185,16 +185,17 @@ def pa_decode_num_workers() -> int:
     return n
 
 
-def pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, max_context_len,
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                              num_workers=0) -> int:
-    return int(lib().pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, max_context_len,
-                                              num_workers))
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, num_workers))
 
 
-def new_workspace(num_seqs, num_kv_heads, head_dim, max_context_len, num_workers=0,
+def new_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, num_workers=0,
                   device="cuda"):
     """A zero-filled decode workspace (the counters must start at zero)."""
-    n = pa_decode_workspace_size(num_seqs, num_kv_heads, head_dim, max_context_len, num_workers)
+    n = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                 num_workers)
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -239,7 +240,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_k
     if max_context_len is None:
         max_context_len = mb * bs
     if workspace is None:
-        workspace = new_workspace(S, hkv, d, int(max_context_len), num_workers, device=q.device)
+        workspace = new_workspace(S, hq, hkv, d, int(max_context_len), num_workers, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")
@@ -298,7 +299,7 @@ def pa_decode_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block
     if max_context_len is None:
         max_context_len = mb * bs
     if workspace is None:
-        workspace = new_workspace(S, hkv, d, int(max_context_len), num_workers, device=q.device)
+        workspace = new_workspace(S, hq, hkv, d, int(max_context_len), num_workers, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     if not math.isfinite(float(scale)):
         raise ValueError("scale must be finite")

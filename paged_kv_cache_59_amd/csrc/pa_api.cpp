@@ -34,6 +34,13 @@ bool block_size_supported(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The decode's heads: a KV head of G > kMaxGroup query heads counts as
+// ceil(G / kMaxGroup) virtual heads of up to kMaxGroup query heads each
+// (num_q_heads a multiple of num_kv_heads).
+int32_t virtual_kv_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  return num_kv_heads * (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
+}
+
 // Decode workers for the current device: kWorkersPerCU per compute unit,
 // rounded up to a multiple of 8 (the XCD count).  Cached per device; calls
 // from several threads may each fill an entry, with the same value.
@@ -143,13 +150,15 @@ int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_
 
 int32_t pa_decode_num_workers(void) { return auto_workers(); }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t num_workers) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t num_workers) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
   const int32_t w = resolve_workers(num_workers);
   if (w <= 0) return 0;
   const int64_t s = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
-  return pa::decode_workspace_bytes(s, num_kv_heads, head_dim, w);
+  return pa::decode_workspace_bytes(s, virtual_kv_heads(num_q_heads, num_kv_heads), head_dim, w);
 }
 
 }  // extern "C"
@@ -173,7 +182,6 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!block_size_supported(block_size) || !head_dim_supported(head_dim))
     return PA_ERR_UNSUPPORTED;
-  if (num_q_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_INVALID_ARG;
   if (num_workers < 0 || num_workers > pa::kMaxWorkers) return PA_ERR_INVALID_ARG;
@@ -187,16 +195,20 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   // one launch takes at most kMaxSeqsPerLaunch sequences; its 64-token units
   // (all heads) must fit a 32-bit index
   const int64_t per_launch = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
-  if (per_launch * num_kv_heads * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
+  // a KV head of more than kMaxGroup query heads is attended as split
+  // virtual heads of up to kMaxGroup each (hv of them in all)
+  const int32_t split = (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
+  const int32_t hv = virtual_kv_heads(num_q_heads, num_kv_heads);
+  if (per_launch * hv * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
     return PA_ERR_UNSUPPORTED;
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
   const size_t need =
-      pa::decode_workspace_bytes(per_launch, num_kv_heads, head_dim, w);
+      pa::decode_workspace_bytes(per_launch, hv, head_dim, w);
   if (static_scratch) {
     // the library's own device array stands in for the workspace
     if (need > pa::kStaticScratchBytes ||
-        pa::decode_control_bytes(per_launch, num_kv_heads) > pa::kStaticControlBytes)
+        pa::decode_control_bytes(per_launch, hv) > pa::kStaticControlBytes)
       return PA_ERR_SCRATCH_LIMIT;
     if (pa::decode_static_scratch(stream, &workspace) != hipSuccess) return PA_ERR_HIP;
     workspace_bytes = pa::kStaticScratchBytes;
@@ -205,13 +217,13 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
-  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, per_launch, num_kv_heads, head_dim,
-                                    w);
+  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, per_launch, hv, head_dim, w);
   a.k_cache = static_cast<const pa::half_t*>(k_cache);
   a.v_cache = static_cast<const pa::half_t*>(v_cache);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
   a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
+  a.num_kv_heads = hv;
+  a.kv_split = split;
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -258,7 +270,8 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
       p.scale_log2 = a.scale_log2;
       p.num_seqs = (int)n;
       p.num_q_heads = num_q_heads;
-      p.num_kv_heads = num_kv_heads;
+      p.num_kv_heads = hv;
+      p.kv_split = split;
       p.head_dim = head_dim;
       p.block_size = block_size;
       p.max_blocks_per_seq = max_blocks_per_seq;

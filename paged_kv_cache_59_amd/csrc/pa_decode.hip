@@ -33,7 +33,9 @@
 //  * The grouped query heads of one KV head (G <= 4) are the 4 rows of the
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
-//    would cost 64 per lane and halve the waves a SIMD holds).
+//    would cost 64 per lane and halve the waves a SIMD holds).  A larger
+//    group is split into ceil(G / 4) virtual heads of up to 4 rows, each its
+//    own run over the KV head's K and V (which it then reads that often).
 //  * q . K: lane l owns token l of the 64; it loads its 16-byte chunks of the
 //    K row (K pool [NB][Hkv][D/8][16][8]: for a fixed chunk the 64 lanes read
 //    four contiguous 256-byte runs) and feeds them as the B operand, so the
@@ -238,7 +240,15 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
-  const int G = Hq / Hkv;
+  // Virtual heads: a KV head with more than 4 query heads is attended as
+  // kv_split consecutive virtual heads (Hkv counts those) of up to 4 query
+  // heads each, the 4 rows of the MFMA; each reads its KV head's K and V.
+  const int split = a.kv_split;
+  const int Hkr = Hkv / split;  // KV heads of the pools, k_new and v_new
+  const int G = Hq / Hkr;       // query heads per KV head
+  auto kv_of = [&](int h) { return split == 1 ? h : h / split; };
+  auto q_first = [&](int h) { return split == 1 ? h * G : h / split * G + h % split * 4; };
+  auto q_rows = [&](int h) { return split == 1 ? G : min(4, G - h % split * 4); };
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
   int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
   const int my_blk = lane / BS;  // which of a unit's blocks holds this lane's token
   const int g_lane = lane & 3;   // q head of the group this lane's MFMA row carries
-  const int64_t block_stride = (int64_t)Hkv * kTile;
+  const int64_t block_stride = (int64_t)Hkr * kTile;
 
   // Table entries of unit c's NBU blocks: one vector load, lane i reads
   // entry NBU g + i % NBU.  Blocks past the sequence's last re-read its last
@@ -510,14 +520,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   auto load_k = [&](const Cursor& c, int tbl) {
     const int e = __shfl(tbl, my_blk);
     const int phys = (e >= 0 && e < a.num_blocks) ? e : 0;
-    const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
+    const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)kv_of(c.h) * kTile +
                        (lane % BS) * kChunk;
     if constexpr (Fused) {
       // the run's last unit holds the new token (position len - 1, which the
       // pools do not hold yet): its lane reads the K row from k_new
       const int tn = c.len - 1 - (c.base + c.g * kGroupTokens);
       if (tn < kGroupTokens) {  // (uniform)
-        const half_t* np = a.k_new + ((int64_t)c.s * Hkv + c.h) * D;
+        const half_t* np = a.k_new + ((int64_t)c.s * Hkr + kv_of(c.h)) * D;
         const bool mine = lane == tn;
 #pragma unroll
         for (int cc = 0; cc < kChunks; ++cc)
@@ -534,22 +544,25 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const half_t* vp = a.v_cache + (int64_t)pb[g / kGroups] * block_stride +
-                         (int64_t)c.h * kTile + (int64_t)(g % kGroups) * D * kChunk;
+                         (int64_t)kv_of(c.h) * kTile + (int64_t)(g % kGroups) * D * kChunk;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vreg[g][st] = load_kv(vp + (st * 64 + lane) * kChunk);
     }
   };
-  // q rows of c's run; every lane loads (rows past G and lanes past the rows
-  // re-read row 0 and are zeroed at the LDS write) so the load is unconditional
+  // q rows of c's run; every lane loads (rows past the head's and lanes past
+  // the rows re-read row 0 and are zeroed at the LDS write) so the load is
+  // unconditional
   const int q_row = lane / kChunks, q_chunk = lane % kChunks;
+  int q_nr = 0;  // rows of the q load last issued
   auto load_q = [&](const Cursor& c) {
-    const int row = (q_row < G && q_row < 4) ? q_row : 0;
-    qreg = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)c.s * Hq + c.h * G + row) * D +
+    q_nr = q_rows(c.h);
+    const int row = q_row < q_nr ? q_row : 0;
+    qreg = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)c.s * Hq + q_first(c.h) + row) * D +
                                              q_chunk * kChunk);
   };
   // Shared: the prefix pass's first chunk for a run, loaded for a unit that
   // starts the run one iteration ahead, ahead of that unit's K (rows: dims
-  // 64 st + lane of head g; lane g < G: head g's log-sum-exp).  A piece that
+  // 64 st + lane of head g; lane g < rows: head g's log-sum-exp).  A piece that
   // starts a run begins from it, a piece of weight 1 at its log-sum-exp,
   // instead of from nothing: the run's online softmax then takes the prefix
   // in with no fold afterwards.  (Further chunks, of prefixes above one
@@ -558,19 +571,20 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   float pre_m = 0.0f;
   auto load_pre = [&](const Cursor& c) {
     if constexpr (Shared) {
-      const int64_t row0 = (int64_t)c.s * Hq + c.h * G;
+      const int64_t row0 = (int64_t)c.s * Hq + q_first(c.h);
+      const int nr = q_rows(c.h);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int st = 0; st < kSets; ++st)
-          pre_o[g][st] = g < G ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
-      pre_m = a.pre_lse[row0 + min(lane, G - 1)];
+          pre_o[g][st] = g < nr ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
+      pre_m = a.pre_lse[row0 + min(lane, nr - 1)];
     }
   };
   auto starts_with_pre = [&](const Cursor& c) { return Shared && c.valid && c.g == 0 && c.base > 0; };
   auto store_q = [&]() {
     if (q_row < 4) {
-      const half8_t v = q_row < G ? qreg : half8_t{};
+      const half8_t v = q_row < q_nr ? qreg : half8_t{};
       *reinterpret_cast<half8_t*>(q_lds + q_row * kQRow + q_chunk * kChunk) = v;
     }
   };
@@ -582,7 +596,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // that every iteration issues the same loads.
   auto load_new = [&](const Cursor& c, half_t (&vn)[kSets]) {
     if constexpr (Fused) {
-      const int64_t row = ((int64_t)c.s * Hkv + c.h) * D;
+      const int64_t row = ((int64_t)c.s * Hkr + kv_of(c.h)) * D;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
     }
@@ -602,13 +616,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       auto flush = [&]() {
         if (my_s >= 0 && ch < kChunks) {
           const int64_t slot = a.slot_mapping[my_s];
-          const int64_t row = ((int64_t)my_s * Hkv + my_h) * D + ch * kChunk;
+          const int64_t row = ((int64_t)my_s * Hkr + kv_of(my_h)) * D + ch * kChunk;
           const half8_t kr = *reinterpret_cast<const half8_t*>(a.k_new + row);
           const half8_t vr = *reinterpret_cast<const half8_t*>(a.v_new + row);
           if (slot >= 0 && slot < a.num_blocks * BS) {
             const int64_t b = slot / BS;
             const int o = (int)(slot - b * BS);
-            const int64_t tile = (b * Hkv + my_h) * kTile;
+            const int64_t tile = (b * Hkr + kv_of(my_h)) * kTile;
             *reinterpret_cast<half8_t*>(a.k_cache_w + tile + ((int64_t)ch * BS + o) * kChunk) = kr;
             half_t* vp = a.v_cache_w + tile + ((int64_t)(o / kChunk) * D + ch * kChunk) * kChunk +
                          o % kChunk;
@@ -624,7 +638,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         const int run0 = Hkv * uniform(off_lds[c.s]) + c.h * c.n_s;  // the run's first unit
         if (run0 >= end) break;
         const int last = run0 + c.n_s - 1;
-        if (last >= first && last < end) {
+        // (the first of a KV head's virtual heads stores its rows)
+        if (last >= first && last < end && c.h % split == 0) {
           if ((lane >> 4) == grp) {
             my_s = c.s;
             my_h = c.h;
@@ -659,9 +674,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // only what they use
   // (own_slot >= 0: the piece of that slot is not in the workspace but in
   // ring entry own_k, where the merger still holds it)
-  auto absorb = [&](auto batch, Merged& m, int sl, int nb, int own_slot, int own_k) {
+  auto absorb = [&](auto batch, Merged& m, int sl, int nb, int own_slot, int own_k, int nr) {
     constexpr int B = decltype(batch)::value;
-    const bool valid = pq < nb && gq < G;
+    const bool valid = pq < nb && gq < nr;
     const bool own = sl == own_slot;
     float m_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq) : -INFINITY;
     float l_p = valid ? load_through(a.ws.ml + (int64_t)sl * 8 + 2 * gq + 1) : 0.0f;
@@ -711,6 +726,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int n = uniform(run_units(s));
     const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
     const int r = s * Hkv + kvh;
+    const int nr = q_rows(kvh), q0 = q_first(kvh);
     // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
     // starts the run began from chunk 0), loaded before the pieces so that
     // the two round trips overlap
@@ -721,10 +737,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     int nch = 0;
     if constexpr (Shared) {
       nch = prefix_chunks(uniform(base_lds[s]));
-      const bool valid = gq < G;
+      const bool valid = gq < nr;
 #pragma unroll
       for (int c = 1; c < NC; ++c) {
-        const int64_t qrow = ((int64_t)min(c, max(nch - 1, 0)) * S + s) * Hq + kvh * G + (valid ? gq : 0);
+        const int64_t qrow = ((int64_t)min(c, max(nch - 1, 0)) * S + s) * Hq + q0 + (valid ? gq : 0);
         m_c[c] = (c < nch && valid) ? a.pre_lse[qrow] : -INFINITY;
         o_c[c] = c < nch ? *reinterpret_cast<const hvec_t*>(a.pre_o + qrow * D + pq * kF) : hvec_t{};
       }
@@ -738,11 +754,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const int v = va + p;
       const int sl = v == va ? r : R + v;
       if (nb <= 2)
-        absorb(std::integral_constant<int, 2>{}, m, sl, nb, own_slot, own_k);
+        absorb(std::integral_constant<int, 2>{}, m, sl, nb, own_slot, own_k, nr);
       else if (nb <= 4)
-        absorb(std::integral_constant<int, 4>{}, m, sl, nb, own_slot, own_k);
+        absorb(std::integral_constant<int, 4>{}, m, sl, nb, own_slot, own_k, nr);
       else
-        absorb(std::integral_constant<int, 16>{}, m, sl, nb, own_slot, own_k);
+        absorb(std::integral_constant<int, 16>{}, m, sl, nb, own_slot, own_k, nr);
     }
     // Shared: each chunk a piece of weight 1 (in lane pq = 0 of each row)
     // at its log-sum-exp
@@ -752,7 +768,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         if (c < nch) {
           const float m_new = fmaxf(m.mx, m_c[c]);
           const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m.mx - m_new);
-          const float wt = gq < G ? fast_exp2(m_c[c] - m_new) : 0.0f;
+          const float wt = gq < nr ? fast_exp2(m_c[c] - m_new) : 0.0f;
           m.lsum = m.lsum * alpha + (pq == 0 ? wt : 0.0f);
           m.mx = m_new;
 #pragma unroll
@@ -766,8 +782,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // counter for the next call
   auto merge_out = [&](int s, int kvh, const Merged& m) {
     const float inv = 1.0f / row_sum16(m.lsum);
-    if (gq < G) {
-      half_t* o = a.out + ((int64_t)s * Hq + kvh * G + gq) * D + pq * kF;
+    if (gq < q_rows(kvh)) {
+      half_t* o = a.out + ((int64_t)s * Hq + q_first(kvh) + gq) * D + pq * kF;
 #pragma unroll
       for (int j = 0; j < kF; ++j) o[j] = (half_t)(m.acc[j] * inv);
     }
@@ -788,10 +804,12 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   };
-  auto seed_pre = [&]() {  // a piece that starts a run with a prefix: begin from its first chunk
+  // a piece that starts a run (of nr query rows) with a prefix: begin from
+  // its first chunk
+  auto seed_pre = [&](int nr) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (g < G) {
+      if (g < nr) {
         m_run[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre_m), g));
         l_lane[g] = lane == 0 ? 1.0f : 0.0f;
 #pragma unroll
@@ -812,17 +830,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // Shared: chunks 1.. of a whole run's prefix (the streamer began the run
     // from chunk 0), loaded when the run comes
     half_t pf_o[kPrefixMaxChunks][4][kSets];  // dims 64 st + lane of head g, chunk c
-    float pf_m[kPrefixMaxChunks];             // lane g < G: head g's log-sum-exp, chunk c
+    float pf_m[kPrefixMaxChunks];             // lane g < rows: head g's log-sum-exp, chunk c
     auto load_pieces = [&](int s, int hh, int nch) {
 #pragma unroll
       for (int c = 1; c < kPrefixMaxChunks; ++c) {
-        const int64_t row0 = ((int64_t)c * S + s) * Hq + hh * G;
-        pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, G - 1)] : -INFINITY;
+        const int64_t row0 = ((int64_t)c * S + s) * Hq + q_first(hh);
+        const int nr = q_rows(hh);
+        pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, nr - 1)] : -INFINITY;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int st = 0; st < kSets; ++st)
-            pf_o[c][g][st] = (c < nch && g < G) ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
+            pf_o[c][g][st] = (c < nch && g < nr) ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
       }
     };
     int idle = 0;
@@ -894,12 +913,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           const int s_i = ps[i];
           const int nch = Shared ? prefix_chunks(uniform(base_lds[s_i])) : 0;
           if (Shared && nch > 1) load_pieces(s_i, ph[i], nch);
+          const int nr = q_rows(ph[i]), q0 = q_first(ph[i]);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            if (g < G) {
+            if (g < nr) {
               const float mr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g));
               const float lt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g + 1));
-              const int64_t row = (int64_t)s_i * Hq + ph[i] * G + g;
+              const int64_t row = (int64_t)s_i * Hq + q0 + g;
               float v[kSets], den = lt;
 #pragma unroll
               for (int st = 0; st < kSets; ++st) v[st] = pv[i][g][st];
@@ -932,13 +952,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         } else if (i < avail && !((fast >> i) & 1)) {
           // a cut piece: written through to its slot
           float* po = a.ws.o + pslot[i] * 4 * D;
+          const int nr = q_rows(ph[i]);
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            if (g < G)
+            if (g < nr)
 #pragma unroll
               for (int st = 0; st < kSets; ++st)
                 store_through(po + g * D + st * 64 + lane, pv[i][g][st]);
-          if (lane < 2 * G) store_through(a.ws.ml + pslot[i] * 8 + lane, pml[i]);
+          if (lane < 2 * nr) store_through(a.ws.ml + pslot[i] * 8 + lane, pml[i]);
         }
       }
       // the slots are written through before they are counted (a round
@@ -1019,19 +1040,20 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   store_q();
   __builtin_amdgcn_wave_barrier();
   reset_run();
-  if (starts_with_pre(cur)) seed_pre();
+  if (starts_with_pre(cur)) seed_pre(q_rows(cur.h));
   uint64_t t_iter = stamp_now();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
   while (cur.valid) {
     const int t0 = cur.base + cur.g * kGroupTokens;  // position of the unit's first token
+    const int nr = q_rows(cur.h);                    // query rows of the run
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.
     if (q_pending) {
       store_q();
-      if (starts_with_pre(cur)) seed_pre();
+      if (starts_with_pre(cur)) seed_pre(nr);
     }
     q_pending = false;
 
@@ -1042,7 +1064,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // row, read from LDS by every lane at once, in pairs of dims
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (g < G) {
+        if (g < nr) {
           float acc = 0.0f;
 #pragma unroll
           for (int c = 0; c < kChunks; ++c) {
@@ -1085,7 +1107,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       half_t ph = (half_t)0.0f;
-      if (g < G) {
+      if (g < nr) {
         const float z = live ? sacc[g] * a.scale_log2 : -INFINITY;
         const float m_new = fmaxf(m_run[g], wave_max(z));
         const float alpha = fast_exp2(m_run[g] - m_new);  // 0 at the piece's first unit
@@ -1137,7 +1159,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // pairs of tokens
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (g < G) {
+        if (g < nr) {
 #pragma unroll
           for (int grp = 0; grp < 8; ++grp) {
             const half8_t pv = *reinterpret_cast<const half8_t*>(p_lds + g * kPRow + grp * 8);
@@ -1175,7 +1197,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     if (run_end || !nxt.valid) {
       float l_tot[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) l_tot[g] = (g < G) ? wave_sum(l_lane[g]) : 1.0f;
+      for (int g = 0; g < 4; ++g) l_tot[g] = (g < nr) ? wave_sum(l_lane[g]) : 1.0f;
       // The piece goes to the merger through the LDS ring (wait while the
       // ring is full, which the merger rarely lets happen): a whole run
       // (slot -1), which the merger normalises and stores, or a cut piece: a

@@ -127,7 +127,10 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
-  int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int num_seqs, num_q_heads;
+  int num_kv_heads;  // virtual heads: KV heads x kv_split
+  int kv_split;      // virtual heads per KV head: ceil(G / kMaxGroup)
+  int head_dim;
   int block_size;  // 8, 16 or 32
   int max_blocks_per_seq;
   int64_t num_blocks;
@@ -222,7 +225,10 @@ struct PrefixArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
-  int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int num_seqs, num_q_heads;
+  int num_kv_heads;  // virtual heads, as DecodeArgs
+  int kv_split;
+  int head_dim;
   int block_size;
   int max_blocks_per_seq;
   int64_t num_blocks;

@@ -80,13 +80,19 @@ __global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const Pref
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;  // operand / result column: this lane's row of a sub-tile
   const int j = lane >> 4;    // k-slot group
-  const int S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  // (virtual heads as in the decode: a KV head of more than 4 query heads
+  // is kv_split heads of up to 4, Hkv counts them)
+  const int split = a.kv_split, Hkr = Hkv / split;
   // workgroup -> (chunk, window, KV head), the chunk slowest: chunks that
   // turn out empty (past a group's prefix) are dispatched last
   const int bid = (int)blockIdx.x;
   const int per_chunk = (int)(gridDim.x / a.max_chunks);
   const int chunk = bid / per_chunk;
   const int h = bid % Hkv;
+  const int hr = h / split;                                          // KV head of the pools
+  const int G = split == 1 ? Hq / Hkv : min(4, Hq / Hkr - h % split * 4);  // query rows per member
+  const int qh0 = hr * (Hq / Hkr) + h % split * 4;                   // their first query head
   const int s0 = (bid % per_chunk) / Hkv * kPrefixWindow;
   const int n = min(kPrefixWindow, S - s0);
 
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const Pref
       half8_t v = {};
       if (r < rows)
         v = *reinterpret_cast<const half8_t*>(
-            a.q + ((int64_t)(s0 + gf + r / G) * Hq + h * G + r % G) * D + 8 * c);
+            a.q + ((int64_t)(s0 + gf + r / G) * Hq + qh0 + r % G) * D + 8 * c);
       *reinterpret_cast<half8_t*>(q_lds + r * kQRow + 8 * c) = v;
     }
     __syncthreads();
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const Pref
     const int bk = (8 * gk) / BS, bv = (8 * j) / BS;
     const int klane = (j * BS + (8 * gk) % BS + (c16 & 3)) * 8;
     const int vlane = (((8 * j) % BS) / 8 * D + c16) * 8;
-    const int64_t hoff = (int64_t)h * kTile, bstride = (int64_t)Hkv * kTile;
+    const int64_t hoff = (int64_t)hr * kTile, bstride = (int64_t)Hkr * kTile;
     auto pick = [&](int sel, int b0, int b1, int b2, int b3) {
       if constexpr (NBS == 1) return b0;
       else if constexpr (NBS == 2) return sel ? b1 : b0;
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const Pref
       }
     }
     if (r < rows) {
-      const int64_t ro = ((int64_t)chunk * S + (s0 + gf + r / G)) * Hq + h * G + r % G;
+      const int64_t ro = ((int64_t)chunk * S + (s0 + gf + r / G)) * Hq + qh0 + r % G;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
       for (int d = 0; d < kDL; d += 4) {

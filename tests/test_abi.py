@@ -77,7 +77,9 @@ def test_decode_argument_errors(L):
     assert dec(L, hq=30) == E.PA_ERR_INVALID_ARG            # Hq % Hkv != 0
     assert dec(L, D=96) == E.PA_ERR_UNSUPPORTED
     assert dec(L, bs=24) == E.PA_ERR_UNSUPPORTED             # block size not 8, 16 or 32
-    assert dec(L, hq=64) == E.PA_ERR_UNSUPPORTED             # G = 8
+    # G = 8 and G = 7 (virtual heads): past the argument checks, to the missing workspace
+    assert dec(L, hq=64) == E.PA_ERR_WORKSPACE
+    assert dec(L, hq=56) == E.PA_ERR_WORKSPACE
     assert dec(L, maxctx=129) == E.PA_ERR_INVALID_ARG        # > 8 blocks * 16
     assert dec(L, S=-1) == E.PA_ERR_INVALID_ARG
     assert dec(L, workers=-3) == E.PA_ERR_INVALID_ARG
@@ -86,7 +88,7 @@ def test_decode_argument_errors(L):
     assert dec(L, S=0, out=NULL) == E.PA_OK                  # empty batch: no-op
     # a decode always needs its workspace
     assert dec(L) == E.PA_ERR_WORKSPACE
-    need = L.pa_decode_workspace_size(4, 8, 128, 100, 64)
+    need = L.pa_decode_workspace_size(4, 32, 8, 128, 100, 64)
     assert dec(L, ws=256, wsb=need - 1) == E.PA_ERR_WORKSPACE
     assert dec(L, ws=257, wsb=need) == E.PA_ERR_WORKSPACE    # misaligned
 
@@ -98,20 +100,30 @@ def test_workspace_sizes(L):
     # sequences x 8 KV heads x 4 query heads a log-sum-exp (fp32) and a row of
     # 128 fp16; then one arrival counter per run and 256 bytes ending in the
     # status word
-    need = L.pa_decode_workspace_size(64, 8, 128, 2048, 2048)
+    need = L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 2048)
     slots = 64 * 8 + 2048
     a256 = lambda x: -(-x // 256) * 256
     pre_rows = 4 * 64 * 8 * 4
     assert need == (slots * 8 * 4 + slots * 4 * 128 * 4 + a256(64 * 4) + a256(pre_rows * 4)
                     + a256(pre_rows * 128 * 2) + 64 * 8 * 4 + 256)
     # batches above one launch (4096 sequences) reuse the counters
-    assert (L.pa_decode_workspace_size(10000, 8, 128, 100, 64)
-            == L.pa_decode_workspace_size(4096, 8, 128, 100, 64))
-    assert L.pa_decode_workspace_size(64, 8, 64, 2048, 2048) < need
-    assert L.pa_decode_workspace_size(64, 8, 128, 2048, 4096) > need
-    assert L.pa_decode_workspace_size(-1, 8, 128, 100, 16) == 0
-    assert L.pa_decode_workspace_size(4, 8, 128, -1, 16) == 0
-    assert L.pa_decode_workspace_size(4, 8, 128, 100, -2) == 0
+    assert (L.pa_decode_workspace_size(10000, 32, 8, 128, 100, 64)
+            == L.pa_decode_workspace_size(4096, 32, 8, 128, 100, 64))
+    assert L.pa_decode_workspace_size(64, 32, 8, 64, 2048, 2048) < need
+    assert L.pa_decode_workspace_size(64, 32, 8, 128, 2048, 4096) > need
+    # fewer query heads per KV head take the same slots (4 rows each)
+    assert L.pa_decode_workspace_size(64, 8, 8, 128, 2048, 2048) == need
+    assert L.pa_decode_workspace_size(-1, 32, 8, 128, 100, 16) == 0
+    assert L.pa_decode_workspace_size(4, 32, 8, 128, -1, 16) == 0
+    assert L.pa_decode_workspace_size(4, 32, 8, 128, 100, -2) == 0
+    assert L.pa_decode_workspace_size(4, 30, 8, 128, 100, 16) == 0   # Hq % Hkv != 0
+    # a KV head of G = 8 or 7 query heads: 2 virtual heads of up to 4 rows
+    for hq in (64, 56):
+        v = 64 * 16 + 2048
+        pre = 4 * 64 * 16 * 4
+        assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
+            v * 8 * 4 + v * 4 * 128 * 4 + a256(64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
+            + 64 * 16 * 4 + 256)
 
 
 def test_cache_op_argument_errors(L):

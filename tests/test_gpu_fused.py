@@ -177,7 +177,8 @@ def test_fused_and_plain_share_a_workspace():
     every call leaves the arrival counters at zero."""
     big = wl.make_workload("fused-ws1", 344, 32, 8, 128, len_range=(100, 3000), num_seqs=40)
     small = wl.make_workload("fused-ws2", 345, 8, 2, 64, context_lens=FUSED_LENS)
-    n = max(pk.pa_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len, 64)
+    n = max(pk.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                        w.max_context_len, 64)
             for w in (big, small))
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     for w, fused in ((big, True), (small, False), (small, True), (big, False)):
@@ -212,7 +213,7 @@ def test_fused_errors():
     assert code == pk.PA_ERR_INVALID_ARG
     # a misaligned K row buffer
     kn = torch.empty(d["k_new"].numel() + 1, dtype=torch.float16, device="cuda")
-    ws = pk.new_workspace(2, 2, 64, w.max_context_len)
+    ws = pk.new_workspace(2, 8, 2, 64, w.max_context_len)
     code = L.pa_decode_append(d["out"].data_ptr(), d["q"].data_ptr(), kn.data_ptr() + 2,
                               d["v_new"].data_ptr(), d["slot_mapping"].data_ptr(),
                               d["k_cache"].data_ptr(), d["v_cache"].data_ptr(),
@@ -230,7 +231,8 @@ def test_fused_errors():
     assert code == pk.PA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("name", ["llama8b_b64", "prefix_b256", "opt13b_b128", "longctx_b16"])
+@pytest.mark.parametrize("name", ["llama8b_b64", "prefix_b256", "opt13b_b128", "longctx_b16",
+                                  "llama70b_b64"])
 def test_fused_full_size(name):
     """The benchmark's batches in its launch configuration (automatic worker
     count, the shared-blocks flag where blocks are shared): pools bit for bit,

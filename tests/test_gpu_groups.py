@@ -1,0 +1,79 @@
+"""Decode with more than 4 query heads per KV head (GQA groups of 5 to 16),
+on the GPU, through the C-ABI, against the oracle.
+
+The decode's matrix instruction holds 4 query rows, so a KV head of G > 4
+query heads is attended as ceil(G / 4) virtual heads of up to 4 rows (the
+last one short when 4 does not divide G), each a run of its own over the KV
+head's K and V.  The cases cover groups that 4 divides and groups it does
+not, both head dimensions and every block size, the plain and the fused
+decode (pools bit for bit), cut runs (many workers) and one worker holding
+every run, the shared-prefix pass, and the batch above one launch.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_59_amd import workloads as wl
+from tests.gpu_util import compare, gpu_step, log, oracle_decode, oracle_pools, to_device
+from tests.test_gpu_fused import FUSED_LENS, run_fused
+
+pytestmark = pytest.mark.gpu
+
+# (Hq, Hkv, D): G = 8 (4 + 4), 7 (4 + 3), 5 (4 + 1), 6 (4 + 2), 12, 16
+GROUPS = [(8, 1, 128), (64, 8, 128), (28, 4, 128), (5, 1, 64), (12, 2, 64), (16, 1, 128),
+          (6, 1, 128)]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", GROUPS)
+@pytest.mark.parametrize("workers", [0, 1, 7, 5000])
+def test_decode_large_groups(Hq, Hkv, D, workers):
+    w = wl.make_workload("groups", 400 + Hq + Hkv + D, Hq, Hkv, D, context_lens=FUSED_LENS)
+    log(f"decode G{Hq // Hkv} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
+    d = to_device(w)
+    out = gpu_step(w, d, workers)
+    kc, vc = oracle_pools(w)
+    compare(out, oracle_decode(w, kc, vc), f"decode G{Hq // Hkv} D{D} workers{workers}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", GROUPS)
+@pytest.mark.parametrize("workers", [0, 5000])
+def test_fused_large_groups(Hq, Hkv, D, workers):
+    """The new rows are stored once per KV head (by its first virtual head)
+    and enter every virtual head's attention."""
+    w = wl.make_workload("groups-fused", 420 + Hq + Hkv + D, Hq, Hkv, D, context_lens=FUSED_LENS)
+    run_fused(w, workers, f"fused G{Hq // Hkv} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
+
+
+@pytest.mark.parametrize("BS", [8, 32])
+def test_large_group_block_sizes(BS):
+    w = wl.make_workload("groups-bs", 440 + BS, 28, 4, 128, context_lens=FUSED_LENS,
+                         block_size=BS)
+    run_fused(w, 0, f"fused G7 BS{BS}")
+
+
+@pytest.mark.parametrize("workers", [64, 512])
+def test_large_group_long_runs_cut(workers):
+    """Two long runs per KV head, cut into a piece per worker: every virtual
+    head's pieces merge on their own."""
+    w = wl.make_workload("groups-long", 450 + workers, 8, 1, 128, context_lens=[9000, 70, 4097])
+    run_fused(w, workers, f"fused G8 long runs over {workers} workers")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64)])
+@pytest.mark.parametrize("workers", [0, 5000])
+def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
+    """The prefix pass attends each virtual head's rows of a group's members
+    (up to 8 x 4) to the common prefix; a prefix of two chunks."""
+    w = wl.make_workload("groups-prefix", 460 + Hq + D, Hq, Hkv, D, num_seqs=18, prefix_groups=3,
+                         prefix_len=1536, suffix_range=(1, 300))
+    assert w.shares_blocks()
+    run_fused(w, workers, f"prefix G{Hq // Hkv} Hq{Hq} D{D} workers{workers}",
+              shared_blocks=True)
+
+
+def test_large_group_batch_above_one_launch():
+    w = wl.make_workload("groups-wide", 470, 8, 1, 64, len_range=(1, 40), num_seqs=4100)
+    d = to_device(w)
+    out = gpu_step(w, d, 0)
+    kc, vc = oracle_pools(w)
+    seqs = np.r_[0:40, 4050:4100]
+    compare(out[seqs], oracle_decode(w, kc, vc, seqs), "G8 4100 sequences")

@@ -252,7 +252,7 @@ def test_workspace_reuse_leaves_counters_zero():
     w2 = wl.make_workload("reuse2", 217, 32, 8, 128, len_range=(1, 500), num_seqs=5)
     workers = 50
     ws_len = max(w1.max_context_len, w2.max_context_len)
-    ws = pk.new_workspace(7, 8, 128, ws_len, workers)
+    ws = pk.new_workspace(7, 32, 8, 128, ws_len, workers)
     for rep in range(3):
         for w in (w1, w2):
             d = to_device(w)

@@ -35,7 +35,7 @@ def test_status_word_reports_a_wait_that_gives_up():
     # unit its own share, so runs are cut and the merger has work
     w = wl.make_workload("status", 77, 8, 2, 64, num_seqs=6, len_range=(100, 400))
     d = to_device(w)
-    ws = pk.new_workspace(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_context_len)
+    ws = pk.new_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)
     kc, vc = oracle_pools(w)
     ref = oracle_decode(w, kc, vc)
 
