@@ -173,7 +173,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   const int32_t* row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int last_blk = (len + BS - 1) / BS - 1;
   const int64_t hoff = (int64_t)h * kTile;
-  const int64_t bstride = (int64_t)a.num_kv_heads * kTile;
+  // elements per physical block (all heads); below 2^32, so a block's
+  // offset is one 32 x 32 -> 64-bit product
+  const uint32_t bstride = (uint32_t)a.num_kv_heads * (uint32_t)kTile;
+  // ids at or past the pool's end (or negative) are broken entries
+  const uint32_t nblk = (uint32_t)min(a.num_blocks, (int64_t)0x7fffffff);
   // physical block of logical block lb (clamped to the sequence's last): a
   // scalar load, whose wait (lgkmcnt) does not drain the loads in flight
   // (read through the constant address space: a scalar load, which the LDS
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       (const __attribute__((address_space(4))) int32_t*)row;
   auto phys_of = [&](int lb) -> int {
     const int e = crow[__builtin_amdgcn_readfirstlane(min(lb, last_blk))];
-    return (e >= 0 && e < a.num_blocks) ? e : 0;  // a broken table entry reads block 0
+    return (uint32_t)e < nblk ? e : 0;  // a broken table entry reads block 0
   };
   // The NBS blocks of a step (keys i BS .. i BS + BS - 1 in block i), as
   // separate scalars (uniform): a lane picks its own with selects.  (Held
@@ -228,13 +232,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // step the lane selects between two 64-bit offsets; with four it selects
     // the block id and multiplies.  Each form measured the faster at its
     // block size (at 8: 317 against 329 us; at 16: 287 against 299 us).
-    const int64_t o0 = (int64_t)b0 * bstride + hoff, o1 = (int64_t)b1 * bstride + hoff;
+    auto boff = [&](int b) { return (int64_t)((uint64_t)(uint32_t)b * bstride) + hoff; };
+    const int64_t o0 = boff(b0), o1 = boff(b1);
     auto sel = [&](int i) -> int64_t {
       if constexpr (NBS == 1) return o0;
       else if constexpr (NBS == 2) return (i & 1) ? o1 : o0;
       else {
         const int lo = (i & 1) ? b1 : b0, hi = (i & 1) ? b3 : b2;
-        return (int64_t)((i & 2) ? hi : lo) * bstride + hoff;
+        return boff((i & 2) ? hi : lo);
       }
     };
 #pragma unroll
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // past a row's position (removed: z = -inf) or past the context (V := 0
     // by selection: the last block's tail holds any bits, NaN included, and
     // 0 * NaN would not be 0).  One uniform branch for both.
-    if (__builtin_amdgcn_readfirstlane(st * 32 + 31 > pos_first)) {
+    if (st * 32 + 31 > pos_first) {  // (uniform: st and pos_first are)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kp = st * 32 + 8 * j + e;
