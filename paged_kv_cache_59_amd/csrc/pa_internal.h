@@ -168,9 +168,10 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, const int32_t* orde
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                          hipEvent_t stop);
 
-// Multi-query paged attention (chunked prefill).  One wave per tile of 32
-// rows of one (sequence, KV head); a workgroup holds 4 such tiles, and
-// tile_groups workgroups cover the longest chunk: ceil(max_query_len * G / 128).
+// Multi-query paged attention (chunked prefill).  One wave per tile of
+// kPrefillWaveRows rows of one (sequence, KV head); a workgroup holds 4 such
+// tiles, and tile_groups workgroups cover the longest chunk:
+// ceil(max_query_len * G / (4 kPrefillWaveRows)).
 struct PrefillArgs {
   half_t* out;
   const half_t* q;
@@ -192,6 +193,7 @@ struct PrefillArgs {
 
 // 32-key K/V steps a prefill workgroup keeps in its LDS ring (64 KiB at D = 128)
 constexpr int kPrefillStages = 4;
+constexpr int kPrefillWaveRows = 32;  // query rows of one wave
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
