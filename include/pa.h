@@ -169,8 +169,8 @@ int32_t pa_decode_num_workers(void);
  * device).  Returns 0 for invalid sizes (num_q_heads not a multiple of
  * num_kv_heads included).  The workspace holds, from its start, the partial
  * results of sequences cut between workers (one per (sequence, KV head)
- * run and one per worker, 4 query-head rows each; a KV head of G > 4 query
- * heads counts as ceil(G / 4) heads here and below), then
+ * run and one per worker, 4 query-head rows each; with G > 4 query heads
+ * per KV head each sequence counts ceil(G / 4) times here and below), then
  * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
  * its prefix length, per (chunk, sequence, query head) up to 4 normalised
  * fp16 rows and their log-sum-exps) and, against its end, one arrival
@@ -230,8 +230,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.
  * Any G >= 1: the grouped query heads of a KV head (up to 4 at a time, the
- * rows of the decode's matrix instruction) share each K and V load, so a
- * group of G > 4 reads its KV head's K and V ceil(G / 4) times.
+ * rows of the decode's matrix instruction) share each K and V load; a group
+ * of G > 4 is attended in ceil(G / 4) sub-groups, each a copy of the batch
+ * in the same launch, whose reads of one block fall at the same time (the
+ * L2 serves part of the repeats).
  * num_seqs == 0 is a no-op.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -34,11 +34,17 @@ bool block_size_supported(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The decode's heads: a KV head of G > kMaxGroup query heads counts as
-// ceil(G / kMaxGroup) virtual heads of up to kMaxGroup query heads each
-// (num_q_heads a multiple of num_kv_heads).
-int32_t virtual_kv_heads(int32_t num_q_heads, int32_t num_kv_heads) {
-  return num_kv_heads * (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
+// The decode attends a KV head of G > kMaxGroup query heads in
+// ceil(G / kMaxGroup) sub-groups of up to kMaxGroup query heads, one copy of
+// the batch per sub-group (num_q_heads a multiple of num_kv_heads).
+int32_t kv_split(int32_t num_q_heads, int32_t num_kv_heads) {
+  return (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
+}
+// Sequences of one decode launch: its copies of the batch (split of them)
+// fill at most kMaxSeqsPerLaunch virtual sequences.
+int64_t seqs_per_launch(int64_t num_seqs, int32_t split) {
+  const int64_t cap = pa::kMaxSeqsPerLaunch / split;
+  return num_seqs < cap ? num_seqs : cap;
 }
 
 // Decode workers for the current device: kWorkersPerCU per compute unit,
@@ -157,8 +163,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
     return 0;
   const int32_t w = resolve_workers(num_workers);
   if (w <= 0) return 0;
-  const int64_t s = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
-  return pa::decode_workspace_bytes(s, virtual_kv_heads(num_q_heads, num_kv_heads), head_dim, w);
+  const int32_t split = kv_split(num_q_heads, num_kv_heads);
+  return pa::decode_workspace_bytes(seqs_per_launch(num_seqs, split) * split, num_kv_heads,
+                                    head_dim, w);
 }
 
 }  // extern "C"
@@ -192,23 +199,23 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   if (fused && (!k_new || !v_new || !slot_mapping || (reinterpret_cast<uintptr_t>(k_new) & 15) ||
                 (reinterpret_cast<uintptr_t>(v_new) & 15)))
     return PA_ERR_INVALID_ARG;
-  // one launch takes at most kMaxSeqsPerLaunch sequences; its 64-token units
-  // (all heads) must fit a 32-bit index
-  const int64_t per_launch = num_seqs < pa::kMaxSeqsPerLaunch ? num_seqs : pa::kMaxSeqsPerLaunch;
-  // a KV head of more than kMaxGroup query heads is attended as split
-  // virtual heads of up to kMaxGroup each (hv of them in all)
-  const int32_t split = (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
-  const int32_t hv = virtual_kv_heads(num_q_heads, num_kv_heads);
-  if (per_launch * hv * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
+  // A KV head of more than kMaxGroup query heads is attended in split
+  // sub-groups, one copy of the batch each: a launch sees split x n virtual
+  // sequences, at most kMaxSeqsPerLaunch; its 64-token units (all heads)
+  // must fit a 32-bit index
+  const int32_t split = kv_split(num_q_heads, num_kv_heads);
+  const int64_t per_launch = seqs_per_launch(num_seqs, split);
+  const int64_t vseqs = per_launch * split;
+  if (vseqs * num_kv_heads * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
     return PA_ERR_UNSUPPORTED;
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
   const size_t need =
-      pa::decode_workspace_bytes(per_launch, hv, head_dim, w);
+      pa::decode_workspace_bytes(vseqs, num_kv_heads, head_dim, w);
   if (static_scratch) {
     // the library's own device array stands in for the workspace
     if (need > pa::kStaticScratchBytes ||
-        pa::decode_control_bytes(per_launch, hv) > pa::kStaticControlBytes)
+        pa::decode_control_bytes(vseqs, num_kv_heads) > pa::kStaticControlBytes)
       return PA_ERR_SCRATCH_LIMIT;
     if (pa::decode_static_scratch(stream, &workspace) != hipSuccess) return PA_ERR_HIP;
     workspace_bytes = pa::kStaticScratchBytes;
@@ -217,12 +224,12 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
-  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, per_launch, hv, head_dim, w);
+  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, vseqs, num_kv_heads, head_dim, w);
   a.k_cache = static_cast<const pa::half_t*>(k_cache);
   a.v_cache = static_cast<const pa::half_t*>(v_cache);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2
   a.num_q_heads = num_q_heads;
-  a.num_kv_heads = hv;
+  a.num_kv_heads = num_kv_heads;
   a.kv_split = split;
   a.head_dim = head_dim;
   a.block_size = block_size;
@@ -249,7 +256,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     a.q = static_cast<const pa::half_t*>(q) + row;
     a.block_tables = block_tables + s0 * max_blocks_per_seq;
     a.context_lens = context_lens + s0;
-    a.num_seqs = (int)n;
+    a.num_seqs = (int)(n * split);
     if (fused) {
       const int64_t rows = s0 * num_kv_heads * head_dim;
       a.k_new = static_cast<const pa::half_t*>(k_new) + rows;
@@ -270,7 +277,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
       p.scale_log2 = a.scale_log2;
       p.num_seqs = (int)n;
       p.num_q_heads = num_q_heads;
-      p.num_kv_heads = hv;
+      p.num_kv_heads = num_kv_heads * split;  // (the pass takes sub-groups as heads)
       p.kv_split = split;
       p.head_dim = head_dim;
       p.block_size = block_size;

@@ -34,8 +34,13 @@
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
 //    would cost 64 per lane and halve the waves a SIMD holds).  A larger
-//    group is split into ceil(G / 4) virtual heads of up to 4 rows, each its
-//    own run over the KV head's K and V (which it then reads that often).
+//    group is split into ceil(G / 4) sub-groups of up to 4 rows, and the
+//    batch is attended once per sub-group: the launch sees kv_split x S
+//    virtual sequences, sub-group j's copy of sequence s at j S + s.  Its
+//    units then lie exactly j / kv_split of the way along, so with equal
+//    shares the workers that read one block for different sub-groups read it
+//    at the same time, and (for an even split of the workers into runs of 32
+//    per XCD) on the same XCD, whose L2 serves the repeats.
 //  * q . K: lane l owns token l of the 64; it loads its 16-byte chunks of the
 //    K row (K pool [NB][Hkv][D/8][16][8]: for a fixed chunk the 64 lanes read
 //    four contiguous 256-byte runs) and feeds them as the B operand, so the
@@ -240,15 +245,20 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
-  // Virtual heads: a KV head with more than 4 query heads is attended as
-  // kv_split consecutive virtual heads (Hkv counts those) of up to 4 query
-  // heads each, the 4 rows of the MFMA; each reads its KV head's K and V.
+  // Sub-groups: a KV head with more than 4 query heads is attended in
+  // kv_split sub-groups of up to 4 query heads (the 4 rows of the MFMA), one
+  // per copy of the batch: S counts the virtual sequences, sub-group
+  // s / Sr of sequence s % Sr.
   const int split = a.kv_split;
-  const int Hkr = Hkv / split;  // KV heads of the pools, k_new and v_new
-  const int G = Hq / Hkr;       // query heads per KV head
-  auto kv_of = [&](int h) { return split == 1 ? h : h / split; };
-  auto q_first = [&](int h) { return split == 1 ? h * G : h / split * G + h % split * 4; };
-  auto q_rows = [&](int h) { return split == 1 ? G : min(4, G - h % split * 4); };
+  const int Sr = S / split;  // sequences of the batch (lengths, tables, new rows)
+  const int G = Hq / Hkv;    // query heads per KV head
+  auto sub_of = [&](int s) { return split == 1 ? 0 : s / Sr; };
+  auto real_of = [&](int s) { return split == 1 ? s : s - s / Sr * Sr; };
+  auto q_rows = [&](int s) { return split == 1 ? G : min(4, G - sub_of(s) * 4); };
+  // the q / out row of the first query head of run (s, h)
+  auto q_row0 = [&](int s, int h) -> int64_t {
+    return (int64_t)real_of(s) * Hq + h * G + sub_of(s) * 4;
+  };
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
   int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
@@ -269,8 +279,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int b = 0; b < kLenBatch; ++b) {
       const int s = cb + 64 * b + lane;
-      len_in[b] = s < S ? a.context_lens[s] : 0;
-      pre_in[b] = (Shared && s < S) ? a.pre_len[s] : 0;
+      len_in[b] = s < S ? a.context_lens[real_of(s)] : 0;
+      pre_in[b] = (Shared && s < S) ? a.pre_len[real_of(s)] : 0;
     }
 #pragma unroll
     for (int b = 0; b < kLenBatch; ++b) {
@@ -288,7 +298,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         if constexpr (Shared) base_lds[s] = pre;
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
-      uint64_t empty = streamer ? __ballot(s < S && n == 0 && (s % nw) == w) : 0;
+      // (the first sub-group's copy clears every row of the sequence)
+      uint64_t empty = streamer ? __ballot(s < Sr && n == 0 && (s % nw) == w) : 0;
       while (empty) {
         const int se = c0 + __builtin_ctzll(empty);
         empty &= empty - 1;
@@ -490,14 +501,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
   const int my_blk = lane / BS;  // which of a unit's blocks holds this lane's token
   const int g_lane = lane & 3;   // q head of the group this lane's MFMA row carries
-  const int64_t block_stride = (int64_t)Hkr * kTile;
+  const int64_t block_stride = (int64_t)Hkv * kTile;
 
   // Table entries of unit c's NBU blocks: one vector load, lane i reads
   // entry NBU g + i % NBU.  Blocks past the sequence's last re-read its last
   // block, so every unit issues the same loads; positions past the end are
   // removed later by position.
   auto load_table = [&](const Cursor& c) {
-    const int32_t* row = a.block_tables + (int64_t)c.s * a.max_blocks_per_seq;
+    const int32_t* row = a.block_tables + (int64_t)real_of(c.s) * a.max_blocks_per_seq;
     const int last = (c.len + BS - 1) / BS - 1;
     return row[min(c.base / BS + NBU * c.g + (lane % NBU), last)];
   };
@@ -520,14 +531,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   auto load_k = [&](const Cursor& c, int tbl) {
     const int e = __shfl(tbl, my_blk);
     const int phys = (e >= 0 && e < a.num_blocks) ? e : 0;
-    const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)kv_of(c.h) * kTile +
+    const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
                        (lane % BS) * kChunk;
     if constexpr (Fused) {
       // the run's last unit holds the new token (position len - 1, which the
       // pools do not hold yet): its lane reads the K row from k_new
       const int tn = c.len - 1 - (c.base + c.g * kGroupTokens);
       if (tn < kGroupTokens) {  // (uniform)
-        const half_t* np = a.k_new + ((int64_t)c.s * Hkr + kv_of(c.h)) * D;
+        const half_t* np = a.k_new + ((int64_t)real_of(c.s) * Hkv + c.h) * D;
         const bool mine = lane == tn;
 #pragma unroll
         for (int cc = 0; cc < kChunks; ++cc)
@@ -544,7 +555,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const half_t* vp = a.v_cache + (int64_t)pb[g / kGroups] * block_stride +
-                         (int64_t)kv_of(c.h) * kTile + (int64_t)(g % kGroups) * D * kChunk;
+                         (int64_t)c.h * kTile + (int64_t)(g % kGroups) * D * kChunk;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vreg[g][st] = load_kv(vp + (st * 64 + lane) * kChunk);
     }
@@ -555,9 +566,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int q_row = lane / kChunks, q_chunk = lane % kChunks;
   int q_nr = 0;  // rows of the q load last issued
   auto load_q = [&](const Cursor& c) {
-    q_nr = q_rows(c.h);
+    q_nr = q_rows(c.s);
     const int row = q_row < q_nr ? q_row : 0;
-    qreg = *reinterpret_cast<const half8_t*>(a.q + ((int64_t)c.s * Hq + q_first(c.h) + row) * D +
+    qreg = *reinterpret_cast<const half8_t*>(a.q + (q_row0(c.s, c.h) + row) * D +
                                              q_chunk * kChunk);
   };
   // Shared: the prefix pass's first chunk for a run, loaded for a unit that
@@ -571,8 +582,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   float pre_m = 0.0f;
   auto load_pre = [&](const Cursor& c) {
     if constexpr (Shared) {
-      const int64_t row0 = (int64_t)c.s * Hq + q_first(c.h);
-      const int nr = q_rows(c.h);
+      const int64_t row0 = q_row0(c.s, c.h);
+      const int nr = q_rows(c.s);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // that every iteration issues the same loads.
   auto load_new = [&](const Cursor& c, half_t (&vn)[kSets]) {
     if constexpr (Fused) {
-      const int64_t row = ((int64_t)c.s * Hkr + kv_of(c.h)) * D;
+      const int64_t row = ((int64_t)real_of(c.s) * Hkv + c.h) * D;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
     }
@@ -616,13 +627,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       auto flush = [&]() {
         if (my_s >= 0 && ch < kChunks) {
           const int64_t slot = a.slot_mapping[my_s];
-          const int64_t row = ((int64_t)my_s * Hkr + kv_of(my_h)) * D + ch * kChunk;
+          const int64_t row = ((int64_t)my_s * Hkv + my_h) * D + ch * kChunk;
           const half8_t kr = *reinterpret_cast<const half8_t*>(a.k_new + row);
           const half8_t vr = *reinterpret_cast<const half8_t*>(a.v_new + row);
           if (slot >= 0 && slot < a.num_blocks * BS) {
             const int64_t b = slot / BS;
             const int o = (int)(slot - b * BS);
-            const int64_t tile = (b * Hkr + kv_of(my_h)) * kTile;
+            const int64_t tile = (b * Hkv + my_h) * kTile;
             *reinterpret_cast<half8_t*>(a.k_cache_w + tile + ((int64_t)ch * BS + o) * kChunk) = kr;
             half_t* vp = a.v_cache_w + tile + ((int64_t)(o / kChunk) * D + ch * kChunk) * kChunk +
                          o % kChunk;
@@ -638,8 +649,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         const int run0 = Hkv * uniform(off_lds[c.s]) + c.h * c.n_s;  // the run's first unit
         if (run0 >= end) break;
         const int last = run0 + c.n_s - 1;
-        // (the first of a KV head's virtual heads stores its rows)
-        if (last >= first && last < end && c.h % split == 0) {
+        // (the first sub-group's copy of the sequence stores its rows)
+        if (last >= first && last < end && c.s < Sr) {
           if ((lane >> 4) == grp) {
             my_s = c.s;
             my_h = c.h;
@@ -726,7 +737,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int n = uniform(run_units(s));
     const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
     const int r = s * Hkv + kvh;
-    const int nr = q_rows(kvh), q0 = q_first(kvh);
+    const int nr = q_rows(s);
+    const int64_t q0 = q_row0(s, kvh) - (int64_t)real_of(s) * Hq;  // (its first query head)
     // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
     // starts the run began from chunk 0), loaded before the pieces so that
     // the two round trips overlap
@@ -740,7 +752,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const bool valid = gq < nr;
 #pragma unroll
       for (int c = 1; c < NC; ++c) {
-        const int64_t qrow = ((int64_t)min(c, max(nch - 1, 0)) * S + s) * Hq + q0 + (valid ? gq : 0);
+        const int64_t qrow = ((int64_t)min(c, max(nch - 1, 0)) * Sr + real_of(s)) * Hq + q0 + (valid ? gq : 0);
         m_c[c] = (c < nch && valid) ? a.pre_lse[qrow] : -INFINITY;
         o_c[c] = c < nch ? *reinterpret_cast<const hvec_t*>(a.pre_o + qrow * D + pq * kF) : hvec_t{};
       }
@@ -782,8 +794,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // counter for the next call
   auto merge_out = [&](int s, int kvh, const Merged& m) {
     const float inv = 1.0f / row_sum16(m.lsum);
-    if (gq < q_rows(kvh)) {
-      half_t* o = a.out + ((int64_t)s * Hq + q_first(kvh) + gq) * D + pq * kF;
+    if (gq < q_rows(s)) {
+      half_t* o = a.out + (q_row0(s, kvh) + gq) * D + pq * kF;
 #pragma unroll
       for (int j = 0; j < kF; ++j) o[j] = (half_t)(m.acc[j] * inv);
     }
@@ -834,8 +846,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     auto load_pieces = [&](int s, int hh, int nch) {
 #pragma unroll
       for (int c = 1; c < kPrefixMaxChunks; ++c) {
-        const int64_t row0 = ((int64_t)c * S + s) * Hq + q_first(hh);
-        const int nr = q_rows(hh);
+        const int64_t row0 = ((int64_t)c * Sr + real_of(s)) * Hq + hh * G + sub_of(s) * 4;
+        const int nr = q_rows(s);
         pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, nr - 1)] : -INFINITY;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -913,13 +925,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           const int s_i = ps[i];
           const int nch = Shared ? prefix_chunks(uniform(base_lds[s_i])) : 0;
           if (Shared && nch > 1) load_pieces(s_i, ph[i], nch);
-          const int nr = q_rows(ph[i]), q0 = q_first(ph[i]);
+          const int nr = q_rows(s_i);
+          const int64_t row_0 = q_row0(s_i, ph[i]);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             if (g < nr) {
               const float mr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g));
               const float lt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pml[i]), 2 * g + 1));
-              const int64_t row = (int64_t)s_i * Hq + q0 + g;
+              const int64_t row = row_0 + g;
               float v[kSets], den = lt;
 #pragma unroll
               for (int st = 0; st < kSets; ++st) v[st] = pv[i][g][st];
@@ -952,7 +965,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         } else if (i < avail && !((fast >> i) & 1)) {
           // a cut piece: written through to its slot
           float* po = a.ws.o + pslot[i] * 4 * D;
-          const int nr = q_rows(ph[i]);
+          const int nr = q_rows(ps[i]);
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             if (g < nr)
@@ -1040,14 +1053,14 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   store_q();
   __builtin_amdgcn_wave_barrier();
   reset_run();
-  if (starts_with_pre(cur)) seed_pre(q_rows(cur.h));
+  if (starts_with_pre(cur)) seed_pre(q_rows(cur.s));
   uint64_t t_iter = stamp_now();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
   while (cur.valid) {
     const int t0 = cur.base + cur.g * kGroupTokens;  // position of the unit's first token
-    const int nr = q_rows(cur.h);                    // query rows of the run
+    const int nr = q_rows(cur.s);                    // query rows of the run
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.

@@ -127,9 +127,9 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
-  int num_seqs, num_q_heads;
-  int num_kv_heads;  // virtual heads: KV heads x kv_split
-  int kv_split;      // virtual heads per KV head: ceil(G / kMaxGroup)
+  int num_seqs;      // virtual sequences: kv_split copies of the batch
+  int num_q_heads, num_kv_heads;
+  int kv_split;      // query-head sub-groups per KV head: ceil(G / kMaxGroup)
   int head_dim;
   int block_size;  // 8, 16 or 32
   int max_blocks_per_seq;
@@ -228,8 +228,8 @@ struct PrefixArgs {
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
   int num_seqs, num_q_heads;
-  int num_kv_heads;  // virtual heads, as DecodeArgs
-  int kv_split;
+  int num_kv_heads;  // KV heads x kv_split: each query-head sub-group counts as a head
+  int kv_split;      // sub-groups (of up to kMaxGroup query heads) per KV head
   int head_dim;
   int block_size;
   int max_blocks_per_seq;

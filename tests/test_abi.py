@@ -117,13 +117,14 @@ def test_workspace_sizes(L):
     assert L.pa_decode_workspace_size(4, 32, 8, 128, -1, 16) == 0
     assert L.pa_decode_workspace_size(4, 32, 8, 128, 100, -2) == 0
     assert L.pa_decode_workspace_size(4, 30, 8, 128, 100, 16) == 0   # Hq % Hkv != 0
-    # a KV head of G = 8 or 7 query heads: 2 virtual heads of up to 4 rows
+    # a KV head of G = 8 or 7 query heads: 2 sub-groups of up to 4 rows, one
+    # copy of the batch each (128 virtual sequences x 8 KV heads)
     for hq in (64, 56):
-        v = 64 * 16 + 2048
-        pre = 4 * 64 * 16 * 4
+        v = 128 * 8 + 2048
+        pre = 4 * 128 * 8 * 4
         assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
-            v * 8 * 4 + v * 4 * 128 * 4 + a256(64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
-            + 64 * 16 * 4 + 256)
+            v * 8 * 4 + v * 4 * 128 * 4 + a256(128 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
+            + 128 * 8 * 4 + 256)
 
 
 def test_cache_op_argument_errors(L):

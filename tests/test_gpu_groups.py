@@ -2,19 +2,22 @@
 on the GPU, through the C-ABI, against the oracle.
 
 The decode's matrix instruction holds 4 query rows, so a KV head of G > 4
-query heads is attended as ceil(G / 4) virtual heads of up to 4 rows (the
-last one short when 4 does not divide G), each a run of its own over the KV
-head's K and V.  The cases cover groups that 4 divides and groups it does
+query heads is attended in ceil(G / 4) sub-groups of up to 4 rows (the last
+one short when 4 does not divide G), one copy of the batch per sub-group in
+the same launch.  The cases cover groups that 4 divides and groups it does
 not, both head dimensions and every block size, the plain and the fused
-decode (pools bit for bit), cut runs (many workers) and one worker holding
-every run, the shared-prefix pass, and the batch above one launch.
+decode (pools bit for bit: only the first copy stores the new rows), cut
+runs (many workers) and one worker holding every run, the shared-prefix
+pass, and batches above one launch (4096 virtual sequences: 2048 sequences
+at G = 8).
 """
 import numpy as np
 import pytest
 
 from paged_kv_cache_59_amd import workloads as wl
-from tests.gpu_util import compare, gpu_step, log, oracle_decode, oracle_pools, to_device
-from tests.test_gpu_fused import FUSED_LENS, run_fused
+from tests.gpu_util import (assert_pools_equal, compare, gpu_step, log, oracle_decode,
+                            oracle_pools, to_device)
+from tests.test_gpu_fused import FUSED_LENS, fused_step, run_fused
 
 pytestmark = pytest.mark.gpu
 
@@ -70,10 +73,24 @@ def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
               shared_blocks=True)
 
 
-def test_large_group_batch_above_one_launch():
-    w = wl.make_workload("groups-wide", 470, 8, 1, 64, len_range=(1, 40), num_seqs=4100)
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (12, 1)])
+def test_large_group_batch_above_one_launch(Hq, Hkv):
+    """G = 8: 2 copies, 2048 sequences per launch; G = 12: 3 copies, 1365."""
+    w = wl.make_workload("groups-wide", 470 + Hq, Hq, Hkv, 64, len_range=(1, 40), num_seqs=4100)
     d = to_device(w)
     out = gpu_step(w, d, 0)
     kc, vc = oracle_pools(w)
-    seqs = np.r_[0:40, 4050:4100]
-    compare(out[seqs], oracle_decode(w, kc, vc, seqs), "G8 4100 sequences")
+    seqs = np.unique(np.r_[0:40, 1350:1380, 2030:2070, 2720:2740, 4050:4100])  # launch edges
+    compare(out[seqs], oracle_decode(w, kc, vc, seqs), f"G{Hq // Hkv} 4100 sequences")
+
+
+def test_large_group_fused_batch_above_one_launch():
+    """The fused append across launches at G = 8: each launch's new rows,
+    slots and outputs start at its first sequence; pools bit for bit."""
+    w = wl.make_workload("groups-wide-fused", 480, 8, 1, 64, len_range=(1, 40), num_seqs=4100)
+    d = to_device(w)
+    out = fused_step(w, d, 0)
+    kc, vc = oracle_pools(w)
+    assert_pools_equal(d, kc, vc, "G8 fused 4100")
+    seqs = np.unique(np.r_[0:40, 2030:2070, 4050:4100])
+    compare(out[seqs], oracle_decode(w, kc, vc, seqs), "G8 fused 4100 sequences")
