@@ -81,8 +81,8 @@ __global__ __launch_bounds__(64 * kPrefixWaves, 1) void prefix_kernel(const Pref
   const int c16 = lane & 15;  // operand / result column: this lane's row of a sub-tile
   const int j = lane >> 4;    // k-slot group
   const int S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  // (virtual heads as in the decode: a KV head of more than 4 query heads
-  // is kv_split heads of up to 4, Hkv counts them)
+  // (a KV head of more than 4 query heads is taken as kv_split heads, one
+  // per sub-group of up to 4 query heads; Hkv counts them)
   const int split = a.kv_split, Hkr = Hkv / split;
   // workgroup -> (chunk, window, KV head), the chunk slowest: chunks that
   // turn out empty (past a group's prefix) are dispatched last

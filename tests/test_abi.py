@@ -77,7 +77,7 @@ def test_decode_argument_errors(L):
     assert dec(L, hq=30) == E.PA_ERR_INVALID_ARG            # Hq % Hkv != 0
     assert dec(L, D=96) == E.PA_ERR_UNSUPPORTED
     assert dec(L, bs=24) == E.PA_ERR_UNSUPPORTED             # block size not 8, 16 or 32
-    # G = 8 and G = 7 (virtual heads): past the argument checks, to the missing workspace
+    # G = 8 and G = 7 (sub-groups): past the argument checks, to the missing workspace
     assert dec(L, hq=64) == E.PA_ERR_WORKSPACE
     assert dec(L, hq=56) == E.PA_ERR_WORKSPACE
     assert dec(L, maxctx=129) == E.PA_ERR_INVALID_ARG        # > 8 blocks * 16

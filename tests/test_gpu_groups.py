@@ -40,8 +40,8 @@ def test_decode_large_groups(Hq, Hkv, D, workers):
 @pytest.mark.parametrize("Hq,Hkv,D", GROUPS)
 @pytest.mark.parametrize("workers", [0, 5000])
 def test_fused_large_groups(Hq, Hkv, D, workers):
-    """The new rows are stored once per KV head (by its first virtual head)
-    and enter every virtual head's attention."""
+    """The new rows are stored once (by the first sub-group's copy of the
+    batch) and enter every sub-group's attention."""
     w = wl.make_workload("groups-fused", 420 + Hq + Hkv + D, Hq, Hkv, D, context_lens=FUSED_LENS)
     run_fused(w, workers, f"fused G{Hq // Hkv} Hq{Hq} Hkv{Hkv} D{D} workers{workers}")
 
@@ -55,8 +55,8 @@ def test_large_group_block_sizes(BS):
 
 @pytest.mark.parametrize("workers", [64, 512])
 def test_large_group_long_runs_cut(workers):
-    """Two long runs per KV head, cut into a piece per worker: every virtual
-    head's pieces merge on their own."""
+    """Two long runs per KV head, cut into a piece per worker: every
+    sub-group's pieces merge on their own."""
     w = wl.make_workload("groups-long", 450 + workers, 8, 1, 128, context_lens=[9000, 70, 4097])
     run_fused(w, workers, f"fused G8 long runs over {workers} workers")
 
@@ -64,7 +64,7 @@ def test_large_group_long_runs_cut(workers):
 @pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64)])
 @pytest.mark.parametrize("workers", [0, 5000])
 def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
-    """The prefix pass attends each virtual head's rows of a group's members
+    """The prefix pass attends each sub-group's rows of a group's members
     (up to 8 x 4) to the common prefix; a prefix of two chunks."""
     w = wl.make_workload("groups-prefix", 460 + Hq + D, Hq, Hkv, D, num_seqs=18, prefix_groups=3,
                          prefix_len=1536, suffix_range=(1, 300))
