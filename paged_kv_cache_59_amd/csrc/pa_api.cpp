@@ -409,7 +409,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_INVALID_ARG;
   const int64_t G = num_q_heads / num_kv_heads;
-  const int64_t tile_groups = ceil_div((int64_t)max_query_len * G, 4 * pa::kPrefillWaveRows);
+  const int64_t tile_groups =
+      ceil_div((int64_t)max_query_len * G, pa::kPrefillWaves * pa::kPrefillWaveRows);
   if (((int64_t)num_seqs * num_kv_heads + 7) / 8 * 8 * tile_groups > 0x7fffffff)
     return PA_ERR_UNSUPPORTED;
   pa::PrefillArgs a{};

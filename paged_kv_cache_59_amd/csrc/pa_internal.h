@@ -169,9 +169,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t sta
                          hipEvent_t stop);
 
 // Multi-query paged attention (chunked prefill).  One wave per tile of
-// kPrefillWaveRows rows of one (sequence, KV head); a workgroup holds 4 such
-// tiles, and tile_groups workgroups cover the longest chunk:
-// ceil(max_query_len * G / (4 kPrefillWaveRows)).
+// kPrefillWaveRows rows of one (sequence, KV head); a workgroup holds
+// kPrefillWaves such tiles, and tile_groups workgroups cover the longest
+// chunk: ceil(max_query_len * G / (kPrefillWaves kPrefillWaveRows)).
 struct PrefillArgs {
   half_t* out;
   const half_t* q;
@@ -194,6 +194,7 @@ struct PrefillArgs {
 // 32-key K/V steps a prefill workgroup keeps in its LDS ring (64 KiB at D = 128)
 constexpr int kPrefillStages = 4;
 constexpr int kPrefillWaveRows = 32;  // query rows of one wave
+constexpr int kPrefillWaves = 4;      // waves of one workgroup
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int64_t kTile = (int64_t)BS * D;
   constexpr int NBS = 32 / BS;           // blocks per 32-key step (4, 2 or 1)
   static_assert(NBS * BS == 32, "block size 8, 16 or 32");
+  static_assert(kPrefillWaves == 4 && kPrefillWaveRows == 32, "4 waves of 32 rows");
   constexpr float kStale = 8.0f;         // see the rescale below
   constexpr float kFloor = -1.0e30f;     // initial reference max (log2 units)
   constexpr int kTileBytes = 32 * D * 2;        // K (or V) of one 32-key step
