@@ -282,7 +282,8 @@ int pa_decode_timed(void* out, const void* q, const void* k_cache, const void* v
  *                  prefix P is the multiple of 64 tokens every member holds
  *                  in those blocks short of its last position (the new
  *                  token's).  The pass attends all the group's query rows
- *                  (members x query heads of a KV head, at most 32) to
+ *                  (members x up to 4 query heads of a KV head, at most
+ *                  32; larger groups of query heads in sub-groups) to
  *                  those P positions once, and the decode covers each
  *                  member's positions from P on, starting its online
  *                  softmax from that result.  Results equal the flagless
