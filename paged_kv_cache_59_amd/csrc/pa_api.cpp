@@ -165,7 +165,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (w <= 0) return 0;
   const int32_t split = kv_split(num_q_heads, num_kv_heads);
   return pa::decode_workspace_bytes(seqs_per_launch(num_seqs, split) * split, num_kv_heads,
-                                    head_dim, w);
+                                    head_dim, pa::decode_pairs(split) ? 2 * w : w);
 }
 
 }  // extern "C"
@@ -210,8 +210,10 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     return PA_ERR_UNSUPPORTED;
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
+  // (paired sub-groups: two share slots per worker)
+  const int32_t slot_workers = pa::decode_pairs(split) ? 2 * w : w;
   const size_t need =
-      pa::decode_workspace_bytes(vseqs, num_kv_heads, head_dim, w);
+      pa::decode_workspace_bytes(vseqs, num_kv_heads, head_dim, slot_workers);
   if (static_scratch) {
     // the library's own device array stands in for the workspace
     if (need > pa::kStaticScratchBytes ||
@@ -224,7 +226,8 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
-  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, vseqs, num_kv_heads, head_dim, w);
+  a.ws = pa::decode_workspace_carve(workspace, workspace_bytes, vseqs, num_kv_heads, head_dim,
+                                    slot_workers);
   a.k_cache = static_cast<const pa::half_t*>(k_cache);
   a.v_cache = static_cast<const pa::half_t*>(v_cache);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e) = 1 / ln 2

@@ -195,7 +195,12 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 // pass per group over its common blocks, results in out and pre_lse); each
 // run covers its sequence's positions from a.pre_len[s] on, and its result
 // is folded together with the prefix pass's.
-template <int D, int BS, bool Fused, bool Shared>
+// Pair (kv_split == 2, 5..8 query heads per KV head): one pass over each
+// unit attends both sub-groups (8 query rows on two sets of MFMAs over the
+// same K and V registers); the units enumerate the batch once, and each
+// piece is handed to the merger twice, as the pieces of the two copies
+// (sequences s and Sr + s) would be.
+template <int D, int BS, bool Fused, bool Shared, bool Pair>
 __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
@@ -215,8 +220,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // (unpadded, rows 128 and 256 bytes apart share banks: 4-way conflicts).
   constexpr int kQRow = D + 8;  // halves per q row
   constexpr int kPRow = 64 + 16;  // halves per softmax-weight row
-  __shared__ __attribute__((aligned(16))) half_t p_lds[4 * kPRow];
-  __shared__ __attribute__((aligned(16))) half_t q_lds[4 * kQRow];
+  constexpr int kRows = Pair ? 8 : 4;  // query rows a unit is attended for
+  static_assert(!(Pair && kValu), "the vector-ALU measurement build attends 4 rows");
+  __shared__ __attribute__((aligned(16))) half_t p_lds[kRows * kPRow];
+  __shared__ __attribute__((aligned(16))) half_t q_lds[kRows * kQRow];
   // streamer -> merger: cut pieces, a ring of kRing entries
   __shared__ float ring_o[kRing][4 * D];
   __shared__ float ring_ml[kRing][8];
@@ -242,7 +249,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     kw = min(per_xcd & -per_xcd, 32);
   }
   const int w = (nw % 8 == 0) ? ((bx / 8) / kw) * 8 * kw + (bx % 8) * kw + (bx / 8) % kw : bx;
-  const int S = a.num_seqs;
+  const int Sv = a.num_seqs;          // virtual sequences (slots, counters)
+  const int S = Pair ? Sv / 2 : Sv;   // sequences in unit order (the unit tables)
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   // Sub-groups: a KV head with more than 4 query heads is attended in
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // per copy of the batch: S counts the virtual sequences, sub-group
   // s / Sr of sequence s % Sr.
   const int split = a.kv_split;
-  const int Sr = S / split;  // sequences of the batch (lengths, tables, new rows)
+  const int Sr = Sv / split;  // sequences of the batch (lengths, tables, new rows)
   const int G = Hq / Hkv;    // query heads per KV head
   auto sub_of = [&](int s) { return split == 1 ? 0 : s / Sr; };
   auto real_of = [&](int s) { return split == 1 ? s : s - s / Sr * Sr; };
@@ -259,6 +267,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   auto q_row0 = [&](int s, int h) -> int64_t {
     return (int64_t)real_of(s) * Hq + h * G + sub_of(s) * 4;
   };
+  // a virtual sequence's entry in the unit tables
+  auto tab = [&](int s) { return Pair ? real_of(s) : s; };
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
   int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   if (my_first >= my_end) return;
   // Partial slots: [0, R) the piece that starts run r, R + j the piece that
   // starts share j inside a run.
-  const int R = S * Hkv;
+  const int R = Sv * Hkv;  // (Pair: slots R + w and R + nw + w for a share's first piece)
 
   // ---- cursors over units --------------------------------------------------
   struct Cursor {
@@ -524,7 +534,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
   half8_t kreg[kChunks];
   half8_t vreg[8][kSets];  // 8-token group g of the unit, 64-dim range st
-  half8_t qreg;  // lane g*kChunks + c: 16-byte chunk c of q row g of a run
+  // q rows of a run: load i, lane r*kChunks + c: 16-byte chunk c of row
+  // i * 64 / kChunks + r
+  constexpr int kSub = Pair ? 2 : 1;  // sub-groups of 4 rows a pass attends
+  constexpr int kQLoads = (kRows * kChunks + 63) / 64;
+  half8_t qreg[kQLoads];
   // K of unit c: lane l's token lies in the unit's block l / BS, whose table
   // entry lane l / BS of the table load tbl holds (a cross-lane read, not a
   // register-indexed select, which the compiler would turn into scratch)
@@ -563,13 +577,24 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // q rows of c's run; every lane loads (rows past the head's and lanes past
   // the rows re-read row 0 and are zeroed at the LDS write) so the load is
   // unconditional
+  // (Pair: rows 0..7 of the 8 are query heads h G + 0..7 of the sequence,
+  // rows past G zero; one load covers 64 / kChunks rows)
   const int q_row = lane / kChunks, q_chunk = lane % kChunks;
-  int q_nr = 0;  // rows of the q load last issued
+  bool q_ok[kQLoads];  // this lane's row of each load holds a query head
   auto load_q = [&](const Cursor& c) {
-    q_nr = q_rows(c.s);
-    const int row = q_row < q_nr ? q_row : 0;
-    qreg = *reinterpret_cast<const half8_t*>(a.q + (q_row0(c.s, c.h) + row) * D +
-                                             q_chunk * kChunk);
+#pragma unroll
+    for (int i = 0; i < kQLoads; ++i) {
+      const int r = i * (64 / kChunks) + q_row;
+      int64_t row;
+      if constexpr (Pair) {
+        q_ok[i] = r < G;
+        row = (int64_t)c.s * Hq + c.h * G + (q_ok[i] ? r : 0);
+      } else {
+        q_ok[i] = r < q_rows(c.s);
+        row = q_row0(c.s, c.h) + (q_ok[i] ? r : 0);
+      }
+      qreg[i] = *reinterpret_cast<const half8_t*>(a.q + row * D + q_chunk * kChunk);
+    }
   };
   // Shared: the prefix pass's first chunk for a run, loaded for a unit that
   // starts the run one iteration ahead, ahead of that unit's K (rows: dims
@@ -578,25 +603,33 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // instead of from nothing: the run's online softmax then takes the prefix
   // in with no fold afterwards.  (Further chunks, of prefixes above one
   // chunk, are folded by the merger.)
-  half_t pre_o[4][kSets];
-  float pre_m = 0.0f;
+  half_t pre_o[kSub][4][kSets];
+  float pre_m[kSub];
   auto load_pre = [&](const Cursor& c) {
     if constexpr (Shared) {
-      const int64_t row0 = q_row0(c.s, c.h);
-      const int nr = q_rows(c.s);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int u = 0; u < kSub; ++u) {
+        const int sv = u ? Sr + c.s : c.s;  // (Pair: the second sub-group's copy)
+        const int64_t row0 = q_row0(sv, c.h);
+        const int nr = q_rows(sv);
 #pragma unroll
-        for (int st = 0; st < kSets; ++st)
-          pre_o[g][st] = g < nr ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
-      pre_m = a.pre_lse[row0 + min(lane, nr - 1)];
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int st = 0; st < kSets; ++st)
+            pre_o[u][g][st] = g < nr ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
+        pre_m[u] = a.pre_lse[row0 + min(lane, nr - 1)];
+      }
     }
   };
   auto starts_with_pre = [&](const Cursor& c) { return Shared && c.valid && c.g == 0 && c.base > 0; };
   auto store_q = [&]() {
-    if (q_row < 4) {
-      const half8_t v = q_row < q_nr ? qreg : half8_t{};
-      *reinterpret_cast<half8_t*>(q_lds + q_row * kQRow + q_chunk * kChunk) = v;
+#pragma unroll
+    for (int i = 0; i < kQLoads; ++i) {
+      const int r = i * (64 / kChunks) + q_row;
+      if (r < kRows) {
+        const half8_t v = q_ok[i] ? qreg[i] : half8_t{};
+        *reinterpret_cast<half8_t*>(q_lds + r * kQRow + q_chunk * kChunk) = v;
+      }
     }
   };
   // Fused append: the new token of sequence s sits at position len - 1, in
@@ -734,9 +767,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     m.lsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kF; ++j) m.acc[j] = 0.0f;
-    const int n = uniform(run_units(s));
-    const int u0 = Hkv * uniform(off_lds[s]) + kvh * n;
+    const int ts = tab(s);
+    const int n = uniform(run_units(ts));
+    const int u0 = Hkv * uniform(off_lds[ts]) + kvh * n;
     const int r = s * Hkv + kvh;
+    // the slot of a piece that starts share v inside the run (Pair: the
+    // second sub-group's pieces have slots of their own)
+    const int r_share = Pair && sub_of(s) ? R + nw : R;
     const int nr = q_rows(s);
     const int64_t q0 = q_row0(s, kvh) - (int64_t)real_of(s) * Hq;  // (its first query head)
     // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
@@ -748,7 +785,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     hvec_t o_c[NC];
     int nch = 0;
     if constexpr (Shared) {
-      nch = prefix_chunks(uniform(base_lds[s]));
+      nch = prefix_chunks(uniform(base_lds[ts]));
       const bool valid = gq < nr;
 #pragma unroll
       for (int c = 1; c < NC; ++c) {
@@ -764,7 +801,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // piece p0 + pq (pieces past the batch repeat its last)
       const int p = p0 + min(pq, nb - 1);
       const int v = va + p;
-      const int sl = v == va ? r : R + v;
+      const int sl = v == va ? r : r_share + v;
       if (nb <= 2)
         absorb(std::integral_constant<int, 2>{}, m, sl, nb, own_slot, own_k, nr);
       else if (nb <= 4)
@@ -805,29 +842,35 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   };
 
   // per-piece softmax state
-  float m_run[4], l_lane[4];
-  float4_t acc_o[kSets];
+  // (one set per sub-group the pass attends)
+  float m_run[kSub][4], l_lane[kSub][4];
+  float4_t acc_o[kSub][kSets];
   auto reset_run = [&]() {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      m_run[g] = -INFINITY;
-      l_lane[g] = 0.0f;
-    }
+    for (int u = 0; u < kSub; ++u) {
 #pragma unroll
-    for (int st = 0; st < kSets; ++st) acc_o[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  };
-  // a piece that starts a run (of nr query rows) with a prefix: begin from
-  // its first chunk
-  auto seed_pre = [&](int nr) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < nr) {
-        m_run[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre_m), g));
-        l_lane[g] = lane == 0 ? 1.0f : 0.0f;
-#pragma unroll
-        for (int st = 0; st < kSets; ++st) acc_o[st][g] = (float)pre_o[g][st];
+      for (int g = 0; g < 4; ++g) {
+        m_run[u][g] = -INFINITY;
+        l_lane[u][g] = 0.0f;
       }
+#pragma unroll
+      for (int st = 0; st < kSets; ++st) acc_o[u][st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  };
+  // a piece that starts a run with a prefix: begin from its first chunk
+  // (nr[u]: query rows of sub-group u)
+  auto seed_pre = [&](const int (&nr)[kSub]) {
+#pragma unroll
+    for (int u = 0; u < kSub; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g < nr[u]) {
+          m_run[u][g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre_m[u]), g));
+          l_lane[u][g] = lane == 0 ? 1.0f : 0.0f;
+#pragma unroll
+          for (int st = 0; st < kSets; ++st) acc_o[u][st][g] = (float)pre_o[u][g][st];
+        }
+      }
   };
 
   // ---- the merger wave --------------------------------------------------------
@@ -912,7 +955,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // unit of the run already counted): merged straight from the ring,
       // neither written through nor counted.  Their ring entries are released
       // after the merge, the others' at once.
-      const bool last_known = counted && seen + ui == run_units(ci / Hkv);
+      const bool last_known = counted && seen + ui == run_units(tab(ci / Hkv));
       const uint64_t fast = __ballot(last_known);  // bit i: piece i
       const int cons0 = cons;
       cons += avail;
@@ -923,7 +966,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           // a whole run: its output rows (Shared: with the prefix pass's
           // chunks 1.. folded in, each a piece of weight 1 at its log-sum-exp)
           const int s_i = ps[i];
-          const int nch = Shared ? prefix_chunks(uniform(base_lds[s_i])) : 0;
+          const int nch = Shared ? prefix_chunks(uniform(base_lds[tab(s_i)])) : 0;
           if (Shared && nch > 1) load_pieces(s_i, ph[i], nch);
           const int nr = q_rows(s_i);
           const int64_t row_0 = q_row0(s_i, ph[i]);
@@ -985,7 +1028,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int i = 0; i < kRing; ++i) {
         if (i < avail && pslot[i] >= 0) {
           const bool fi = (fast >> i) & 1;
-          const int n = uniform(run_units(ps[i]));
+          const int n = uniform(run_units(tab(ps[i])));
           if (fi || __builtin_amdgcn_readlane(arr, i) + pu[i] == n) {
             merge_out(ps[i], ph[i],
                       merge_pieces(ps[i], ph[i], fi ? (int)pslot[i] : -1, (cons0 + i) % kRing));
@@ -1053,25 +1096,43 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   store_q();
   __builtin_amdgcn_wave_barrier();
   reset_run();
-  if (starts_with_pre(cur)) seed_pre(q_rows(cur.s));
+  // query rows of each sub-group a pass over (cur.s, .) attends
+  auto rows_of = [&](int s, int (&nr)[kSub]) {
+    if constexpr (Pair) {
+      nr[0] = min(4, G);
+      nr[1] = G - 4;
+    } else {
+      nr[0] = q_rows(s);
+    }
+  };
+  {
+    int nr0[kSub];
+    rows_of(cur.s, nr0);
+    if (starts_with_pre(cur)) seed_pre(nr0);
+  }
   uint64_t t_iter = stamp_now();
   int piece_g0 = cur.g;  // unit of the run where the piece began
   bool q_pending = false;  // a new piece starts: its q rows go to LDS first
 
   while (cur.valid) {
     const int t0 = cur.base + cur.g * kGroupTokens;  // position of the unit's first token
-    const int nr = q_rows(cur.s);                    // query rows of the run
+    int nrs[kSub];  // query rows of each sub-group of the run
+    rows_of(cur.s, nrs);
+    const int nr = nrs[0];
     // q rows of a piece that starts here.  Their load was issued one
     // iteration ago, before this unit's K: waiting for it here costs nothing,
     // as the logits wait for that K anyway.
     if (q_pending) {
       store_q();
-      if (starts_with_pre(cur)) seed_pre(nr);
+      if (starts_with_pre(cur)) seed_pre(nrs);
     }
     q_pending = false;
 
     // logits: S[g][token lane] = q_g . K_token  (rows = heads, columns = tokens)
-    float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t sacc_u[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) sacc_u[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t& sacc = sacc_u[0];
     if constexpr (kValu) {
       // (measurement build) lane = token: its K row against each head's q
       // row, read from LDS by every lane at once, in pairs of dims
@@ -1093,9 +1154,13 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     } else {
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
-        const half8_t qv = *reinterpret_cast<const half8_t*>(q_lds + g_lane * kQRow + c * kChunk);
-        sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {  // (Pair: the second sub-group's rows 4..7)
+          const half8_t qv =
+              *reinterpret_cast<const half8_t*>(q_lds + (4 * u + g_lane) * kQRow + c * kChunk);
+          sacc_u[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc_u[u], 0, 0, 0);
+          sacc_u[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(hi4(qv), hi4(kreg[c]), sacc_u[u], 0, 0, 0);
+        }
       }
     }
     // keep the next unit's address work below the logits: hoisted above
@@ -1118,20 +1183,22 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // (every unit holds at least one position: its first, t0 < len)
     const bool live = (t0 + lane) < cur.len;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      half_t ph = (half_t)0.0f;
-      if (g < nr) {
-        const float z = live ? sacc[g] * a.scale_log2 : -INFINITY;
-        const float m_new = fmaxf(m_run[g], wave_max(z));
-        const float alpha = fast_exp2(m_run[g] - m_new);  // 0 at the piece's first unit
-        ph = (half_t)fast_exp2(z - m_new);
-        l_lane[g] = l_lane[g] * alpha + (float)ph;
+    for (int u = 0; u < kSub; ++u)
 #pragma unroll
-        for (int st = 0; st < kSets; ++st) acc_o[st][g] *= alpha;
-        m_run[g] = m_new;
+      for (int g = 0; g < 4; ++g) {
+        half_t ph = (half_t)0.0f;
+        if (g < nrs[u]) {
+          const float z = live ? sacc_u[u][g] * a.scale_log2 : -INFINITY;
+          const float m_new = fmaxf(m_run[u][g], wave_max(z));
+          const float alpha = fast_exp2(m_run[u][g] - m_new);  // 0 at the piece's first unit
+          ph = (half_t)fast_exp2(z - m_new);
+          l_lane[u][g] = l_lane[u][g] * alpha + (float)ph;
+#pragma unroll
+          for (int st = 0; st < kSets; ++st) acc_o[u][st][g] *= alpha;
+          m_run[u][g] = m_new;
+        }
+        p_lds[(4 * u + g) * kPRow + lane] = ph;
       }
-      p_lds[g * kPRow + lane] = ph;
-    }
 
     if constexpr (kTrace) {
       if (tr[kTrUnits]++ == 0) tr[kTrFirstUnit] = stamp_now();
@@ -1180,25 +1247,30 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
             for (int st = 0; st < kSets; ++st)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                acc_o[st][g] = __builtin_amdgcn_fdot2(
+                acc_o[0][st][g] = __builtin_amdgcn_fdot2(
                     half2x{pv[2 * i], pv[2 * i + 1]},
-                    half2x{vreg[grp][st][2 * i], vreg[grp][st][2 * i + 1]}, acc_o[st][g], false);
+                    half2x{vreg[grp][st][2 * i], vreg[grp][st][2 * i + 1]}, acc_o[0][st][g], false);
           }
         }
       }
     } else {
       // lane 4c+g: weights of head g for tokens 4c..4c+3
-      const half4_t pfrag =
-          *reinterpret_cast<const half4_t*>(p_lds + (lane & 3) * kPRow + (lane >> 2) * 4);
+      half4_t pfrag[kSub];
+#pragma unroll
+      for (int u = 0; u < kSub; ++u)
+        pfrag[u] = *reinterpret_cast<const half4_t*>(p_lds + (4 * u + (lane & 3)) * kPRow +
+                                                     (lane >> 2) * 4);
 
       // out[g][d] += sum_t P[g][t] V[t][d]; chunk c = tokens 4c..4c+3 of the unit
       static_for<0, 16>([&](auto ic) {
         constexpr int c = decltype(ic)::value;
-        constexpr int g = c / 2, sub = c % 2;  // 8-token group, its half
+        constexpr int g = c / 2, half = c % 2;  // 8-token group, its half
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
-          const half4_t vf = sub ? hi4(vreg[g][st]) : lo4(vreg[g][st]);
-          acc_o[st] = __builtin_amdgcn_mfma_f32_4x4x4f16(pfrag, vf, acc_o[st], 4, c, 0);
+          const half4_t vf = half ? hi4(vreg[g][st]) : lo4(vreg[g][st]);
+#pragma unroll
+          for (int u = 0; u < kSub; ++u)
+            acc_o[u][st] = __builtin_amdgcn_mfma_f32_4x4x4f16(pfrag[u], vf, acc_o[u][st], 4, c, 0);
         }
       });
     }
@@ -1208,9 +1280,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // ---- end of a piece: the run or the share ends ------------------------
     const bool run_end = cur.g + 1 == cur.n_s;
     if (run_end || !nxt.valid) {
-      float l_tot[4];
+      float l_tot[kSub][4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) l_tot[g] = (g < nr) ? wave_sum(l_lane[g]) : 1.0f;
+      for (int u = 0; u < kSub; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) l_tot[u][g] = (g < nrs[u]) ? wave_sum(l_lane[u][g]) : 1.0f;
       // The piece goes to the merger through the LDS ring (wait while the
       // ring is full, which the merger rarely lets happen): a whole run
       // (slot -1), which the merger normalises and stores, or a cut piece: a
@@ -1219,9 +1293,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // stores nothing inside the loop: a wave's memory operations complete
       // in order, so a store here would hold back the K/V loads issued after
       // it, a memory latency at every run end.
-      const int slot = (piece_g0 == 0 && run_end) ? -1 : piece_g0 == 0 ? cur.s * Hkv + cur.h : R + w;
+      // (Pair: one entry per sub-group, as the pieces of the two copies of
+      // the batch: sequence Sr + s and share slot R + nw + w for the second)
       const uint64_t t_ring = stamp_now();
-      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) >= kRing; ++spin) {
+      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) > kRing - kSub; ++spin) {
         if (spin >= a.spin_limit) {  // give up (reported in the status word)
           if (lane == 0)
             __hip_atomic_store(a.ws.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1230,25 +1305,39 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         __builtin_amdgcn_s_sleep(1);
       }
       if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
-      const int k = ring_made % kRing;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int u = 0; u < kSub; ++u) {
+        const int sv = u ? Sr + cur.s : cur.s;
+        const int slot = (piece_g0 == 0 && run_end) ? -1
+                         : piece_g0 == 0            ? sv * Hkv + cur.h
+                                                    : R + u * nw + w;
+        const int k = (ring_made + u) % kRing;
 #pragma unroll
-        for (int st = 0; st < kSets; ++st)
-          ring_o[k][g * D + st * 64 + lane] = acc_o[st][g];
-      if (lane < 8) {  // (max, sum) of head lane/2
-        const int gi = lane >> 1;
-        const float mv = gi == 0 ? m_run[0] : gi == 1 ? m_run[1] : gi == 2 ? m_run[2] : m_run[3];
-        const float lv = gi == 0 ? l_tot[0] : gi == 1 ? l_tot[1] : gi == 2 ? l_tot[2] : l_tot[3];
-        ring_ml[k][lane] = (lane & 1) ? lv : mv;
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int st = 0; st < kSets; ++st)
+            ring_o[k][g * D + st * 64 + lane] = acc_o[u][st][g];
+        if (lane < 8) {  // (max, sum) of head lane/2
+          const int gi = lane >> 1;
+          const float mv = gi == 0   ? m_run[u][0]
+                           : gi == 1 ? m_run[u][1]
+                           : gi == 2 ? m_run[u][2]
+                                     : m_run[u][3];
+          const float lv = gi == 0   ? l_tot[u][0]
+                           : gi == 1 ? l_tot[u][1]
+                           : gi == 2 ? l_tot[u][2]
+                                     : l_tot[u][3];
+          ring_ml[k][lane] = (lane & 1) ? lv : mv;
+        }
+        if (lane == 0) {
+          ring_meta[k][0] = sv;
+          ring_meta[k][1] = cur.h;
+          ring_meta[k][2] = slot;
+          ring_meta[k][3] = cur.g - piece_g0 + 1;
+        }
       }
-      if (lane == 0) {
-        ring_meta[k][0] = cur.s;
-        ring_meta[k][1] = cur.h;
-        ring_meta[k][2] = slot;
-        ring_meta[k][3] = cur.g - piece_g0 + 1;
-      }
-      lds_st(&ctl[kCtlRingMade], ++ring_made);
+      ring_made += kSub;
+      lds_st(&ctl[kCtlRingMade], ring_made);
       if constexpr (kTrace) ++tr[kTrPieces];
       reset_run();
       q_pending = true;
@@ -1388,25 +1477,36 @@ DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int6
   return w;
 }
 
-template <int D, int BS, bool Fused, bool Shared>
+template <int D, int BS, bool Fused, bool Shared, bool Pair>
 void launch_decode_f(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
   const uint32_t lds = (uint32_t)((size_t)a.num_seqs * (Shared ? 3 : 2) * sizeof(int));
   if (!start && !stop)
-    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared>), grid, dim3(128), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Pair>), grid, dim3(128), lds, stream, a);
   else  // the events take the kernel's own start and end times
-    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared>), grid, dim3(128), lds, stream,
-                          start, stop, 0, a);
+    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Pair>), grid, dim3(128), lds,
+                          stream, start, stop, 0, a);
+}
+
+template <int D, int BS, bool Pair>
+void launch_decode_p(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (a.k_new && a.pre_len)
+    launch_decode_f<D, BS, true, true, Pair>(a, stream, start, stop);
+  else if (a.k_new)
+    launch_decode_f<D, BS, true, false, Pair>(a, stream, start, stop);
+  else
+    launch_decode_f<D, BS, false, false, Pair>(a, stream, start, stop);
 }
 
 template <int D, int BS>
 void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (a.k_new && a.pre_len)
-    launch_decode_f<D, BS, true, true>(a, stream, start, stop);
-  else if (a.k_new)
-    launch_decode_f<D, BS, true, false>(a, stream, start, stop);
-  else
-    launch_decode_f<D, BS, false, false>(a, stream, start, stop);
+  if constexpr (!kValu) {
+    if (decode_pairs(a.kv_split)) {
+      launch_decode_p<D, BS, true>(a, stream, start, stop);
+      return;
+    }
+  }
+  launch_decode_p<D, BS, false>(a, stream, start, stop);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,

@@ -118,13 +118,20 @@ def test_workspace_sizes(L):
     assert L.pa_decode_workspace_size(4, 32, 8, 128, 100, -2) == 0
     assert L.pa_decode_workspace_size(4, 30, 8, 128, 100, 16) == 0   # Hq % Hkv != 0
     # a KV head of G = 8 or 7 query heads: 2 sub-groups of up to 4 rows, one
-    # copy of the batch each (128 virtual sequences x 8 KV heads)
+    # copy of the batch each (128 virtual sequences x 8 KV heads), attended
+    # in one pass: two share slots per worker
     for hq in (64, 56):
-        v = 128 * 8 + 2048
+        v = 128 * 8 + 2 * 2048
         pre = 4 * 128 * 8 * 4
         assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
             v * 8 * 4 + v * 4 * 128 * 4 + a256(128 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
             + 128 * 8 * 4 + 256)
+    # G = 12: 3 sub-groups, three copies of the batch, one share slot per worker
+    v = 3 * 64 * 8 + 2048
+    pre = 4 * 3 * 64 * 8 * 4
+    assert L.pa_decode_workspace_size(64, 96, 8, 128, 2048, 2048) == (
+        v * 8 * 4 + v * 4 * 128 * 4 + a256(3 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
+        + 3 * 64 * 8 * 4 + 256)
 
 
 def test_cache_op_argument_errors(L):
