@@ -171,7 +171,7 @@ int32_t pa_decode_num_workers(void);
  * results of sequences cut between workers (one per (sequence, KV head)
  * run and one per worker, 4 query-head rows each; with G > 4 query heads
  * per KV head each sequence counts ceil(G / 4) times here and below, and
- * for 5 <= G <= 8 each worker twice), then
+ * with an even number of sub-groups each worker twice), then
  * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
  * its prefix length, per (chunk, sequence, query head) up to 4 normalised
  * fp16 rows and their log-sum-exps) and, against its end, one arrival
@@ -232,8 +232,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * the value product rounded to fp16); out is rounded to nearest even fp16.
  * Any G >= 1: the grouped query heads of a KV head (up to 4 at a time, the
  * rows of the decode's matrix instruction) share each K and V load; a group
- * of 5 <= G <= 8 is attended as two such sub-groups in one pass over K and
- * V, a larger group in ceil(G / 4) sub-groups, each a copy of the batch in
+ * of G > 4 is attended in ceil(G / 4) sub-groups, two per pass over K and V
+ * when their number is even (else one), each pass a copy of the batch in
  * the same launch, whose reads of one block fall at the same time (the L2
  * serves part of the repeats).
  * num_seqs == 0 is a no-op.

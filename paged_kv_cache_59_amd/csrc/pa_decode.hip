@@ -195,11 +195,12 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 // pass per group over its common blocks, results in out and pre_lse); each
 // run covers its sequence's positions from a.pre_len[s] on, and its result
 // is folded together with the prefix pass's.
-// Pair (kv_split == 2, 5..8 query heads per KV head): one pass over each
-// unit attends both sub-groups (8 query rows on two sets of MFMAs over the
-// same K and V registers); the units enumerate the batch once, and each
-// piece is handed to the merger twice, as the pieces of the two copies
-// (sequences s and Sr + s) would be.
+// Pair (an even kv_split: 5..8, 13..16, .. query heads per KV head): one
+// pass over a unit attends two sub-groups (8 query rows on two sets of
+// MFMAs over the same K and V registers); the units enumerate kv_split / 2
+// copies of the batch, copy c for sub-groups 2c and 2c + 1, and each piece
+// is handed to the merger twice, as the pieces of those sub-groups' copies
+// (virtual sequences 2c Sr + s and (2c + 1) Sr + s) would be.
 template <int D, int BS, bool Fused, bool Shared, bool Pair>
 __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
@@ -268,7 +269,17 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     return (int64_t)real_of(s) * Hq + h * G + sub_of(s) * 4;
   };
   // a virtual sequence's entry in the unit tables
-  auto tab = [&](int s) { return Pair ? real_of(s) : s; };
+  auto tab = [&](int s) { return Pair ? sub_of(s) / 2 * Sr + real_of(s) : s; };
+  // Pair: the first of the two sub-groups a table entry's pass attends (one
+  // pair, kv_split == 2: the table holds the batch once, no division), the
+  // sequence of the batch at table entry t, and the virtual sequence of the
+  // pass's sub-group u
+  auto pair_sub0 = [&](int t) { return split == 2 ? 0 : 2 * (t / Sr); };
+  auto seq_of = [&](int t) {
+    if constexpr (Pair) return split == 2 ? t : t - t / Sr * Sr;
+    else return real_of(t);
+  };
+  auto pair_seq = [&](int t, int u) { return (pair_sub0(t) + u) * Sr + seq_of(t); };
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
   int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
@@ -289,8 +300,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int b = 0; b < kLenBatch; ++b) {
       const int s = cb + 64 * b + lane;
-      len_in[b] = s < S ? a.context_lens[real_of(s)] : 0;
-      pre_in[b] = (Shared && s < S) ? a.pre_len[real_of(s)] : 0;
+      len_in[b] = s < S ? a.context_lens[seq_of(s)] : 0;
+      pre_in[b] = (Shared && s < S) ? a.pre_len[seq_of(s)] : 0;
     }
 #pragma unroll
     for (int b = 0; b < kLenBatch; ++b) {
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   if (my_first >= my_end) return;
   // Partial slots: [0, R) the piece that starts run r, R + j the piece that
   // starts share j inside a run.
-  const int R = Sv * Hkv;  // (Pair: slots R + w and R + nw + w for a share's first piece)
+  const int R = Sv * Hkv;  // (Pair: slots R + w, and R + nw + w for odd sub-groups, for a share's first piece)
 
   // ---- cursors over units --------------------------------------------------
   struct Cursor {
@@ -518,7 +529,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // block, so every unit issues the same loads; positions past the end are
   // removed later by position.
   auto load_table = [&](const Cursor& c) {
-    const int32_t* row = a.block_tables + (int64_t)real_of(c.s) * a.max_blocks_per_seq;
+    const int32_t* row = a.block_tables + (int64_t)seq_of(c.s) * a.max_blocks_per_seq;
     const int last = (c.len + BS - 1) / BS - 1;
     return row[min(c.base / BS + NBU * c.g + (lane % NBU), last)];
   };
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // pools do not hold yet): its lane reads the K row from k_new
       const int tn = c.len - 1 - (c.base + c.g * kGroupTokens);
       if (tn < kGroupTokens) {  // (uniform)
-        const half_t* np = a.k_new + ((int64_t)real_of(c.s) * Hkv + c.h) * D;
+        const half_t* np = a.k_new + ((int64_t)seq_of(c.s) * Hkv + c.h) * D;
         const bool mine = lane == tn;
 #pragma unroll
         for (int cc = 0; cc < kChunks; ++cc)
@@ -587,8 +598,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       const int r = i * (64 / kChunks) + q_row;
       int64_t row;
       if constexpr (Pair) {
-        q_ok[i] = r < G;
-        row = (int64_t)c.s * Hq + c.h * G + (q_ok[i] ? r : 0);
+        const int q0 = 4 * pair_sub0(c.s);  // the pass's first query head of the group
+        q_ok[i] = q0 + r < G;
+        row = (int64_t)seq_of(c.s) * Hq + c.h * G + q0 + (q_ok[i] ? r : 0);
       } else {
         q_ok[i] = r < q_rows(c.s);
         row = q_row0(c.s, c.h) + (q_ok[i] ? r : 0);
@@ -609,7 +621,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     if constexpr (Shared) {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
-        const int sv = u ? Sr + c.s : c.s;  // (Pair: the second sub-group's copy)
+        const int sv = Pair ? pair_seq(c.s, u) : c.s;
         const int64_t row0 = q_row0(sv, c.h);
         const int nr = q_rows(sv);
 #pragma unroll
@@ -640,7 +652,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // that every iteration issues the same loads.
   auto load_new = [&](const Cursor& c, half_t (&vn)[kSets]) {
     if constexpr (Fused) {
-      const int64_t row = ((int64_t)real_of(c.s) * Hkv + c.h) * D;
+      const int64_t row = ((int64_t)seq_of(c.s) * Hkv + c.h) * D;
 #pragma unroll
       for (int st = 0; st < kSets; ++st) vn[st] = a.v_new[row + st * 64 + lane];
     }
@@ -773,7 +785,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int r = s * Hkv + kvh;
     // the slot of a piece that starts share v inside the run (Pair: the
     // second sub-group's pieces have slots of their own)
-    const int r_share = Pair && sub_of(s) ? R + nw : R;
+    const int r_share = Pair && (sub_of(s) & 1) ? R + nw : R;
     const int nr = q_rows(s);
     const int64_t q0 = q_row0(s, kvh) - (int64_t)real_of(s) * Hq;  // (its first query head)
     // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
@@ -1099,8 +1111,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // query rows of each sub-group a pass over (cur.s, .) attends
   auto rows_of = [&](int s, int (&nr)[kSub]) {
     if constexpr (Pair) {
-      nr[0] = min(4, G);
-      nr[1] = G - 4;
+      const int q0 = 4 * pair_sub0(s);
+      nr[0] = min(4, G - q0);
+      nr[1] = min(4, G - q0 - 4);
     } else {
       nr[0] = q_rows(s);
     }
@@ -1307,7 +1320,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
-        const int sv = u ? Sr + cur.s : cur.s;
+        const int sv = Pair ? pair_seq(cur.s, u) : cur.s;
         const int slot = (piece_g0 == 0 && run_end) ? -1
                          : piece_g0 == 0            ? sv * Hkv + cur.h
                                                     : R + u * nw + w;

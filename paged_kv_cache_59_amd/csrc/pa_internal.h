@@ -89,10 +89,11 @@ enum {
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
-// The decode attends the two sub-groups of a KV head of 5..8 query heads in
-// one pass over the units (8 query rows), and then needs two share slots per
-// worker; other groups run one pass per sub-group (the copies of the batch).
-inline bool decode_pairs(int kv_split) { return kv_split == 2 && !kValu; }
+// With an even number of sub-groups (5..8, 13..16, .. query heads per KV
+// head) the decode attends them two per pass over the units (8 query rows),
+// and then needs two share slots per worker; otherwise one pass per
+// sub-group (the copies of the batch).
+inline bool decode_pairs(int kv_split) { return kv_split % 2 == 0 && !kValu; }
 // Bytes of arrival counters a launch over S sequences keeps against the end
 // of its workspace.
 size_t decode_control_bytes(int64_t S, int64_t Hkv);

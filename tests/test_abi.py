@@ -126,6 +126,12 @@ def test_workspace_sizes(L):
         assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
             v * 8 * 4 + v * 4 * 128 * 4 + a256(128 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
             + 128 * 8 * 4 + 256)
+    # G = 16: 4 sub-groups attended two per pass: two share slots per worker
+    v = 4 * 64 * 8 + 2 * 2048
+    pre = 4 * 4 * 64 * 8 * 4
+    assert L.pa_decode_workspace_size(64, 128, 8, 128, 2048, 2048) == (
+        v * 8 * 4 + v * 4 * 128 * 4 + a256(4 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
+        + 4 * 64 * 8 * 4 + 256)
     # G = 12: 3 sub-groups, three copies of the batch, one share slot per worker
     v = 3 * 64 * 8 + 2048
     pre = 4 * 3 * 64 * 8 * 4

@@ -61,7 +61,7 @@ def test_large_group_long_runs_cut(workers):
     run_fused(w, workers, f"fused G8 long runs over {workers} workers")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64), (16, 1, 128)])
 @pytest.mark.parametrize("workers", [0, 5000])
 def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
     """The prefix pass attends each sub-group's rows of a group's members
@@ -73,14 +73,16 @@ def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
               shared_blocks=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (12, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (12, 1), (16, 1)])
 def test_large_group_batch_above_one_launch(Hq, Hkv):
-    """G = 8: 2 copies, 2048 sequences per launch; G = 12: 3 copies, 1365."""
+    """G = 8: 2 sub-groups in one pass, 2048 sequences per launch; G = 12:
+    3 copies, 1365; G = 16: 2 copies of paired sub-groups, 1024."""
     w = wl.make_workload("groups-wide", 470 + Hq, Hq, Hkv, 64, len_range=(1, 40), num_seqs=4100)
     d = to_device(w)
     out = gpu_step(w, d, 0)
     kc, vc = oracle_pools(w)
-    seqs = np.unique(np.r_[0:40, 1350:1380, 2030:2070, 2720:2740, 4050:4100])  # launch edges
+    seqs = np.unique(np.r_[0:40, 1010:1040, 1350:1380, 2030:2070, 2720:2740, 3060:3080,
+                           4050:4100])  # launch edges
     compare(out[seqs], oracle_decode(w, kc, vc, seqs), f"G{Hq // Hkv} 4100 sequences")
 
 
