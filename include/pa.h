@@ -170,8 +170,8 @@ int32_t pa_decode_num_workers(void);
  * num_kv_heads included).  The workspace holds, from its start, the partial
  * results of sequences cut between workers (one per (sequence, KV head)
  * run and one per worker, 4 query-head rows each; with G > 4 query heads
- * per KV head each sequence counts ceil(G / 4) times here and below, and
- * with an even number of sub-groups each worker twice), then
+ * per KV head each sequence counts ceil(G / 4) times, rounded up to even,
+ * here and below, and each worker twice), then
  * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
  * its prefix length, per (chunk, sequence, query head) up to 4 normalised
  * fp16 rows and their log-sum-exps) and, against its end, one arrival
@@ -232,8 +232,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * the value product rounded to fp16); out is rounded to nearest even fp16.
  * Any G >= 1: the grouped query heads of a KV head (up to 4 at a time, the
  * rows of the decode's matrix instruction) share each K and V load; a group
- * of G > 4 is attended in ceil(G / 4) sub-groups, two per pass over K and V
- * when their number is even (else one), each pass a copy of the batch in
+ * of G > 4 is attended in ceil(G / 4) sub-groups (an empty one added to an
+ * odd count), two per pass over K and V, each pass a copy of the batch in
  * the same launch, whose reads of one block fall at the same time (the L2
  * serves part of the repeats).
  * num_seqs == 0 is a no-op.

@@ -163,7 +163,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
     return 0;
   const int32_t w = resolve_workers(num_workers);
   if (w <= 0) return 0;
-  const int32_t split = kv_split(num_q_heads, num_kv_heads);
+  const int32_t split = pa::decode_split(kv_split(num_q_heads, num_kv_heads));
   return pa::decode_workspace_bytes(seqs_per_launch(num_seqs, split) * split, num_kv_heads,
                                     head_dim, pa::decode_pairs(split) ? 2 * w : w);
 }
@@ -203,7 +203,10 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   // sub-groups, one copy of the batch each: a launch sees split x n virtual
   // sequences, at most kMaxSeqsPerLaunch; its 64-token units (all heads)
   // must fit a 32-bit index
-  const int32_t split = kv_split(num_q_heads, num_kv_heads);
+  // (split: the decode's sub-groups, an empty one added to an odd count
+  // above one; the prefix pass takes the sub-groups that hold query heads)
+  const int32_t groups = kv_split(num_q_heads, num_kv_heads);
+  const int32_t split = pa::decode_split(groups);
   const int64_t per_launch = seqs_per_launch(num_seqs, split);
   const int64_t vseqs = per_launch * split;
   if (vseqs * num_kv_heads * ceil_div(max_context_len, pa::kGroupTokens) > 0x7fffffff)
@@ -280,8 +283,8 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
       p.scale_log2 = a.scale_log2;
       p.num_seqs = (int)n;
       p.num_q_heads = num_q_heads;
-      p.num_kv_heads = num_kv_heads * split;  // (the pass takes sub-groups as heads)
-      p.kv_split = split;
+      p.num_kv_heads = num_kv_heads * groups;  // (the pass takes sub-groups as heads)
+      p.kv_split = groups;
       p.head_dim = head_dim;
       p.block_size = block_size;
       p.max_blocks_per_seq = max_blocks_per_seq;

@@ -263,7 +263,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int G = Hq / Hkv;    // query heads per KV head
   auto sub_of = [&](int s) { return split == 1 ? 0 : s / Sr; };
   auto real_of = [&](int s) { return split == 1 ? s : s - s / Sr * Sr; };
-  auto q_rows = [&](int s) { return split == 1 ? G : min(4, G - sub_of(s) * 4); };
+  // (an empty sub-group, added to an odd count, has none)
+  auto q_rows = [&](int s) { return split == 1 ? G : max(0, min(4, G - sub_of(s) * 4)); };
   // the q / out row of the first query head of run (s, h)
   auto q_row0 = [&](int s, int h) -> int64_t {
     return (int64_t)real_of(s) * Hq + h * G + sub_of(s) * 4;
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int st = 0; st < kSets; ++st)
             pre_o[u][g][st] = g < nr ? a.pre_o[(row0 + g) * D + st * 64 + lane] : (half_t)0.0f;
-        pre_m[u] = a.pre_lse[row0 + min(lane, nr - 1)];
+        pre_m[u] = nr > 0 ? a.pre_lse[row0 + min(lane, nr - 1)] : -INFINITY;
       }
     }
   };
@@ -903,7 +904,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       for (int c = 1; c < kPrefixMaxChunks; ++c) {
         const int64_t row0 = ((int64_t)c * Sr + real_of(s)) * Hq + hh * G + sub_of(s) * 4;
         const int nr = q_rows(s);
-        pf_m[c] = c < nch ? a.pre_lse[row0 + min(lane, nr - 1)] : -INFINITY;
+        pf_m[c] = (c < nch && nr > 0) ? a.pre_lse[row0 + min(lane, nr - 1)] : -INFINITY;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -1112,8 +1113,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   auto rows_of = [&](int s, int (&nr)[kSub]) {
     if constexpr (Pair) {
       const int q0 = 4 * pair_sub0(s);
-      nr[0] = min(4, G - q0);
-      nr[1] = min(4, G - q0 - 4);
+      nr[0] = max(0, min(4, G - q0));
+      nr[1] = max(0, min(4, G - q0 - 4));
     } else {
       nr[0] = q_rows(s);
     }

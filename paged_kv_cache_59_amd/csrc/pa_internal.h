@@ -89,11 +89,14 @@ enum {
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
-// With an even number of sub-groups (5..8, 13..16, .. query heads per KV
-// head) the decode attends them two per pass over the units (8 query rows),
-// and then needs two share slots per worker; otherwise one pass per
-// sub-group (the copies of the batch).
-inline bool decode_pairs(int kv_split) { return kv_split % 2 == 0 && !kValu; }
+// The decode attends sub-groups two per pass over the units (8 query rows)
+// and then needs two share slots per worker; an odd number of sub-groups
+// (above one) gets an empty last one.  The vector-ALU measurement build
+// takes one sub-group per pass (one copy of the batch each).
+inline int decode_split(int kv_split) {
+  return (kv_split > 1 && !kValu) ? kv_split + (kv_split & 1) : kv_split;
+}
+inline bool decode_pairs(int split) { return split % 2 == 0 && !kValu; }
 // Bytes of arrival counters a launch over S sequences keeps against the end
 // of its workspace.
 size_t decode_control_bytes(int64_t S, int64_t Hkv);

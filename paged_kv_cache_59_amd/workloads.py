@@ -426,6 +426,10 @@ WORKLOADS = {
     # lengths and K/V bytes of llama8b_b64.
     "llama405b_b64": dict(seed=2, num_q_heads=128, num_kv_heads=8, head_dim=128,
                           len_range=(128, 2048), num_seqs=64),
+    # 96 q / 8 KV heads (a group of 12: Mistral-Large-2-shaped), the lengths
+    # and K/V bytes of llama8b_b64.
+    "g12_b64": dict(seed=2, num_q_heads=96, num_kv_heads=8, head_dim=128,
+                    len_range=(128, 2048), num_seqs=64),
     # OPT-13B-shaped multi-head layer: batch 128, 40 heads, head_dim 128,
     # lengths uniform in [1, 2048].
     "opt13b_b128": dict(seed=3, num_q_heads=40, num_kv_heads=40, head_dim=128,

@@ -132,12 +132,9 @@ def test_workspace_sizes(L):
     assert L.pa_decode_workspace_size(64, 128, 8, 128, 2048, 2048) == (
         v * 8 * 4 + v * 4 * 128 * 4 + a256(4 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
         + 4 * 64 * 8 * 4 + 256)
-    # G = 12: 3 sub-groups, three copies of the batch, one share slot per worker
-    v = 3 * 64 * 8 + 2048
-    pre = 4 * 3 * 64 * 8 * 4
-    assert L.pa_decode_workspace_size(64, 96, 8, 128, 2048, 2048) == (
-        v * 8 * 4 + v * 4 * 128 * 4 + a256(3 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
-        + 3 * 64 * 8 * 4 + 256)
+    # G = 12: 3 sub-groups and an empty fourth, two per pass: as G = 16
+    assert (L.pa_decode_workspace_size(64, 96, 8, 128, 2048, 2048)
+            == L.pa_decode_workspace_size(64, 128, 8, 128, 2048, 2048))
 
 
 def test_cache_op_argument_errors(L):
