@@ -34,9 +34,10 @@ bool block_size_supported(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The decode attends a KV head of G > kMaxGroup query heads in
-// ceil(G / kMaxGroup) sub-groups of up to kMaxGroup query heads, one copy of
-// the batch per sub-group (num_q_heads a multiple of num_kv_heads).
+// A KV head of G > kMaxGroup query heads is attended in ceil(G / kMaxGroup)
+// sub-groups of up to kMaxGroup query heads (num_q_heads a multiple of
+// num_kv_heads): the prefix pass's heads; the decode takes them two per pass
+// (decode_split).
 int32_t kv_split(int32_t num_q_heads, int32_t num_kv_heads) {
   return (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
 }
@@ -200,9 +201,9 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
                 (reinterpret_cast<uintptr_t>(v_new) & 15)))
     return PA_ERR_INVALID_ARG;
   // A KV head of more than kMaxGroup query heads is attended in split
-  // sub-groups, one copy of the batch each: a launch sees split x n virtual
-  // sequences, at most kMaxSeqsPerLaunch; its 64-token units (all heads)
-  // must fit a 32-bit index
+  // sub-groups: the launch's merger sees split x n virtual sequences (one
+  // per sub-group and sequence), at most kMaxSeqsPerLaunch; its 64-token
+  // units (all heads) must fit a 32-bit index
   // (split: the decode's sub-groups, an empty one added to an odd count
   // above one; the prefix pass takes the sub-groups that hold query heads)
   const int32_t groups = kv_split(num_q_heads, num_kv_heads);

@@ -34,13 +34,16 @@
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
 //    would cost 64 per lane and halve the waves a SIMD holds).  A larger
-//    group is split into ceil(G / 4) sub-groups of up to 4 rows, and the
-//    batch is attended once per sub-group: the launch sees kv_split x S
-//    virtual sequences, sub-group j's copy of sequence s at j S + s.  Its
-//    units then lie exactly j / kv_split of the way along, so with equal
-//    shares the workers that read one block for different sub-groups read it
-//    at the same time, and (for an even split of the workers into runs of 32
-//    per XCD) on the same XCD, whose L2 serves the repeats.
+//    group is split into kv_split = ceil(G / 4) sub-groups of up to 4 rows
+//    (an empty one added to an odd count), attended two per pass: one pass
+//    over a unit forms both sub-groups' logits and products on two sets of
+//    MFMAs over the same K and V registers (8 q rows).  Each pair is a copy
+//    of the batch in the unit order, and the merger sees kv_split x S
+//    virtual sequences, sub-group j's copy of sequence s at j S + s.  With
+//    several copies, copy c's units lie exactly c / copies of the way along,
+//    so with equal shares the workers that read one block for different
+//    copies read it at the same time, and (for an even split of the workers
+//    into runs of 32 per XCD) on the same XCD, whose L2 serves the repeats.
 //  * q . K: lane l owns token l of the 64; it loads its 16-byte chunks of the
 //    K row (K pool [NB][Hkv][D/8][16][8]: for a fixed chunk the 64 lanes read
 //    four contiguous 256-byte runs) and feeds them as the B operand, so the

@@ -135,9 +135,9 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   float scale_log2;  // softmax scale times log2(e)
-  int num_seqs;      // virtual sequences: kv_split copies of the batch
+  int num_seqs;      // virtual sequences: one copy of the batch per sub-group
   int num_q_heads, num_kv_heads;
-  int kv_split;      // query-head sub-groups per KV head: ceil(G / kMaxGroup)
+  int kv_split;      // query-head sub-groups per KV head: decode_split(ceil(G / kMaxGroup))
   int head_dim;
   int block_size;  // 8, 16 or 32
   int max_blocks_per_seq;
