@@ -53,6 +53,25 @@ def test_noalloc_matches_workspace_call_twice_in_a_row():
         compare(out, oracle_decode(w, kc, vc), f"noalloc {w.name}")
 
 
+def test_noalloc_large_groups():
+    """8 and 12 query heads per KV head (sub-groups two per pass, two share
+    slots per worker in the array): bit for bit as with a workspace, and the
+    oracle's result, one call after the other."""
+    for w, workers in ((wl.make_workload("noalloc-g8", 404, 64, 8, 128, len_range=(1, 1500),
+                                         num_seqs=20), 0),
+                       (wl.make_workload("noalloc-g12", 405, 24, 2, 64, len_range=(1, 700),
+                                         num_seqs=9), 5)):
+        log(f"noalloc case {w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+            f"workers={workers}")
+        d_ref, d_new = to_device(w), to_device(w)
+        ref_out = _with_workspace(w, d_ref, workers)
+        out = _noalloc(w, d_new, workers)
+        assert np.array_equal(out.view(np.uint16), ref_out.view(np.uint16)), w.name
+        kc, vc = oracle_pools(w)
+        assert_pools_equal(d_new, kc, vc, w.name)
+        compare(out, oracle_decode(w, kc, vc), f"noalloc {w.name}")
+
+
 def test_noalloc_rejects_a_batch_above_its_array():
     """256 sequences x 64 KV heads at 512 workers need about 35 MB of partial
     results: the call returns PA_ERR_SCRATCH_LIMIT and enqueues nothing (the
