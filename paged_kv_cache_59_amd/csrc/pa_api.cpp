@@ -166,7 +166,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (w <= 0) return 0;
   const int32_t split = pa::decode_split(kv_split(num_q_heads, num_kv_heads));
   return pa::decode_workspace_bytes(seqs_per_launch(num_seqs, split) * split, num_kv_heads,
-                                    head_dim, pa::decode_pairs(split) ? 2 * w : w);
+                                    head_dim, pa::decode_slot_factor(split) * w);
 }
 
 }  // extern "C"
@@ -214,8 +214,8 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     return PA_ERR_UNSUPPORTED;
   const int32_t w = resolve_workers(num_workers);
   if (w < 0) return w;
-  // (paired sub-groups: two share slots per worker)
-  const int32_t slot_workers = pa::decode_pairs(split) ? 2 * w : w;
+  // (sub-groups attended together: a share slot per worker for each)
+  const int32_t slot_workers = pa::decode_slot_factor(split) * w;
   const size_t need =
       pa::decode_workspace_bytes(vseqs, num_kv_heads, head_dim, slot_workers);
   if (static_scratch) {

@@ -152,6 +152,25 @@ __device__ __forceinline__ half8_t load_kv(const half_t* p) { return load_nt(p);
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Max and sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes that
+// hold one query row of a 16x16 tile), with the gfx950 cross-row swaps; all
+// four lanes end with the same bits.
+__device__ __forceinline__ float max_row4(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum_row4(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // Measurement builds: a 100 MHz timestamp (the same clock on every CU), and
 // the XCC_ID / HW_ID hardware registers of the wave.
 __device__ __forceinline__ uint64_t stamp_now() {
@@ -198,13 +217,13 @@ __device__ __forceinline__ float4_t load_through16(const float* base, int off) {
 // pass per group over its common blocks, results in out and pre_lse); each
 // run covers its sequence's positions from a.pre_len[s] on, and its result
 // is folded together with the prefix pass's.
-// Pair (an even kv_split: 5..8, 13..16, .. query heads per KV head): one
-// pass over a unit attends two sub-groups (8 query rows on two sets of
-// MFMAs over the same K and V registers); the units enumerate kv_split / 2
-// copies of the batch, copy c for sub-groups 2c and 2c + 1, and each piece
-// is handed to the merger twice, as the pieces of those sub-groups' copies
-// (virtual sequences 2c Sr + s and (2c + 1) Sr + s) would be.
-template <int D, int BS, bool Fused, bool Shared, bool Pair>
+// Wide (more than 4 query heads per KV head): one pass over a unit attends
+// up to 4 sub-groups, 16 query rows, as the columns of 16x16x32 MFMA tiles;
+// the units enumerate one copy of the batch per 4 sub-groups (kv_split <= 4:
+// the batch once), and each piece is handed to the merger once per
+// sub-group, as the pieces of the sub-groups' copies (virtual sequences
+// j Sr + s) would be.
+template <int D, int BS, bool Fused, bool Shared, bool Wide>
 __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / kChunk;  // 16-byte chunks in one K row
   constexpr int kSets = D / 64;        // 64-dim ranges a lane covers in P.V
@@ -223,13 +242,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // Rows padded so that the 4 rows of one access fall in different LDS banks
   // (unpadded, rows 128 and 256 bytes apart share banks: 4-way conflicts).
   constexpr int kQRow = D + 8;  // halves per q row
-  constexpr int kPRow = 64 + 16;  // halves per softmax-weight row
-  constexpr int kRows = Pair ? 8 : 4;  // query rows a unit is attended for
-  static_assert(!(Pair && kValu), "the vector-ALU measurement build attends 4 rows");
+  // (Wide: 16 rows of 64 weights, 144 bytes apart, so that the 16 rows of a
+  // 16-byte access fall in distinct banks)
+  constexpr int kPRow = Wide ? 64 + 8 : 64 + 16;  // halves per softmax-weight row
+  constexpr int kRows = Wide ? 16 : 4;  // query rows a unit is attended for
+  constexpr int kSub = Wide ? 4 : 1;    // sub-groups of 4 rows a pass can attend
+  constexpr int kWT = D / 16;           // Wide: 16-dim tiles of the output and of V
+  constexpr int kWK = D / 32;           // Wide: 32-dim steps of the logits
+  static_assert(!(Wide && kValu), "the vector-ALU measurement build attends 4 rows");
   __shared__ __attribute__((aligned(16))) half_t p_lds[kRows * kPRow];
   __shared__ __attribute__((aligned(16))) half_t q_lds[kRows * kQRow];
   // streamer -> merger: cut pieces, a ring of kRing entries
-  __shared__ float ring_o[kRing][4 * D];
+  __shared__ __attribute__((aligned(16))) float ring_o[kRing][4 * D];
   __shared__ float ring_ml[kRing][8];
   __shared__ int ring_meta[kRing][4];  // sequence, KV head, partial slot, units
   __shared__ int ctl[4];  // ring produced/consumed, streamer done
@@ -254,7 +278,6 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   }
   const int w = (nw % 8 == 0) ? ((bx / 8) / kw) * 8 * kw + (bx % 8) * kw + (bx / 8) % kw : bx;
   const int Sv = a.num_seqs;          // virtual sequences (slots, counters)
-  const int S = Pair ? Sv / 2 : Sv;   // sequences in unit order (the unit tables)
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   // Sub-groups: a KV head with more than 4 query heads is attended in
@@ -263,6 +286,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // s / Sr of sequence s % Sr.
   const int split = a.kv_split;
   const int Sr = Sv / split;  // sequences of the batch (lengths, tables, new rows)
+  // sequences in unit order (the unit tables); Wide: one copy of the batch
+  // per 4 sub-groups (a split above 4 is a multiple of 4)
+  const int S = !Wide ? Sv : split <= kSub ? Sr : Sv / kSub;
+  const int n_sub = Wide ? min(split, kSub) : 1;  // sub-groups a pass attends
   const int G = Hq / Hkv;    // query heads per KV head
   auto sub_of = [&](int s) { return split == 1 ? 0 : s / Sr; };
   auto real_of = [&](int s) { return split == 1 ? s : s - s / Sr * Sr; };
@@ -273,17 +300,19 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     return (int64_t)real_of(s) * Hq + h * G + sub_of(s) * 4;
   };
   // a virtual sequence's entry in the unit tables
-  auto tab = [&](int s) { return Pair ? sub_of(s) / 2 * Sr + real_of(s) : s; };
-  // Pair: the first of the two sub-groups a table entry's pass attends (one
-  // pair, kv_split == 2: the table holds the batch once, no division), the
-  // sequence of the batch at table entry t, and the virtual sequence of the
-  // pass's sub-group u
-  auto pair_sub0 = [&](int t) { return split == 2 ? 0 : 2 * (t / Sr); };
+  auto tab = [&](int s) {
+    if constexpr (Wide) return split <= kSub ? real_of(s) : sub_of(s) / kSub * Sr + real_of(s);
+    else return s;
+  };
+  // Wide: the first of the sub-groups a table entry's pass attends (kv_split
+  // <= 4: the table holds the batch once, no division), the sequence of the
+  // batch at table entry t, and the virtual sequence of the pass's sub-group u
+  auto pass_sub0 = [&](int t) { return split <= kSub ? 0 : kSub * (t / Sr); };
   auto seq_of = [&](int t) {
-    if constexpr (Pair) return split == 2 ? t : t - t / Sr * Sr;
+    if constexpr (Wide) return split <= kSub ? t : t - t / Sr * Sr;
     else return real_of(t);
   };
-  auto pair_seq = [&](int t, int u) { return (pair_sub0(t) + u) * Sr + seq_of(t); };
+  auto pass_seq = [&](int t, int u) { return (pass_sub0(t) + u) * Sr + seq_of(t); };
   int* const off_lds = seq_lds;
   int* const len_lds = seq_lds + S;
   int* const base_lds = seq_lds + 2 * S;  // Shared: the positions before unit 0 of s's runs
@@ -459,7 +488,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   if (my_first >= my_end) return;
   // Partial slots: [0, R) the piece that starts run r, R + j the piece that
   // starts share j inside a run.
-  const int R = Sv * Hkv;  // (Pair: slots R + w, and R + nw + w for odd sub-groups, for a share's first piece)
+  // (Wide: slot R + u nw + j for sub-group u of a pass)
+  const int R = Sv * Hkv;
 
   // ---- cursors over units --------------------------------------------------
   struct Cursor {
@@ -547,17 +577,60 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  half8_t kreg[kChunks];
+  half8_t kreg[kChunks];  // (Wide: [tile kt][32-dim step j], kt * kWK + j)
   half8_t vreg[8][kSets];  // 8-token group g of the unit, 64-dim range st
+  half8_t vw[kWT][2];      // Wide: V^T operand of 16-dim tile i, 32-token step kk
+  // Wide: lane 16 wq + wm holds column wm (query row wm, or token wm of a
+  // tile) and k-slice wq of the 16x16x32 operands
+  const int wq = lane >> 4, wm = lane & 15;
   // q rows of a run: load i, lane r*kChunks + c: 16-byte chunk c of row
   // i * 64 / kChunks + r
-  constexpr int kSub = Pair ? 2 : 1;  // sub-groups of 4 rows a pass attends
   constexpr int kQLoads = (kRows * kChunks + 63) / 64;
   half8_t qreg[kQLoads];
   // K of unit c: lane l's token lies in the unit's block l / BS, whose table
   // entry lane l / BS of the table load tbl holds (a cross-lane read, not a
   // register-indexed select, which the compiler would turn into scratch)
-  auto load_k = [&](const Cursor& c, int tbl) {
+  auto load_k = [&](const Cursor& c, int tbl, const int (&pb)[NBU]) {
+    if constexpr (Wide) {
+      // A operand of the logits: tile kt holds tokens 16 kt .. 16 kt + 15 of
+      // the unit as its rows; for the 32-dim step j lane 16 wq + wm loads
+      // 16-byte chunk 4 j + wq of token 16 kt + wm (with blocks of 16, one
+      // load reads 1 KiB contiguous)
+      auto tile = [&](int kt) {
+        int phys, slot;
+        if constexpr (BS >= 16) {
+          phys = pb[16 * kt / BS];
+          slot = 16 * kt % BS + wm;
+        } else {
+          phys = (wm >> 3) ? pb[2 * kt + 1] : pb[2 * kt];
+          slot = wm & 7;
+        }
+        return a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
+               (int64_t)(wq * BS + slot) * kChunk;
+      };
+      if constexpr (Fused) {
+        const int tn = c.len - 1 - (c.base + c.g * kGroupTokens);
+        if (tn < kGroupTokens) {  // (uniform) the new token's lanes read k_new
+          const half_t* np = a.k_new + ((int64_t)seq_of(c.s) * Hkv + c.h) * D + wq * kChunk;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const half_t* kp = tile(kt);
+            const bool mine = 16 * kt + wm == tn;
+#pragma unroll
+            for (int j = 0; j < kWK; ++j)
+              kreg[kt * kWK + j] = load_kv(mine ? np + j * 4 * kChunk : kp + j * 4 * BS * kChunk);
+          }
+          return;
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const half_t* kp = tile(kt);
+#pragma unroll
+        for (int j = 0; j < kWK; ++j) kreg[kt * kWK + j] = load_kv(kp + j * 4 * BS * kChunk);
+      }
+      return;
+    }
     const int e = __shfl(tbl, my_blk);
     const int phys = (e >= 0 && e < a.num_blocks) ? e : 0;
     const half_t* kp = a.k_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
@@ -581,6 +654,24 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // V group g (tokens 8g..8g+7 of the unit) is group g % kGroups of the
   // unit's block g / kGroups: for a fixed 64-dim range one 1 KiB load
   auto load_v = [&](const Cursor& c, const int (&pb)[NBU]) {
+    if constexpr (Wide) {
+      // A operand of the products (V^T): for the 32-token step kk lane
+      // 16 wq + wm loads dim 16 i + wm of the unit's 8-token group 4 kk + wq
+      // (16 bytes), for each 16-dim tile i
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        int phys;
+        if constexpr (kGroups == 4) phys = pb[kk];
+        else if constexpr (kGroups == 2) phys = (wq >> 1) ? pb[2 * kk + 1] : pb[2 * kk];
+        else
+          phys = wq == 0 ? pb[4 * kk] : wq == 1 ? pb[4 * kk + 1] : wq == 2 ? pb[4 * kk + 2] : pb[4 * kk + 3];
+        const half_t* vp = a.v_cache + (int64_t)phys * block_stride + (int64_t)c.h * kTile +
+                           (int64_t)(((4 * kk + wq) % kGroups) * D + wm) * kChunk;
+#pragma unroll
+        for (int i = 0; i < kWT; ++i) vw[i][kk] = load_kv(vp + i * 16 * kChunk);
+      }
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       const half_t* vp = a.v_cache + (int64_t)pb[g / kGroups] * block_stride +
@@ -592,8 +683,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // q rows of c's run; every lane loads (rows past the head's and lanes past
   // the rows re-read row 0 and are zeroed at the LDS write) so the load is
   // unconditional
-  // (Pair: rows 0..7 of the 8 are query heads h G + 0..7 of the sequence,
-  // rows past G zero; one load covers 64 / kChunks rows)
+  // (Wide: rows 0..15 of the 16 are query heads h G + q0 + 0..15 of the
+  // sequence, q0 the pass's first, rows past G zero; one load covers
+  // 64 / kChunks rows)
   const int q_row = lane / kChunks, q_chunk = lane % kChunks;
   bool q_ok[kQLoads];  // this lane's row of each load holds a query head
   auto load_q = [&](const Cursor& c) {
@@ -601,8 +693,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     for (int i = 0; i < kQLoads; ++i) {
       const int r = i * (64 / kChunks) + q_row;
       int64_t row;
-      if constexpr (Pair) {
-        const int q0 = 4 * pair_sub0(c.s);  // the pass's first query head of the group
+      if constexpr (Wide) {
+        const int q0 = 4 * pass_sub0(c.s);  // the pass's first query head of the group
         q_ok[i] = q0 + r < G;
         row = (int64_t)seq_of(c.s) * Hq + c.h * G + q0 + (q_ok[i] ? r : 0);
       } else {
@@ -619,13 +711,27 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // instead of from nothing: the run's online softmax then takes the prefix
   // in with no fold afterwards.  (Further chunks, of prefixes above one
   // chunk, are folded by the merger.)
+  // (Wide: lane 16 wq + wm, the pass's query row wm, dims 16 i + 4 wq .. + 3)
   half_t pre_o[kSub][4][kSets];
   float pre_m[kSub];
+  half4_t pre_w[kWT];
+  float pre_mw = -INFINITY;
   auto load_pre = [&](const Cursor& c) {
-    if constexpr (Shared) {
+    if constexpr (Shared && Wide) {
+      const int q0 = 4 * pass_sub0(c.s);
+      const bool ok = q0 + wm < G;
+      const int64_t row = (int64_t)seq_of(c.s) * Hq + c.h * G + q0 + (ok ? wm : 0);
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) {
+        const half4_t v = *reinterpret_cast<const half4_t*>(a.pre_o + row * D + 16 * i + 4 * wq);
+        pre_w[i] = ok ? v : half4_t{};
+      }
+      const float lse = a.pre_lse[row];
+      pre_mw = ok ? lse : -INFINITY;
+    } else if constexpr (Shared) {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
-        const int sv = Pair ? pair_seq(c.s, u) : c.s;
+        const int sv = c.s;
         const int64_t row0 = q_row0(sv, c.h);
         const int nr = q_rows(sv);
 #pragma unroll
@@ -787,9 +893,9 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const int n = uniform(run_units(ts));
     const int u0 = Hkv * uniform(off_lds[ts]) + kvh * n;
     const int r = s * Hkv + kvh;
-    // the slot of a piece that starts share v inside the run (Pair: the
-    // second sub-group's pieces have slots of their own)
-    const int r_share = Pair && (sub_of(s) & 1) ? R + nw : R;
+    // the slot of a piece that starts share v inside the run (Wide: each
+    // sub-group of a pass has slots of its own)
+    const int r_share = Wide ? R + (sub_of(s) & (kSub - 1)) * nw : R;
     const int nr = q_rows(s);
     const int64_t q0 = q_row0(s, kvh) - (int64_t)real_of(s) * Hq;  // (its first query head)
     // Shared: the prefix pass's chunks 1.. of the run's rows (the piece that
@@ -861,7 +967,18 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // (one set per sub-group the pass attends)
   float m_run[kSub][4], l_lane[kSub][4];
   float4_t acc_o[kSub][kSets];
+  // (Wide: lane 16 wq + wm holds query row wm: its running max, its part of
+  // the sum, and dims 16 i + 4 wq .. + 3 of its unnormalised output, tile i)
+  float w_m = -INFINITY, w_l = 0.0f;
+  float4_t w_acc[kWT];
   auto reset_run = [&]() {
+    if constexpr (Wide) {
+      w_m = -INFINITY;
+      w_l = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) w_acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
 #pragma unroll
@@ -876,6 +993,15 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // a piece that starts a run with a prefix: begin from its first chunk
   // (nr[u]: query rows of sub-group u)
   auto seed_pre = [&](const int (&nr)[kSub]) {
+    if constexpr (Wide) {  // (rows past the group: max -inf, nothing)
+      w_m = pre_mw;
+      w_l = (wq == 0 && pre_mw != -INFINITY) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kWT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w_acc[i][e] = (float)pre_w[i][e];
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
 #pragma unroll
@@ -1104,7 +1230,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   // wait counts at the loop head are merged over both ways in
   __builtin_amdgcn_sched_barrier(0);
   half_t vn_cur[kSets] = {}, vn_nxt[kSets] = {};
-  load_k(cur, tbl_cur);
+  load_k(cur, tbl_cur, pb_cur);
   load_new(cur, vn_cur);
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur, pb_cur);
@@ -1114,10 +1240,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   reset_run();
   // query rows of each sub-group a pass over (cur.s, .) attends
   auto rows_of = [&](int s, int (&nr)[kSub]) {
-    if constexpr (Pair) {
-      const int q0 = 4 * pair_sub0(s);
-      nr[0] = max(0, min(4, G - q0));
-      nr[1] = max(0, min(4, G - q0 - 4));
+    if constexpr (Wide) {
+      const int q0 = 4 * pass_sub0(s);
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) nr[u] = max(0, min(4, G - q0 - 4 * u));
     } else {
       nr[0] = q_rows(s);
     }
@@ -1150,7 +1276,16 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < kSub; ++u) sacc_u[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float4_t& sacc = sacc_u[0];
-    if constexpr (kValu) {
+    if constexpr (Wide) {
+      // S^T = K Q^T, one 16x16 tile per 16 tokens: sacc_u[kt] holds, in lane
+      // 16 wq + wm, query row wm's logits at tokens 16 kt + 4 wq + 0..3
+#pragma unroll
+      for (int j = 0; j < kWK; ++j) {
+        const half8_t qb = *reinterpret_cast<const half8_t*>(q_lds + wm * kQRow + 32 * j + 8 * wq);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sacc_u[kt] = mfma16(kreg[kt * kWK + j], qb, sacc_u[kt]);
+      }
+    } else if constexpr (kValu) {
       // (measurement build) lane = token: its K row against each head's q
       // row, read from LDS by every lane at once, in pairs of dims
 #pragma unroll
@@ -1172,7 +1307,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {  // (Pair: the second sub-group's rows 4..7)
+        for (int u = 0; u < kSub; ++u) {
           const half8_t qv =
               *reinterpret_cast<const half8_t*>(q_lds + (4 * u + g_lane) * kQRow + c * kChunk);
           sacc_u[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(lo4(qv), lo4(kreg[c]), sacc_u[u], 0, 0, 0);
@@ -1190,7 +1325,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     // table entries two units ahead, then the next unit's K and q
     const int tbl_nxt2 = load_table(nxt2);
     blocks_of(tbl_nxt, pb_nxt);
-    load_k(nxt, tbl_nxt);
+    load_k(nxt, tbl_nxt, pb_nxt);
     load_q(nxt);
     load_new(nxt, vn_nxt);
     // the unit after nxt2, computed while this unit's V is in flight
@@ -1198,6 +1333,36 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
 
     // online softmax over these 64 positions
     // (every unit holds at least one position: its first, t0 < len)
+    if constexpr (Wide) {
+      // lane 16 wq + wm: query row wm at positions t0 + 16 kt + 4 wq + e; the
+      // row's max over the unit from its four lanes
+      float z[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[kt][e] = t0 + 16 * kt + 4 * wq + e < cur.len ? sacc_u[kt][e] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, z[kt][e]);
+        }
+      const float m_new = fmaxf(w_m, max_row4(mx));
+      const float alpha = fast_exp2(w_m - m_new);  // 0 at the piece's first unit
+      const half2x one = {(half_t)1.0f, (half_t)1.0f};
+      float ls = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        half4_t ph;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ph[e] = (half_t)fast_exp2(z[kt][e] - m_new);
+        ls = __builtin_amdgcn_fdot2(half2x{ph[0], ph[1]}, one, ls, false);
+        ls = __builtin_amdgcn_fdot2(half2x{ph[2], ph[3]}, one, ls, false);
+        *reinterpret_cast<half4_t*>(p_lds + wm * kPRow + 16 * kt + 4 * wq) = ph;
+      }
+      w_l = w_l * alpha + ls;
+#pragma unroll
+      for (int i = 0; i < kWT; ++i) w_acc[i] *= alpha;
+      w_m = m_new;
+    } else {
     const bool live = (t0 + lane) < cur.len;
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
@@ -1216,6 +1381,7 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         }
         p_lds[(4 * u + g) * kPRow + lane] = ph;
       }
+    }
 
     if constexpr (kTrace) {
       if (tr[kTrUnits]++ == 0) tr[kTrFirstUnit] = stamp_now();
@@ -1230,6 +1396,33 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     if (Fused ? t_end <= kGroupTokens : t_end < kGroupTokens) {
       const int tn = Fused ? t_end - 1 : kGroupTokens;
       const int keep_end = Fused ? tn : t_end;  // positions < keep_end come from the pools
+      if constexpr (Wide) {
+        // lane 16 wq + wm holds positions 32 kk + 8 wq + 2 x, + 1 of dim
+        // 16 i + wm in word x of vw[i][kk] (masks per lane); the new token's
+        // V element comes from the lane of v_new's load that holds the dim
+        uint32_t vnw[kWT] = {};
+        if constexpr (Fused) {
+#pragma unroll
+          for (int i = 0; i < kWT; ++i) {
+            const int bits = __shfl((int)__builtin_bit_cast(uint16_t, vn_cur[i / 4]), 16 * (i % 4) + wm);
+            vnw[i] = ((uint32_t)bits & 0xffffu) << (16 * (tn & 1));
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int p0 = 32 * kk + 8 * wq + 2 * x;
+            const uint32_t keep = (p0 < keep_end ? 0x0000ffffu : 0u) | (p0 + 1 < keep_end ? 0xffff0000u : 0u);
+            const bool put = Fused && p0 == (tn & ~1);
+#pragma unroll
+            for (int i = 0; i < kWT; ++i) {
+              uint4_t wv = __builtin_bit_cast(uint4_t, vw[i][kk]);
+              wv[x] = (wv[x] & keep) | (put ? vnw[i] : 0u);
+              vw[i][kk] = __builtin_bit_cast(half8_t, wv);
+            }
+          }
+      } else {
       uint32_t vnw[kSets];
 #pragma unroll
       for (int st = 0; st < kSets; ++st)
@@ -1247,10 +1440,20 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           vreg[g][st] = __builtin_bit_cast(half8_t, w);
         }
       });
+      }
     }
 
     __builtin_amdgcn_wave_barrier();
-    if constexpr (kValu) {
+    if constexpr (Wide) {
+      // O^T tile i += V^T (dims 16 i .., tokens 32 kk ..) P^T: lane 16 wq + wm
+      // takes query row wm's weights of tokens 32 kk + 8 wq .. + 7
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const half8_t pb8 = *reinterpret_cast<const half8_t*>(p_lds + wm * kPRow + 32 * kk + 8 * wq);
+#pragma unroll
+        for (int i = 0; i < kWT; ++i) w_acc[i] = mfma16(vw[i][kk], pb8, w_acc[i]);
+      }
+    } else if constexpr (kValu) {
       // (measurement build) lane = dim 64 st + lane: each head's weights,
       // read from LDS by every lane at once, against its 8-token V groups, in
       // pairs of tokens
@@ -1298,10 +1501,15 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
     const bool run_end = cur.g + 1 == cur.n_s;
     if (run_end || !nxt.valid) {
       float l_tot[kSub][4];
+      float lt_w = 0.0f;  // Wide: query row wm's sum
+      if constexpr (Wide) {
+        lt_w = sum_row4(w_l);
+      } else {
 #pragma unroll
-      for (int u = 0; u < kSub; ++u)
+        for (int u = 0; u < kSub; ++u)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) l_tot[u][g] = (g < nrs[u]) ? wave_sum(l_lane[u][g]) : 1.0f;
+          for (int g = 0; g < 4; ++g) l_tot[u][g] = (g < nrs[u]) ? wave_sum(l_lane[u][g]) : 1.0f;
+      }
       // The piece goes to the merger through the LDS ring (wait while the
       // ring is full, which the merger rarely lets happen): a whole run
       // (slot -1), which the merger normalises and stores, or a cut piece: a
@@ -1310,10 +1518,11 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
       // stores nothing inside the loop: a wave's memory operations complete
       // in order, so a store here would hold back the K/V loads issued after
       // it, a memory latency at every run end.
-      // (Pair: one entry per sub-group, as the pieces of the two copies of
-      // the batch: sequence Sr + s and share slot R + nw + w for the second)
+      // (Wide: one entry per sub-group of the pass, as the pieces of the
+      // sub-groups' copies of the batch: sequence u Sr + s and share slot
+      // R + u nw + w for sub-group u)
       const uint64_t t_ring = stamp_now();
-      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) > kRing - kSub; ++spin) {
+      for (int spin = 0; ring_made - lds_ld(&ctl[kCtlRingTaken]) > kRing - n_sub; ++spin) {
         if (spin >= a.spin_limit) {  // give up (reported in the status word)
           if (lane == 0)
             __hip_atomic_store(a.ws.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1322,9 +1531,34 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
         __builtin_amdgcn_s_sleep(1);
       }
       if constexpr (kTrace) tr[kTrRingWait] += stamp_now() - t_ring;
+      if constexpr (Wide) {
+        // lane u < n_sub describes entry u; lane 16 wq + wm writes query row
+        // wm's part into entry wm / 4, as its row wm % 4
+        if (lane < n_sub) {
+          const int sv = pass_seq(cur.s, lane);
+          const int k = (ring_made + lane) % kRing;
+          ring_meta[k][0] = sv;
+          ring_meta[k][1] = cur.h;
+          ring_meta[k][2] = (piece_g0 == 0 && run_end) ? -1
+                            : piece_g0 == 0            ? sv * Hkv + cur.h
+                                                       : R + lane * nw + w;
+          ring_meta[k][3] = cur.g - piece_g0 + 1;
+        }
+        const int u = wm >> 2, g = wm & 3;
+        if (u < n_sub) {
+          const int k = (ring_made + u) % kRing;
+#pragma unroll
+          for (int i = 0; i < kWT; ++i)
+            *reinterpret_cast<float4_t*>(&ring_o[k][g * D + 16 * i + 4 * wq]) = w_acc[i];
+          if (wq == 0) {
+            ring_ml[k][2 * g] = w_m;
+            ring_ml[k][2 * g + 1] = lt_w;
+          }
+        }
+      } else {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
-        const int sv = Pair ? pair_seq(cur.s, u) : cur.s;
+        const int sv = cur.s;
         const int slot = (piece_g0 == 0 && run_end) ? -1
                          : piece_g0 == 0            ? sv * Hkv + cur.h
                                                     : R + u * nw + w;
@@ -1353,7 +1587,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
           ring_meta[k][3] = cur.g - piece_g0 + 1;
         }
       }
-      ring_made += kSub;
+      }
+      ring_made += n_sub;
       lds_st(&ctl[kCtlRingMade], ring_made);
       if constexpr (kTrace) ++tr[kTrPieces];
       reset_run();
@@ -1494,31 +1729,31 @@ DecodeWorkspace decode_workspace_carve(void* base, size_t bytes, int64_t S, int6
   return w;
 }
 
-template <int D, int BS, bool Fused, bool Shared, bool Pair>
+template <int D, int BS, bool Fused, bool Shared, bool Wide>
 void launch_decode_f(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((unsigned)a.num_workers);
   const uint32_t lds = (uint32_t)((size_t)a.num_seqs * (Shared ? 3 : 2) * sizeof(int));
   if (!start && !stop)
-    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Pair>), grid, dim3(128), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Wide>), grid, dim3(128), lds, stream, a);
   else  // the events take the kernel's own start and end times
-    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Pair>), grid, dim3(128), lds,
+    hipExtLaunchKernelGGL((decode_kernel<D, BS, Fused, Shared, Wide>), grid, dim3(128), lds,
                           stream, start, stop, 0, a);
 }
 
-template <int D, int BS, bool Pair>
+template <int D, int BS, bool Wide>
 void launch_decode_p(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (a.k_new && a.pre_len)
-    launch_decode_f<D, BS, true, true, Pair>(a, stream, start, stop);
+    launch_decode_f<D, BS, true, true, Wide>(a, stream, start, stop);
   else if (a.k_new)
-    launch_decode_f<D, BS, true, false, Pair>(a, stream, start, stop);
+    launch_decode_f<D, BS, true, false, Wide>(a, stream, start, stop);
   else
-    launch_decode_f<D, BS, false, false, Pair>(a, stream, start, stop);
+    launch_decode_f<D, BS, false, false, Wide>(a, stream, start, stop);
 }
 
 template <int D, int BS>
 void launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if constexpr (!kValu) {
-    if (decode_pairs(a.kv_split)) {
+    if (decode_wide(a.kv_split)) {
       launch_decode_p<D, BS, true>(a, stream, start, stop);
       return;
     }

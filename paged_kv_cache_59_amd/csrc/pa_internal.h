@@ -89,14 +89,18 @@ enum {
 };
 
 size_t decode_workspace_bytes(int64_t S, int64_t Hkv, int64_t D, int64_t workers);
-// The decode attends sub-groups two per pass over the units (8 query rows)
-// and then needs two share slots per worker; an odd number of sub-groups
-// (above one) gets an empty last one.  The vector-ALU measurement build
-// takes one sub-group per pass (one copy of the batch each).
+// The decode attends up to 4 sub-groups per pass over the units (16 query
+// rows, the columns of 16x16 MFMA tiles) and then needs one share slot per
+// worker and sub-group of a pass; a count above 4 is rounded up to a
+// multiple of 4 (empty sub-groups at the end), one copy of the batch per 4.
+// The vector-ALU measurement build takes one sub-group per pass (one copy of
+// the batch each).
 inline int decode_split(int kv_split) {
-  return (kv_split > 1 && !kValu) ? kv_split + (kv_split & 1) : kv_split;
+  return (kv_split > 4 && !kValu) ? (kv_split + 3) / 4 * 4 : kv_split;
 }
-inline bool decode_pairs(int split) { return split % 2 == 0 && !kValu; }
+inline bool decode_wide(int split) { return split > 1 && !kValu; }
+// share slots per worker: one per sub-group a pass attends
+inline int decode_slot_factor(int split) { return decode_wide(split) ? (split < 4 ? split : 4) : 1; }
 // Bytes of arrival counters a launch over S sequences keeps against the end
 // of its workspace.
 size_t decode_control_bytes(int64_t S, int64_t Hkv);

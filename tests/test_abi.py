@@ -126,15 +126,21 @@ def test_workspace_sizes(L):
         assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
             v * 8 * 4 + v * 4 * 128 * 4 + a256(128 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
             + 128 * 8 * 4 + 256)
-    # G = 16: 4 sub-groups attended two per pass: two share slots per worker
-    v = 4 * 64 * 8 + 2 * 2048
-    pre = 4 * 4 * 64 * 8 * 4
-    assert L.pa_decode_workspace_size(64, 128, 8, 128, 2048, 2048) == (
-        v * 8 * 4 + v * 4 * 128 * 4 + a256(4 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
-        + 4 * 64 * 8 * 4 + 256)
-    # G = 12: 3 sub-groups and an empty fourth, two per pass: as G = 16
-    assert (L.pa_decode_workspace_size(64, 96, 8, 128, 2048, 2048)
-            == L.pa_decode_workspace_size(64, 128, 8, 128, 2048, 2048))
+    # G = 16, 12: 4 or 3 sub-groups (virtual sequences 64 each), attended in
+    # one pass: a share slot per worker for each
+    for hq, sub in ((128, 4), (96, 3)):
+        v = sub * 64 * 8 + sub * 2048
+        pre = 4 * sub * 64 * 8 * 4
+        assert L.pa_decode_workspace_size(64, hq, 8, 128, 2048, 2048) == (
+            v * 8 * 4 + v * 4 * 128 * 4 + a256(sub * 64 * 4) + a256(pre * 4)
+            + a256(pre * 128 * 2) + sub * 64 * 8 * 4 + 256)
+    # G = 20: 5 sub-groups, rounded up to 8 (two copies of the batch, 4
+    # sub-groups per pass): four share slots per worker
+    v = 8 * 64 * 8 + 4 * 2048
+    pre = 4 * 8 * 64 * 8 * 4
+    assert L.pa_decode_workspace_size(64, 160, 8, 128, 2048, 2048) == (
+        v * 8 * 4 + v * 4 * 128 * 4 + a256(8 * 64 * 4) + a256(pre * 4) + a256(pre * 128 * 2)
+        + 8 * 64 * 8 * 4 + 256)
 
 
 def test_cache_op_argument_errors(L):

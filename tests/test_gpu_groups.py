@@ -21,10 +21,11 @@ from tests.test_gpu_fused import FUSED_LENS, fused_step, run_fused
 
 pytestmark = pytest.mark.gpu
 
-# (Hq, Hkv, D): G = 8 (4 + 4), 7 (4 + 3), 5 (4 + 1), 6 (4 + 2), 12 (4 + 4 | 4 + an
-# empty sub-group), 9 (4 + 4 | 1 + empty), 16 (two passes of 4 + 4)
+# (Hq, Hkv, D): G = 8 (4 + 4), 7 (4 + 3), 5 (4 + 1), 6 (4 + 2), 12 (4 + 4 + 4), 9
+# (4 + 4 + 1), 16 (4 + 4 + 4 + 4), all in one pass; 20 (two passes: 4 x 4 | 4 +
+# three empty sub-groups), 32 (two passes of 4 x 4)
 GROUPS = [(8, 1, 128), (64, 8, 128), (28, 4, 128), (5, 1, 64), (12, 2, 64), (16, 1, 128),
-          (6, 1, 128), (9, 1, 64)]
+          (6, 1, 128), (9, 1, 64), (20, 1, 64), (64, 2, 128)]
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", GROUPS)
