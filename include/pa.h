@@ -93,7 +93,7 @@ extern "C" {
 enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size     */
-  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block size, G > 4        */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, block size, sizes > 2^31 */
   PA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
   PA_ERR_HIP = -4,         /* a HIP call or kernel launch failed              */
   PA_ERR_SCRATCH_LIMIT = -5, /* pa_decode_append_noalloc: batch above its array */
@@ -170,8 +170,9 @@ int32_t pa_decode_num_workers(void);
  * num_kv_heads included).  The workspace holds, from its start, the partial
  * results of sequences cut between workers (one per (sequence, KV head)
  * run and one per worker, 4 query-head rows each; with G > 4 query heads
- * per KV head each sequence counts ceil(G / 4) times, rounded up to even,
- * here and below, and each worker twice), then
+ * per KV head each sequence counts ceil(G / 4) times, above 4 rounded up to
+ * a multiple of 4, here and below, and each worker min(ceil(G / 4), 4)
+ * times), then
  * the shared-prefix pass's results (PA_DECODE_SHARED_BLOCKS: per sequence
  * its prefix length, per (chunk, sequence, query head) up to 4 normalised
  * fp16 rows and their log-sum-exps) and, against its end, one arrival
@@ -230,12 +231,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *
  * Accumulation is fp32 (products of fp16 inputs; the softmax weights enter
  * the value product rounded to fp16); out is rounded to nearest even fp16.
- * Any G >= 1: the grouped query heads of a KV head (up to 4 at a time, the
- * rows of the decode's matrix instruction) share each K and V load; a group
- * of G > 4 is attended in ceil(G / 4) sub-groups (an empty one added to an
- * odd count), two per pass over K and V, each pass a copy of the batch in
- * the same launch, whose reads of one block fall at the same time (the L2
- * serves part of the repeats).
+ * Any G >= 1: the grouped query heads of a KV head share each K and V load.
+ * Up to 4 are the rows of a 4x4x4 matrix instruction; a group of G > 4 is
+ * taken as ceil(G / 4) sub-groups of up to 4 query heads, up to 16 query
+ * heads per pass over K and V, as the columns of 16x16x32 matrix tiles.
+ * Above 16 the passes are copies of the batch in the same launch, whose
+ * reads of one block fall at the same time (the L2 serves most repeats).
  * num_seqs == 0 is a no-op.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

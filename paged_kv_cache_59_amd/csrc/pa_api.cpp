@@ -36,8 +36,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // A KV head of G > kMaxGroup query heads is attended in ceil(G / kMaxGroup)
 // sub-groups of up to kMaxGroup query heads (num_q_heads a multiple of
-// num_kv_heads): the prefix pass's heads; the decode takes them two per pass
-// (decode_split).
+// num_kv_heads): the prefix pass's heads; the decode takes up to 4 of them
+// per pass (decode_split).
 int32_t kv_split(int32_t num_q_heads, int32_t num_kv_heads) {
   return (int32_t)ceil_div(num_q_heads / num_kv_heads, kMaxGroup);
 }

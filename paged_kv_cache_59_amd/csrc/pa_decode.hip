@@ -34,16 +34,19 @@
 //    4x4x4 16-block MFMA, so every K and V element loaded serves all G heads;
 //    the G q rows stay in 1 KiB of LDS for the whole run (in registers they
 //    would cost 64 per lane and halve the waves a SIMD holds).  A larger
-//    group is split into kv_split = ceil(G / 4) sub-groups of up to 4 rows
-//    (an empty one added to an odd count), attended two per pass: one pass
-//    over a unit forms both sub-groups' logits and products on two sets of
-//    MFMAs over the same K and V registers (8 q rows).  Each pair is a copy
-//    of the batch in the unit order, and the merger sees kv_split x S
-//    virtual sequences, sub-group j's copy of sequence s at j S + s.  With
-//    several copies, copy c's units lie exactly c / copies of the way along,
-//    so with equal shares the workers that read one block for different
-//    copies read it at the same time, and (for an even split of the workers
-//    into runs of 32 per XCD) on the same XCD, whose L2 serves the repeats.
+//    group (Wide) is taken as kv_split = ceil(G / 4) sub-groups of up to 4
+//    query heads, up to 4 of them (16 rows) per pass: the logits are
+//    S^T = K Q^T on 16x16x32 MFMA tiles (16 tokens x 16 query rows), the
+//    products O^T += V^T P^T on the same tiles (16 dims x 16 rows), so each
+//    lane carries one query row's softmax state and the unit's VALU work
+//    does not grow with G.  The merger sees kv_split x S virtual sequences,
+//    sub-group j's copy of sequence s at j S + s, and a pass hands it one
+//    piece per sub-group.  Above 4 sub-groups the count is rounded up to a
+//    multiple of 4 and the unit order holds one copy of the batch per 4;
+//    copy c's units lie exactly c / copies of the way along, so with equal
+//    shares the workers that read one block for different copies read it at
+//    the same time, and (for an even split of the workers into runs of 32
+//    per XCD) on the same XCD, whose L2 serves the repeats.
 //  * q . K: lane l owns token l of the 64; it loads its 16-byte chunks of the
 //    K row (K pool [NB][Hkv][D/8][16][8]: for a fixed chunk the 64 lanes read
 //    four contiguous 256-byte runs) and feeds them as the B operand, so the

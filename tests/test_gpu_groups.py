@@ -1,13 +1,15 @@
 """Decode with more than 4 query heads per KV head (GQA groups of 5 to 16),
 on the GPU, through the C-ABI, against the oracle.
 
-The decode's matrix instruction holds 4 query rows, so a KV head of G > 4
-query heads is attended in ceil(G / 4) sub-groups of up to 4 rows (the last
-one short when 4 does not divide G), one copy of the batch per sub-group in
-the same launch.  The cases cover groups that 4 divides and groups it does
-not, both head dimensions and every block size, the plain and the fused
-decode (pools bit for bit: only the first copy stores the new rows), cut
-runs (many workers) and one worker holding every run, the shared-prefix
+A KV head of G > 4 query heads is taken as ceil(G / 4) sub-groups of up to
+4 rows (the last one short when 4 does not divide G), up to 4 sub-groups (16
+query rows, the columns of 16x16x32 matrix tiles) per pass over K and V;
+above 4 sub-groups the passes are copies of the batch in the same launch.
+Each sub-group's piece of a run reaches the merger as its own virtual
+sequence.  The cases cover groups that 4 divides and groups it does not, one
+pass and two, both head dimensions and every block size, the plain and the
+fused decode (pools bit for bit: only the first pass stores the new rows),
+cut runs (many workers) and one worker holding every run, the shared-prefix
 pass, and batches above one launch (4096 virtual sequences: 2048 sequences
 at G = 8).
 """
@@ -78,7 +80,7 @@ def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
 @pytest.mark.parametrize("Hq,Hkv", [(8, 1), (12, 1), (16, 1)])
 def test_large_group_batch_above_one_launch(Hq, Hkv):
     """G = 8: 2 sub-groups in one pass, 2048 sequences per launch; G = 12:
-    3 copies, 1365; G = 16: 2 copies of paired sub-groups, 1024."""
+    3 sub-groups, 1365; G = 16: 4 sub-groups, 1024."""
     w = wl.make_workload("groups-wide", 470 + Hq, Hq, Hkv, 64, len_range=(1, 40), num_seqs=4100)
     d = to_device(w)
     out = gpu_step(w, d, 0)

@@ -54,9 +54,9 @@ def test_noalloc_matches_workspace_call_twice_in_a_row():
 
 
 def test_noalloc_large_groups():
-    """8 and 12 query heads per KV head (sub-groups two per pass, two share
-    slots per worker in the array): bit for bit as with a workspace, and the
-    oracle's result, one call after the other."""
+    """8 and 12 query heads per KV head (2 and 3 sub-groups in one pass, as
+    many share slots per worker in the array): bit for bit as with a
+    workspace, and the oracle's result, one call after the other."""
     for w, workers in ((wl.make_workload("noalloc-g8", 404, 64, 8, 128, len_range=(1, 1500),
                                          num_seqs=20), 0),
                        (wl.make_workload("noalloc-g12", 405, 24, 2, 64, len_range=(1, 700),
