@@ -51,10 +51,14 @@ def test_fused_large_groups(Hq, Hkv, D, workers):
 
 
 @pytest.mark.parametrize("BS", [8, 32])
-def test_large_group_block_sizes(BS):
-    w = wl.make_workload("groups-bs", 440 + BS, 28, 4, 128, context_lens=FUSED_LENS,
+@pytest.mark.parametrize("Hq,Hkv,D", [(28, 4, 128), (24, 2, 64), (20, 1, 64)])
+def test_large_group_block_sizes(BS, Hq, Hkv, D):
+    """Every block size for one pass of 2 and 3 sub-groups and for two passes
+    (G = 20), both head dims: the tiles' K rows and V groups span 2 or 4
+    blocks (block size 8) or half a block (32)."""
+    w = wl.make_workload("groups-bs", 440 + BS + Hq + D, Hq, Hkv, D, context_lens=FUSED_LENS,
                          block_size=BS)
-    run_fused(w, 0, f"fused G7 BS{BS}")
+    run_fused(w, 0, f"fused G{Hq // Hkv} D{D} BS{BS}")
 
 
 @pytest.mark.parametrize("workers", [64, 512])
@@ -65,7 +69,8 @@ def test_large_group_long_runs_cut(workers):
     run_fused(w, workers, f"fused G8 long runs over {workers} workers")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64), (16, 1, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 128), (28, 4, 128), (10, 1, 64), (16, 1, 128),
+                                     (20, 1, 64)])
 @pytest.mark.parametrize("workers", [0, 5000])
 def test_shared_prefix_large_groups(Hq, Hkv, D, workers):
     """The prefix pass attends each sub-group's rows of a group's members
