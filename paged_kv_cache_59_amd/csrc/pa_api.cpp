@@ -204,8 +204,9 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   // sub-groups: the launch's merger sees split x n virtual sequences (one
   // per sub-group and sequence), at most kMaxSeqsPerLaunch; its 64-token
   // units (all heads) must fit a 32-bit index
-  // (split: the decode's sub-groups, an empty one added to an odd count
-  // above one; the prefix pass takes the sub-groups that hold query heads)
+  // (split: the decode's sub-groups, a count above 4 rounded up to a
+  // multiple of 4 with empty ones; the prefix pass takes the sub-groups that
+  // hold query heads)
   const int32_t groups = kv_split(num_q_heads, num_kv_heads);
   const int32_t split = pa::decode_split(groups);
   const int64_t per_launch = seqs_per_launch(num_seqs, split);

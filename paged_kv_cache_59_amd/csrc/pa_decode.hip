@@ -283,10 +283,10 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int Sv = a.num_seqs;          // virtual sequences (slots, counters)
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
-  // Sub-groups: a KV head with more than 4 query heads is attended in
-  // kv_split sub-groups of up to 4 query heads (the 4 rows of the MFMA), one
-  // per copy of the batch: S counts the virtual sequences, sub-group
-  // s / Sr of sequence s % Sr.
+  // Sub-groups: a KV head with more than 4 query heads is taken as kv_split
+  // sub-groups of up to 4 query heads; the merger, its counters and the
+  // partial slots see Sv virtual sequences, sub-group s / Sr of sequence
+  // s % Sr.
   const int split = a.kv_split;
   const int Sr = Sv / split;  // sequences of the batch (lengths, tables, new rows)
   // sequences in unit order (the unit tables); Wide: one copy of the batch
@@ -296,7 +296,8 @@ __global__ __launch_bounds__(128) void decode_kernel(const DecodeArgs a) {
   const int G = Hq / Hkv;    // query heads per KV head
   auto sub_of = [&](int s) { return split == 1 ? 0 : s / Sr; };
   auto real_of = [&](int s) { return split == 1 ? s : s - s / Sr * Sr; };
-  // (an empty sub-group, added to an odd count, has none)
+  // (an empty sub-group, which rounds a count above 4 up to a multiple of 4,
+  // has none)
   auto q_rows = [&](int s) { return split == 1 ? G : max(0, min(4, G - sub_of(s) * 4)); };
   // the q / out row of the first query head of run (s, h)
   auto q_row0 = [&](int s, int h) -> int64_t {
