@@ -44,6 +44,7 @@ CASES = [
     ("plain", dict(seed=501, Hq=32, Hkv=8, D=128, len_range=(1, 900), num_seqs=24)),
     ("fused", dict(seed=502, Hq=32, Hkv=8, D=128, len_range=(1, 900), num_seqs=24)),
     ("fused", dict(seed=503, Hq=64, Hkv=8, D=128, len_range=(1, 700), num_seqs=12)),  # G = 8
+    ("fused", dict(seed=506, Hq=32, Hkv=2, D=128, len_range=(1, 700), num_seqs=10)),  # G = 16
     ("fused", dict(seed=504, Hq=32, Hkv=8, D=128, num_seqs=16, prefix_groups=2,
                    prefix_len=512, suffix_range=(1, 200))),  # the prefix pass and the decode
     ("noalloc", dict(seed=505, Hq=16, Hkv=4, D=64, len_range=(1, 600), num_seqs=20)),

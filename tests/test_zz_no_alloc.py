@@ -54,13 +54,15 @@ def test_noalloc_matches_workspace_call_twice_in_a_row():
 
 
 def test_noalloc_large_groups():
-    """8 and 12 query heads per KV head (2 and 3 sub-groups in one pass, as
-    many share slots per worker in the array): bit for bit as with a
+    """8, 12 and 16 query heads per KV head (2, 3 and 4 sub-groups in one
+    pass, as many share slots per worker in the array): bit for bit as with a
     workspace, and the oracle's result, one call after the other."""
     for w, workers in ((wl.make_workload("noalloc-g8", 404, 64, 8, 128, len_range=(1, 1500),
                                          num_seqs=20), 0),
                        (wl.make_workload("noalloc-g12", 405, 24, 2, 64, len_range=(1, 700),
-                                         num_seqs=9), 5)):
+                                         num_seqs=9), 5),
+                       (wl.make_workload("noalloc-g16", 406, 32, 2, 128, len_range=(1, 900),
+                                         num_seqs=11), 0)):
         log(f"noalloc case {w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
             f"workers={workers}")
         d_ref, d_new = to_device(w), to_device(w)
