@@ -11,7 +11,10 @@ timed region.  The pools are cloned into several replicas totalling at least
 serve a step from the previous one's reads.
 
 Prints one JSON line:
-  value        bytes the step must move / step time, GB/s
+  value        bytes the step must move / step time, GB/s (the steps launched
+               one by one from the host)
+  graph_value  the same for the same steps replayed from one captured HIP
+               graph (`graph_ms_per_step`), with no host dispatch between them
   roofline     the decode kernel (one launch: balanced persistent workers with
                the merge of cut sequences and the append fused) timed with HIP
                events bound to the kernel on its stream: its algorithmic bytes
@@ -54,6 +57,8 @@ def parse():
     ap.add_argument("--replica-gb", type=float, default=2.0)
     ap.add_argument("--placement", default="shuffled", choices=["shuffled", "sequential"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the pass that replays the timed steps from one captured HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--probe-gib", type=float, default=4.0,
                     help="read-bandwidth probe size (0: skip the probe)")
@@ -593,6 +598,25 @@ def main():
         flushed_ms = np.array([a.elapsed_time(b) for a, b in fev])
         del scratch
 
+    # The same `steps` steps captured once in a HIP graph (torch.cuda.CUDAGraph:
+    # the library enqueues only kernels) and replayed between two
+    # synchronisations: no host dispatch between the launches, as in a serving
+    # loop that replays captured decode steps.  Reported beside the value.
+    graph_ms_per_step = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(4 * args.steps + i)
+        torch.cuda.synchronize()
+        graph.replay()  # (first replay: warm)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
+
     probe = achievable_read(torch, pk, args.probe_gib) if args.probe_gib > 0 else None
     ms_per_step = wall * 1e3 / args.steps
     # Bytes the method must move.  A block several sequences share is counted
@@ -623,6 +647,11 @@ def main():
         "data": "synthetic",
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        # the same steps replayed from one captured HIP graph
+        "graph_ms_per_step": (None if graph_ms_per_step is None
+                              else round(graph_ms_per_step, 5)),
+        "graph_value": (None if graph_ms_per_step is None
+                        else round(step_bytes / (graph_ms_per_step * 1e-3) / 1e9, 2)),
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
