@@ -52,14 +52,25 @@ def test_fused_large_groups(Hq, Hkv, D, workers):
 
 
 @pytest.mark.parametrize("BS", [8, 32])
-@pytest.mark.parametrize("Hq,Hkv,D", [(28, 4, 128), (24, 2, 64), (20, 1, 64)])
-def test_large_group_block_sizes(BS, Hq, Hkv, D):
-    """Every block size for one pass of 2 and 3 sub-groups and for two passes
-    (G = 20), both head dims: the tiles' K rows and V groups span 2 or 4
-    blocks (block size 8) or half a block (32)."""
+@pytest.mark.parametrize("Hq,Hkv,D", [(28, 4, 128), (24, 2, 64), (20, 1, 64), (32, 2, 128)])
+@pytest.mark.parametrize("workers", [0, 5000])
+def test_large_group_block_sizes(BS, Hq, Hkv, D, workers):
+    """Every block size for one pass of 2, 3 and 4 sub-groups and for two
+    passes (G = 20), both head dims, whole and cut runs: the tiles' K rows and
+    V groups span 2 or 4 blocks (block size 8) or half a block (32)."""
     w = wl.make_workload("groups-bs", 440 + BS + Hq + D, Hq, Hkv, D, context_lens=FUSED_LENS,
                          block_size=BS)
-    run_fused(w, 0, f"fused G{Hq // Hkv} D{D} BS{BS}")
+    run_fused(w, workers, f"fused G{Hq // Hkv} D{D} BS{BS} workers{workers}")
+
+
+@pytest.mark.parametrize("BS", [8, 32])
+def test_shared_prefix_large_groups_block_sizes(BS):
+    """The prefix pass and the 16-row tiles together at block sizes 8 and 32
+    (G = 8)."""
+    w = wl.make_workload("groups-prefix-bs", 480 + BS, 32, 4, 128, num_seqs=16, prefix_groups=2,
+                         prefix_len=512, suffix_range=(1, 200), block_size=BS)
+    assert w.shares_blocks()
+    run_fused(w, 0, f"prefix G8 BS{BS}", shared_blocks=True)
 
 
 @pytest.mark.parametrize("workers", [64, 512])
