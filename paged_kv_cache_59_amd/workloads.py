@@ -430,6 +430,11 @@ WORKLOADS = {
     # and K/V bytes of llama8b_b64.
     "g12_b64": dict(seed=2, num_q_heads=96, num_kv_heads=8, head_dim=128,
                     len_range=(128, 2048), num_seqs=64),
+    # a multi-query layer (32 query heads on one KV head), 512 sequences of
+    # the Llama lengths: about the units and K/V bytes of llama8b_b64, with
+    # two passes of 16 query heads over each unit
+    "mqa_b512": dict(seed=2, num_q_heads=32, num_kv_heads=1, head_dim=128,
+                     len_range=(128, 2048), num_seqs=512),
     # OPT-13B-shaped multi-head layer: batch 128, 40 heads, head_dim 128,
     # lengths uniform in [1, 2048].
     "opt13b_b128": dict(seed=3, num_q_heads=40, num_kv_heads=40, head_dim=128,
