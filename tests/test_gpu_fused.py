@@ -232,7 +232,7 @@ def test_fused_errors():
 
 
 @pytest.mark.parametrize("name", ["llama8b_b64", "prefix_b256", "opt13b_b128", "longctx_b16",
-                                  "llama70b_b64", "g12_b64", "llama405b_b64"])
+                                  "llama70b_b64", "g12_b64", "llama405b_b64", "mqa_b512"])
 def test_fused_full_size(name):
     """The benchmark's batches in its launch configuration (automatic worker
     count, the shared-blocks flag where blocks are shared): pools bit for bit,
